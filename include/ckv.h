@@ -1,0 +1,193 @@
+/*
+ * ckv.h -- C ABI of libckv, cluster-granular recallable KV selection for
+ * long-context decode on AMD Instinct MI355X (gfx950).
+ *
+ * Method: the page "ClusterKV: Manipulating LLM KV Cache in Semantic Space
+ * for Recallable Compression" (summary of arXiv 2412.03213). Section names
+ * are the page's headings, glossed:
+ *   [Clustering in semantic space]  核心方法细节 / 语义空间中的聚类
+ *   [Cluster-granular selection]    核心方法细节 / 语义聚类粒度的选择
+ *   [Selection and indexing]        核心方法细节 / 选择与索引机制 (Fig. 8)
+ *   [Long context & KV compression] 背景知识与设计原则 / 长上下文推理与KV缓存压缩
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or keeps them; the caller also provides the
+ *     scratch workspace, sized by the matching *_workspace() query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Work is enqueued on it; no call synchronises the host. Calls on one
+ *     stream run in order. Calls with distinct workspaces may run
+ *     concurrently on different streams.
+ *   - Arguments are checked on the host before anything is enqueued. On any
+ *     error the call returns a non-zero ckv_status and has written nothing.
+ *     A failure to launch returns CKV_ERR_LAUNCH. No C++ exception crosses
+ *     this boundary.
+ *   - Only head dimension d = 128 is supported (CKV_ERR_UNSUPPORTED
+ *     otherwise). Element type: CKV_F32 or CKV_BF16 for keys, values and
+ *     queries; centroids are always fp32, indices int32, the attention
+ *     output fp32.
+ *   - Rows are row-major with d contiguous elements. "Head stride" is the
+ *     number of ELEMENTS between row 0 of one head and row 0 of the next.
+ *     K, V, q and centroid pointers must be 16-byte aligned and head strides
+ *     a multiple of 16 bytes (CKV_ERR_INVALID_ARG otherwise).
+ */
+#ifndef CKV_H
+#define CKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CKV_OK = 0,
+    CKV_ERR_INVALID_ARG = 1,  /* a pointer, size, stride or range is invalid */
+    CKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d != 128) */
+    CKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+    CKV_ERR_LAUNCH = 4        /* the HIP runtime refused a kernel launch */
+} ckv_status;
+
+typedef enum { CKV_F32 = 0, CKV_BF16 = 1 } ckv_dtype;
+
+/* Static English text for a status code (never NULL). */
+const char *ckv_status_string(int status);
+
+/* Version of this ABI (structure layouts and call signatures). */
+int ckv_abi_version(void);
+
+/* ------------------------------------------------------------ cluster --
+ * Semantic clustering of keys [Clustering in semantic space, Fig. 4]:
+ * K-means with the cosine distance D(i,j) = 1 - <k_i,k_j>/(|k_i||k_j|) over
+ * window rows n_sink .. L-1 of each head (the first n_sink rows are attention
+ * sinks and are not clustered). Initial centroids are the keys at rows
+ * n_sink + s*c, s = floor((L - n_sink) / C). Each of `iters` iterations
+ * assigns every key to the centroid of largest cosine similarity (ties to
+ * the lower id) and replaces every centroid by the mean of the raw keys
+ * assigned to it (an empty cluster keeps its centroid). The returned
+ * partition is the last iteration's and the centroids are its means.
+ * The page's C0 = L/80 and, for decode-time increments, C+ = 4 clusters
+ * over the newest m = 320 tokens with n_sink = 0, are the caller's choice.
+ *
+ * Assignment scores are computed on bf16 unit vectors (each vector scaled by
+ * 1/|x| in fp64, rounded to fp32 then to bf16) with fp32 accumulation for
+ * CKV_BF16 keys, and on fp32 unit vectors with fp32 accumulation for
+ * CKV_F32 keys. Centroid means are accumulated in fp64 and stored as fp32.
+ *
+ * Outputs (per head h, all caller-owned device buffers):
+ *   centroids   fp32 [H][c_cap][d]; slots c_base .. c_base+C-1 written.
+ *   assign      int32 [H][L]; label of every window row, -1 for sinks.
+ *   csr_offsets int32 [H][c_cap+1]; slots c_base .. c_base+C written with
+ *               t_base + exclusive prefix sums of the cluster sizes, so
+ *               cluster c_base+c owns tokens [off[c_base+c], off[c_base+c+1]).
+ *   csr_tokens  int32 [H][t_cap]; slots t_base .. t_base+L-n_sink-1 written
+ *               with absolute token ids (token_base + row), sorted by
+ *               cluster, ascending inside a cluster.
+ * Appending clusters of a later window (c_base > 0, t_base > 0) leaves the
+ * earlier slots untouched, so one CSR can index prompt and decode clusters.
+ */
+typedef struct {
+    int32_t H;              /* independent KV-head problems (batch x KV heads), >= 1 */
+    int32_t d;              /* head dimension, must be 128 */
+    int64_t L;              /* rows in the clustering window, > n_sink */
+    int64_t k_head_stride;  /* elements between heads of K, >= L*d */
+    int64_t token_base;     /* absolute token id of window row 0, >= 0 */
+    int32_t n_sink;         /* leading rows excluded from clustering, >= 0 */
+    int32_t C;              /* clusters, 1 <= C <= min(L - n_sink, 2048) */
+    int32_t iters;          /* K-means iterations, >= 1 */
+    int32_t dtype;          /* ckv_dtype of K */
+    int32_t c_base;         /* first centroid / offset slot written, >= 0 */
+    int32_t c_cap;          /* centroid slots per head, >= c_base + C */
+    int64_t t_base;         /* first token slot written, >= 0 */
+    int64_t t_cap;          /* token slots per head, >= t_base + L - n_sink */
+} ckv_cluster_desc;
+
+/* Bytes of workspace ckv_cluster needs for `desc` (0 if desc is invalid). */
+size_t ckv_cluster_workspace(const ckv_cluster_desc *desc);
+
+/* K: window row 0 of head 0, element type desc->dtype, row r of head h at
+ * K + (h * k_head_stride + r) * d. */
+int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
+                int32_t *assign, int32_t *csr_offsets, int32_t *csr_tokens,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------- select --
+ * Cluster-granular selection for one decode step [Cluster-granular
+ * selection; Selection and indexing, Fig. 8]. For KV head g, with
+ * q_g = sum of its G query rows (fp64, in row order):
+ *   s_c = q_g . mu_c for c < C, an fp64 inner product with a fixed
+ *         association (32 fused-multiply-add chains over 4 consecutive
+ *         channels, then a pairwise tree: run r + run r+16, +8, +4, +2, +1);
+ *   clusters are ranked by (s_c descending, c ascending);
+ *   walking the ranks, whole clusters are admitted until
+ *   B_eff = B - n_sink - n_pending tokens are taken; the last admitted
+ *   cluster is cut to its first (lowest-position) tokens that still fit.
+ * idx[g] = [0 .. n_sink) ++ [pending_begin .. pending_begin + n_pending)
+ *          ++ admitted tokens (rank order, each cluster ascending),
+ * then -1 up to B; n_sel[g] = number of valid entries.
+ * Pending tokens are decode tokens not yet clustered; they are always
+ * selected and count toward the budget, like the sinks.
+ *
+ * Inputs: q [H*G][d] (dtype), centroids fp32 [H][c_cap][d], csr_offsets
+ * int32 [H][c_cap+1] and csr_tokens int32 [H][t_cap] as written by
+ * ckv_cluster. Offsets are clamped to [0, t_cap] on the device.
+ * Outputs: idx int32 [H][B], n_sel int32 [H].
+ */
+typedef struct {
+    int32_t H;              /* KV heads, >= 1 */
+    int32_t G;              /* query heads per KV head, 1..8 */
+    int32_t d;              /* must be 128 */
+    int32_t C;              /* clusters in use, 1 <= C <= min(c_cap, 2048) */
+    int32_t c_cap;          /* centroid slots per head (row stride) */
+    int32_t n_sink;         /* always-selected leading tokens, >= 0 */
+    int64_t t_cap;          /* token slots per head (row stride) */
+    int64_t pending_begin;  /* first pending token id, >= 0 */
+    int64_t n_pending;      /* pending token count, >= 0 */
+    int32_t B;              /* budget incl. sinks and pending; idx row stride */
+    int32_t dtype;          /* ckv_dtype of q */
+} ckv_select_desc;
+
+size_t ckv_select_workspace(const ckv_select_desc *desc);
+
+int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroids,
+               const int32_t *csr_offsets, const int32_t *csr_tokens,
+               int32_t *idx, int32_t *n_sel, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* -------------------------------------------------------- sparse_attn --
+ * Decode attention over the selected rows [Long context & KV compression]:
+ * o_h = softmax(q_h K_S^T * scale) V_S, K_S and V_S the rows idx[g][0 ..
+ * n_sel[g]) of KV head g = h / G, for every query head h. scale <= 0 means
+ * 1/sqrt(d). The G query heads of a KV head share one gather of its rows.
+ * Entries outside [0, kv_rows) are skipped (they contribute nothing);
+ * n_sel is clamped to [0, B]; a head with nothing selected gets o = 0.
+ * CKV_BF16 computes in fp32; CKV_F32 computes scores, softmax and sums in
+ * fp64. The output is fp32.
+ *
+ * Inputs: q [H*G][d] (dtype), K and V (dtype; row r of head g at
+ * (g * kv_head_stride + r) * d), idx int32 [H][B], n_sel int32 [H].
+ * Output: o fp32 [H*G][d].
+ */
+typedef struct {
+    int32_t H;              /* KV heads, >= 1 */
+    int32_t G;              /* query heads per KV head, 1..8 */
+    int32_t d;              /* must be 128 */
+    int32_t B;              /* idx row stride (max selected rows), >= 1 */
+    int64_t kv_head_stride; /* elements between heads of K and V, >= kv_rows*d */
+    int64_t kv_rows;        /* valid rows per head, >= 1 */
+    float scale;            /* softmax scale; <= 0 means 1/sqrt(d) */
+    int32_t dtype;          /* ckv_dtype of q, K and V */
+} ckv_attn_desc;
+
+size_t ckv_attn_workspace(const ckv_attn_desc *desc);
+
+int ckv_sparse_attn(const ckv_attn_desc *desc, const void *q, const void *K,
+                    const void *V, const int32_t *idx, const int32_t *n_sel,
+                    float *o, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CKV_H */

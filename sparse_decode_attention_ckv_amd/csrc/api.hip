@@ -1,0 +1,217 @@
+// api.hip -- the C ABI of libckv (declared in include/ckv.h).
+//
+// Every entry point validates its descriptor and pointers on the host,
+// carves the caller's workspace, and enqueues kernels on the caller's
+// stream. Nothing is allocated, nothing is synchronised, no state is kept.
+#include <math.h>
+#include <string.h>
+
+#include "ckv.h"
+#include "ckv_dev.h"
+
+using namespace ckv;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(int32_t t) { return t == CKV_F32 || t == CKV_BF16; }
+
+// Returns CKV_OK or the reason the cluster descriptor is rejected.
+int check_cluster(const ckv_cluster_desc *d) {
+    if (!d) return CKV_ERR_INVALID_ARG;
+    if (d->H < 1 || !dtype_ok(d->dtype)) return CKV_ERR_INVALID_ARG;
+    if (d->d != kD) return d->d < 1 ? CKV_ERR_INVALID_ARG : CKV_ERR_UNSUPPORTED;
+    if (d->n_sink < 0 || d->L <= d->n_sink) return CKV_ERR_INVALID_ARG;
+    const int64_t Lp = d->L - d->n_sink;
+    if (d->C < 1 || d->C > Lp || d->iters < 1) return CKV_ERR_INVALID_ARG;
+    if (d->C > kMaxC) return CKV_ERR_UNSUPPORTED;
+    if (d->k_head_stride < d->L * kD) return CKV_ERR_INVALID_ARG;
+    if (d->token_base < 0 || d->token_base + d->L > INT32_MAX) return CKV_ERR_INVALID_ARG;
+    if (d->c_base < 0 || (int64_t)d->c_cap < (int64_t)d->c_base + d->C) return CKV_ERR_INVALID_ARG;
+    if (d->t_base < 0 || d->t_cap < d->t_base + Lp || d->t_cap > INT32_MAX)
+        return CKV_ERR_INVALID_ARG;
+    return CKV_OK;
+}
+
+void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char *ws) {
+    p->H = d->H;
+    p->C = d->C;
+    p->Cpad = (d->C + 63) / 64 * 64;
+    p->iters = d->iters;
+    p->n_sink = d->n_sink;
+    p->dtype = d->dtype;
+    p->c_base = d->c_base;
+    p->c_cap = d->c_cap;
+    p->L = d->L;
+    p->Lp = d->L - d->n_sink;
+    p->k_head_stride = d->k_head_stride;
+    p->token_base = d->token_base;
+    p->t_base = d->t_base;
+    p->t_cap = d->t_cap;
+    p->ntiles = (p->Lp + kCsrTile - 1) / kCsrTile;
+    const size_t es = d->dtype == CKV_BF16 ? 2 : 4;
+    size_t o = 0;
+    p->kt = ws ? ws + o : nullptr;
+    o += align_up((size_t)p->H * p->Lp * kD * es);
+    p->mt = ws ? ws + o : nullptr;
+    o += align_up((size_t)p->H * p->Cpad * kD * es);
+    p->tile_hist = ws ? (int32_t *)(ws + o) : nullptr;
+    o += align_up((size_t)p->H * p->ntiles * p->C * sizeof(int32_t));
+    p->tile_rank = ws ? (int32_t *)(ws + o) : nullptr;
+    o += align_up((size_t)p->H * p->Lp * sizeof(int32_t));
+    *bytes = o;
+}
+
+int check_select(const ckv_select_desc *d) {
+    if (!d) return CKV_ERR_INVALID_ARG;
+    if (d->H < 1 || d->G < 1 || d->G > 8 || !dtype_ok(d->dtype)) return CKV_ERR_INVALID_ARG;
+    if (d->d != kD) return d->d < 1 ? CKV_ERR_INVALID_ARG : CKV_ERR_UNSUPPORTED;
+    if (d->C < 1 || d->c_cap < d->C) return CKV_ERR_INVALID_ARG;
+    if (d->C > kMaxC) return CKV_ERR_UNSUPPORTED;
+    if (d->n_sink < 0 || d->n_pending < 0 || d->pending_begin < 0) return CKV_ERR_INVALID_ARG;
+    if (d->pending_begin + d->n_pending > INT32_MAX) return CKV_ERR_INVALID_ARG;
+    if (d->B < 1 || (int64_t)d->B < d->n_sink + d->n_pending) return CKV_ERR_INVALID_ARG;
+    if (d->t_cap < 1 || d->t_cap > INT32_MAX) return CKV_ERR_INVALID_ARG;
+    return CKV_OK;
+}
+
+size_t select_bytes(const ckv_select_desc *d) {
+    return align_up((size_t)d->H * d->C * sizeof(double));
+}
+
+int check_attn(const ckv_attn_desc *d) {
+    if (!d) return CKV_ERR_INVALID_ARG;
+    if (d->H < 1 || d->G < 1 || d->G > 8 || !dtype_ok(d->dtype)) return CKV_ERR_INVALID_ARG;
+    if (d->d != kD) return d->d < 1 ? CKV_ERR_INVALID_ARG : CKV_ERR_UNSUPPORTED;
+    if (d->B < 1 || d->kv_rows < 1) return CKV_ERR_INVALID_ARG;
+    if (d->kv_head_stride < d->kv_rows * kD) return CKV_ERR_INVALID_ARG;
+    if (!(d->scale == d->scale) || isinf(d->scale)) return CKV_ERR_INVALID_ARG;
+    return CKV_OK;
+}
+
+int attn_splits(const ckv_attn_desc *d) { return (d->B + 31) / 32; }
+
+size_t attn_bytes(const ckv_attn_desc *d) {
+    const size_t es = d->dtype == CKV_BF16 ? sizeof(float) : sizeof(double);
+    return align_up((size_t)d->H * d->G * attn_splits(d) * (kD + 2) * es);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? CKV_OK : CKV_ERR_LAUNCH; }
+
+// Kernels read rows with 16-byte vector loads.
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool stride_ok(int64_t elems, int32_t dtype) {
+    return ((elems * (dtype == CKV_BF16 ? 2 : 4)) & 15) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ckv_status_string(int status) {
+    switch (status) {
+        case CKV_OK: return "ok";
+        case CKV_ERR_INVALID_ARG: return "invalid argument";
+        case CKV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case CKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case CKV_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int ckv_abi_version(void) { return 1; }
+
+size_t ckv_cluster_workspace(const ckv_cluster_desc *desc) {
+    if (check_cluster(desc) != CKV_OK) return 0;
+    ClusterPlan p;
+    size_t bytes;
+    plan_cluster(desc, &p, &bytes, nullptr);
+    return bytes;
+}
+
+int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
+                int32_t *assign, int32_t *csr_offsets, int32_t *csr_tokens, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    const int st = check_cluster(desc);
+    if (st != CKV_OK) return st;
+    if (!K || !centroids || !assign || !csr_offsets || !csr_tokens) return CKV_ERR_INVALID_ARG;
+    if (!aligned16(K) || !aligned16(centroids) || !stride_ok(desc->k_head_stride, desc->dtype))
+        return CKV_ERR_INVALID_ARG;
+    ClusterPlan p;
+    size_t need;
+    plan_cluster(desc, &p, &need, (char *)workspace);
+    if (!workspace || workspace_bytes < need) return CKV_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+
+    hipError_t e = launch_normalize_keys(p, K, assign, s);
+    if (e == hipSuccess) e = launch_init_centroids(p, K, centroids, s);
+    for (int t = 0; t < p.iters && e == hipSuccess; ++t) {
+        e = launch_assign(p, assign, s);
+        if (e == hipSuccess) e = launch_csr(p, assign, csr_offsets, csr_tokens, s);
+        if (e == hipSuccess) e = launch_update(p, K, csr_offsets, csr_tokens, centroids, s);
+    }
+    return launch_status(e);
+}
+
+size_t ckv_select_workspace(const ckv_select_desc *desc) {
+    if (check_select(desc) != CKV_OK) return 0;
+    return select_bytes(desc);
+}
+
+int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroids,
+               const int32_t *csr_offsets, const int32_t *csr_tokens, int32_t *idx,
+               int32_t *n_sel, void *workspace, size_t workspace_bytes, void *stream) {
+    const int st = check_select(desc);
+    if (st != CKV_OK) return st;
+    if (!q || !centroids || !csr_offsets || !csr_tokens || !idx || !n_sel)
+        return CKV_ERR_INVALID_ARG;
+    if (!aligned16(centroids)) return CKV_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < select_bytes(desc)) return CKV_ERR_WORKSPACE;
+    SelectPlan p;
+    p.H = desc->H;
+    p.G = desc->G;
+    p.C = desc->C;
+    p.c_cap = desc->c_cap;
+    p.n_sink = desc->n_sink;
+    p.B = desc->B;
+    p.dtype = desc->dtype;
+    p.t_cap = desc->t_cap;
+    p.pending_begin = desc->pending_begin;
+    p.n_pending = desc->n_pending;
+    p.scores = (double *)workspace;
+    return launch_status(launch_select(p, q, centroids, csr_offsets, csr_tokens, idx, n_sel,
+                                       (hipStream_t)stream));
+}
+
+size_t ckv_attn_workspace(const ckv_attn_desc *desc) {
+    if (check_attn(desc) != CKV_OK) return 0;
+    return attn_bytes(desc);
+}
+
+int ckv_sparse_attn(const ckv_attn_desc *desc, const void *q, const void *K, const void *V,
+                    const int32_t *idx, const int32_t *n_sel, float *o, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    const int st = check_attn(desc);
+    if (st != CKV_OK) return st;
+    if (!q || !K || !V || !idx || !n_sel || !o) return CKV_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) ||
+        !stride_ok(desc->kv_head_stride, desc->dtype))
+        return CKV_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < attn_bytes(desc)) return CKV_ERR_WORKSPACE;
+    AttnPlan p;
+    p.H = desc->H;
+    p.G = desc->G;
+    p.B = desc->B;
+    p.dtype = desc->dtype;
+    p.S = attn_splits(desc);
+    p.kv_head_stride = desc->kv_head_stride;
+    p.kv_rows = desc->kv_rows;
+    p.scale = desc->scale > 0.f ? (double)desc->scale : 1.0 / sqrt((double)kD);
+    p.partials = workspace;
+    return launch_status(launch_attn(p, q, K, V, idx, n_sel, o, (hipStream_t)stream));
+}
+
+}  // extern "C"

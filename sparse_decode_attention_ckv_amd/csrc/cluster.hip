@@ -1,0 +1,581 @@
+// cluster.hip -- semantic clustering of keys on gfx950.
+//
+// Method: "ClusterKV: Manipulating LLM KV Cache in Semantic Space for
+// Recallable Compression", section 核心方法细节 / 语义空间中的聚类 (clustering in
+// semantic space, cosine distance D, K-means of Fig. 4) and section
+// 选择与索引机制 (selection and indexing: cluster sizes, prefix sums and
+// label-sorted token indices kept as metadata).
+//
+// One call runs, per independent KV head:
+//   normalize_keys            unit keys, once              (HBM-bound)
+//   init_centroids            mu_c = k_{n_sink + s*c}
+//   iters x {
+//     assign                  cosine GEMM on bf16 MFMA + fused row argmax
+//     csr count/scan/scatter  atomic-free stable counting sort -> CSR
+//     update                  per-cluster fp64 segmented sum of raw keys,
+//                             mean -> fp32 centroid, unit centroid for the
+//                             next assignment                (HBM-bound)
+//   }
+// The page's own update kernel (Fig. 7: shared-memory atomicAdd per cluster,
+// threads strided along the sequence, channels split into P partitions) is
+// replaced by the counting sort + segmented reduction: no atomics, so every
+// result is bitwise reproducible.
+#include "ckv_dev.h"
+
+namespace ckv {
+
+// --------------------------------------------------------------------------
+// Unit vector of a 128-element row held one element per thread (128 threads
+// of the block participate; others pass active=false). |x|^2 is one fp64
+// fused-multiply-add chain over j = 0..127 (evaluated by thread 0 in that
+// order), r = 1/sqrt(|x|^2) in fp64, and element j becomes fp32(x_j * r),
+// rounded once more to bf16 when BF16. A zero row stays zero.
+template <bool BF16>
+__device__ void block_unit_row(float x, bool active, int j, void *out_row,
+                               float *sx, double *sinv) {
+    if (active) sx[j] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double ss = 0.0;
+        for (int k = 0; k < kD; ++k) ss = __fma_rn((double)sx[k], (double)sx[k], ss);
+        *sinv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+    }
+    __syncthreads();
+    if (active) {
+        float y = (float)((double)x * *sinv);
+        if (BF16)
+            ((uint16_t *)out_row)[j] = (uint16_t)f32_to_bf16_rne(y);
+        else
+            ((float *)out_row)[j] = y;
+    }
+}
+
+// --------------------------------------------------------------------------
+// normalize_keys: one thread per key row (the fp64 norm is a sequential
+// chain, so a row is not split across lanes). bf16 rows are 16 x 16 B.
+__global__ __launch_bounds__(256) void k_normalize_keys_bf16(
+    const uint16_t *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
+    uint16_t *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
+    const int h = blockIdx.y;
+    if (blockIdx.x == 0)   // sink rows are labelled -1
+        for (int i = threadIdx.x; i < n_sink; i += 256) assign[(int64_t)h * L + i] = -1;
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= Lp) return;
+    const u32x4 *src = (const u32x4 *)(K + h * head_stride + (n_sink + r) * kD);
+    u32x4 w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = src[i];
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float f[8];
+        unpack8(w[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __fma_rn((double)f[e], (double)f[e], ss);
+    }
+    const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+    u32x4 *dst = (u32x4 *)(kt + ((int64_t)h * Lp + r) * kD);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float f[8];
+        unpack8(w[i], f);
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne((float)((double)f[e] * inv));
+        u32x4 v;
+        v.x = o[0] | (o[1] << 16);
+        v.y = o[2] | (o[3] << 16);
+        v.z = o[4] | (o[5] << 16);
+        v.w = o[6] | (o[7] << 16);
+        dst[i] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_normalize_keys_f32(
+    const float *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
+    float *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
+    const int h = blockIdx.y;
+    if (blockIdx.x == 0)   // sink rows are labelled -1
+        for (int i = threadIdx.x; i < n_sink; i += 256) assign[(int64_t)h * L + i] = -1;
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= Lp) return;
+    const float *src = K + h * head_stride + (n_sink + r) * kD;
+    double ss = 0.0;
+    for (int j = 0; j < kD; ++j) ss = __fma_rn((double)src[j], (double)src[j], ss);
+    const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+    float *dst = kt + ((int64_t)h * Lp + r) * kD;
+    for (int j = 0; j < kD; ++j) dst[j] = (float)((double)src[j] * inv);
+}
+
+hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *assign,
+                                 hipStream_t s) {
+    dim3 grid((unsigned)((p.Lp + 255) / 256), p.H);
+    if (p.dtype == 1)
+        hipLaunchKernelGGL(k_normalize_keys_bf16, grid, dim3(256), 0, s,
+                           (const uint16_t *)K, p.k_head_stride, p.n_sink, p.Lp,
+                           (uint16_t *)p.kt, assign, p.L);
+    else
+        hipLaunchKernelGGL(k_normalize_keys_f32, grid, dim3(256), 0, s,
+                           (const float *)K, p.k_head_stride, p.n_sink, p.Lp,
+                           (float *)p.kt, assign, p.L);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// init_centroids: mu_c = raw key at window row n_sink + s*c, s = floor(Lp/C)
+// (the page samples keys as initial centroids; evenly spaced tokens here).
+template <bool BF16>
+__global__ __launch_bounds__(128) void k_init_centroids(
+    const void *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp, int C,
+    float *__restrict__ cent, int c_base, int c_cap, void *__restrict__ mt, int Cpad) {
+    __shared__ float sx[kD];
+    __shared__ double sinv;
+    const int c = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
+    const int64_t row = n_sink + (Lp / C) * (int64_t)c;
+    const int64_t e = h * head_stride + row * kD + j;
+    const float x = BF16 ? bf16_to_f32(((const uint16_t *)K)[e]) : ((const float *)K)[e];
+    cent[((int64_t)h * c_cap + c_base + c) * kD + j] = x;
+    const int64_t mrow = ((int64_t)h * Cpad + c) * kD;
+    void *out = BF16 ? (void *)((uint16_t *)mt + mrow) : (void *)((float *)mt + mrow);
+    block_unit_row<BF16>(x, true, j, out, sx, &sinv);
+}
+
+hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cent,
+                                 hipStream_t s) {
+    dim3 grid(p.C, p.H);
+    if (p.dtype == 1)
+        hipLaunchKernelGGL(k_init_centroids<true>, grid, dim3(128), 0, s, K,
+                           p.k_head_stride, p.n_sink, p.Lp, p.C, cent, p.c_base,
+                           p.c_cap, p.mt, p.Cpad);
+    else
+        hipLaunchKernelGGL(k_init_centroids<false>, grid, dim3(128), 0, s, K,
+                           p.k_head_stride, p.n_sink, p.Lp, p.C, cent, p.c_base,
+                           p.c_cap, p.mt, p.Cpad);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// assign (bf16): scores = Kt . Mt^T on v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation, fused with a per-token argmax (ties -> lower cluster id).
+//
+// Tokens sit on the MFMA N dimension, clusters on M. A workgroup of 8 waves
+// owns 512 tokens (64 per wave = four 16-token N tiles whose B fragments stay
+// in registers for the whole kernel). Unit centroids stream through LDS in
+// chunks of 64 (four 16-row M tiles), double-buffered, XOR-swizzled so the
+// 16 lanes reading one 16-byte column of 16 rows hit distinct banks.
+//
+// MFMA 16x16x32 fragment layout (wave64): lane l supplies row/column
+// (l & 15) and the 8 consecutive k values 8*(l >> 4) .. +7 of a 32-wide k
+// step, for A and B alike; the 16x16 fp32 result gives lane l column
+// (l & 15) and rows 4*(l >> 4) + i, i = 0..3.
+constexpr int kAsWaves = 8;
+constexpr int kAsTok = 64 * kAsWaves;   // tokens per workgroup
+constexpr int kAsChunk = 64;            // clusters per LDS chunk
+
+__global__ __launch_bounds__(512) void k_assign_bf16(
+    const uint16_t *__restrict__ kt, const uint16_t *__restrict__ mt, int64_t Lp, int C,
+    int Cpad, int32_t *__restrict__ assign, int64_t L, int n_sink, int tiles_per_head) {
+    __shared__ u32x4 sA[2][kAsChunk * 16];
+    const uint32_t lin = xcd_linear(blockIdx.x, gridDim.x);
+    const int h = (int)(lin / tiles_per_head);
+    const int64_t tile = lin % tiles_per_head;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, kq = lane >> 4;
+    const int64_t tok0 = tile * kAsTok + wave * 64;
+    const u32x4 *K4 = (const u32x4 *)(kt + (int64_t)h * Lp * kD);
+    const u32x4 *M4 = (const u32x4 *)(mt + (int64_t)h * Cpad * kD);
+
+    // B fragments: N tile t = tokens tok0 + 16t + col, k step s = channels
+    // 32s + 8kq .. +7 (16-byte chunk 4s + kq of the row).
+    bf16x8 bfr[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t row = tok0 + 16 * t + col;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row < Lp) v = K4[row * 16 + 4 * s + kq];
+            bfr[t][s] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    const int nch = Cpad / kAsChunk;
+    // stage chunk 0
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int e = tid + 512 * i, r = e >> 4, q = e & 15;
+        sA[0][r * 16 + (q ^ (r & 15))] = M4[(int64_t)r * 16 + q];
+    }
+    __syncthreads();
+
+    float best[4];
+    int bid[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        best[t] = -INFINITY;
+        bid[t] = 0;
+    }
+
+    for (int ch = 0; ch < nch; ++ch) {
+        const int buf = ch & 1;
+        const bool more = (ch + 1 < nch);
+        u32x4 pf[2];
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int e = tid + 512 * i, r = e >> 4, q = e & 15;
+                pf[i] = M4[((int64_t)(ch + 1) * kAsChunk + r) * 16 + q];
+            }
+        }
+        const int cbase = ch * kAsChunk;
+        const bool last = !more;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            bf16x8 afr[4];
+            const int r = 16 * m + col;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                afr[s] = __builtin_bit_cast(bf16x8, sA[buf][r * 16 + ((4 * s + kq) ^ col)]);
+            f32x4 acc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], bfr[t][s], acc[t], 0, 0, 0);
+            const int c0 = cbase + 16 * m + 4 * kq;
+            if (!last) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (acc[t][i] > best[t]) {
+                            best[t] = acc[t][i];
+                            bid[t] = c0 + i;
+                        }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (acc[t][i] > best[t] && c0 + i < C) {
+                            best[t] = acc[t][i];
+                            bid[t] = c0 + i;
+                        }
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int e = tid + 512 * i, r = e >> 4, q = e & 15;
+                sA[buf ^ 1][r * 16 + (q ^ (r & 15))] = pf[i];
+            }
+        }
+        __syncthreads();
+    }
+
+    // merge the four row groups (lanes l, l^16, l^32, l^48) of each token
+    int res[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float b = best[t];
+        int id = bid[t];
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            const float ob = __shfl_xor(b, off);
+            const int oid = __shfl_xor(id, off);
+            if (ob > b || (ob == b && oid < id)) {
+                b = ob;
+                id = oid;
+            }
+        }
+        res[t] = id;
+    }
+    const int64_t tok = tok0 + lane;
+    const int v = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];
+    if (tok < Lp) assign[(int64_t)h * L + n_sink + tok] = v;
+}
+
+// assign (fp32): one thread per token, fp32 unit vectors, fp32 dot product
+// over j = 0..127, argmax with ties to the lower id. Used for fp32 keys.
+__global__ __launch_bounds__(256) void k_assign_f32(
+    const float *__restrict__ kt, const float *__restrict__ mt, int64_t Lp, int C, int Cpad,
+    int32_t *__restrict__ assign, int64_t L, int n_sink) {
+    const int h = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= Lp) return;
+    float k[kD];
+    const float *src = kt + ((int64_t)h * Lp + i) * kD;
+#pragma unroll
+    for (int j = 0; j < kD; ++j) k[j] = src[j];
+    float best = -INFINITY;
+    int arg = 0;
+    for (int c = 0; c < C; ++c) {
+        const float *m = mt + ((int64_t)h * Cpad + c) * kD;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < kD; ++j) s = __fmaf_rn(k[j], m[j], s);
+        if (s > best) {
+            best = s;
+            arg = c;
+        }
+    }
+    assign[(int64_t)h * L + n_sink + i] = arg;
+}
+
+hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s) {
+    if (p.dtype == 1) {
+        const int tph = (int)((p.Lp + kAsTok - 1) / kAsTok);
+        hipLaunchKernelGGL(k_assign_bf16, dim3((unsigned)(tph * p.H)), dim3(512), 0, s,
+                           (const uint16_t *)p.kt, (const uint16_t *)p.mt, p.Lp, p.C,
+                           p.Cpad, assign, p.L, p.n_sink, tph);
+    } else {
+        dim3 grid((unsigned)((p.Lp + 255) / 256), p.H);
+        hipLaunchKernelGGL(k_assign_f32, grid, dim3(256), 0, s, (const float *)p.kt,
+                           (const float *)p.mt, p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink);
+    }
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// CSR (cluster sizes, prefix sums, label-sorted token ids) by a stable
+// counting sort in three passes, no atomics:
+//  count:   per 512-token tile, each wave finds, for every lane, the lanes
+//           holding the same label (one ballot per label bit), giving the
+//           lane's rank among equal labels inside the wave; per-wave label
+//           counts in LDS turn that into a rank inside the tile, and their
+//           sums are the tile's histogram.
+//  scan:    per head and cluster, exclusive prefix over tiles (tile bases)
+//           and the cluster size; exclusive prefix over clusters -> offsets.
+//  scatter: token i of tile T with label a goes to
+//           offsets[a] + base[T][a] + rank_i.
+// Ranks grow with the token position, so each cluster lists its tokens in
+// ascending order.
+__global__ __launch_bounds__(kCsrTile) void k_csr_count(
+    const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C, int nbits,
+    int64_t ntiles, int32_t *__restrict__ tile_hist, int32_t *__restrict__ tile_rank) {
+    extern __shared__ int32_t wcnt[];   // [8 waves][C]
+    const int h = blockIdx.y;
+    const int64_t tile = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    for (int e = tid; e < 8 * C; e += kCsrTile) wcnt[e] = 0;
+    __syncthreads();
+    const int64_t i = tile * kCsrTile + tid;
+    const bool valid = i < Lp;
+    int a = valid ? assign[(int64_t)h * L + n_sink + i] : 0;
+    a = a < 0 ? 0 : (a >= C ? C - 1 : a);
+    uint64_t eq = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const int bit = (a >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        eq &= bit ? bb : ~bb;
+    }
+    const int rk = __popcll(eq & __lanemask_lt());
+    if (valid && rk == 0) wcnt[wave * C + a] = __popcll(eq);
+    __syncthreads();
+    if (valid) {
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += wcnt[w * C + a];
+        tile_rank[(int64_t)h * Lp + i] = rk + base;
+    }
+    int32_t *hist = tile_hist + ((int64_t)h * ntiles + tile) * C;
+    for (int c = tid; c < C; c += kCsrTile) {
+        int sacc = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) sacc += wcnt[w * C + c];
+        hist[c] = sacc;
+    }
+}
+
+// Exclusive scan over a block of up to 1024 threads; returns this thread's
+// exclusive prefix; *total receives the block sum.
+__device__ int block_excl_scan(int v, int *wsum, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = (blockDim.x + 63) >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int t = wsum[w];
+            wsum[w] = run;
+            run += t;
+        }
+        wsum[16] = run;
+    }
+    __syncthreads();
+    const int r = wsum[wave] + x - v;
+    *total = wsum[16];
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(1024) void k_csr_scan(
+    int32_t *__restrict__ tile_hist, int64_t ntiles, int C, int32_t *__restrict__ offsets,
+    int c_base, int c_cap, int64_t t_base) {
+    __shared__ int32_t cnt[kMaxC];
+    __shared__ int wsum[17];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    for (int c = tid; c < C; c += 1024) {
+        int32_t *colp = tile_hist + (int64_t)h * ntiles * C + c;
+        int run = 0;
+        int64_t t = 0;
+        for (; t + 4 <= ntiles; t += 4) {
+            const int v0 = colp[(t + 0) * C], v1 = colp[(t + 1) * C];
+            const int v2 = colp[(t + 2) * C], v3 = colp[(t + 3) * C];
+            colp[(t + 0) * C] = run;
+            colp[(t + 1) * C] = run + v0;
+            colp[(t + 2) * C] = run + v0 + v1;
+            colp[(t + 3) * C] = run + v0 + v1 + v2;
+            run += v0 + v1 + v2 + v3;
+        }
+        for (; t < ntiles; ++t) {
+            const int v = colp[t * C];
+            colp[t * C] = run;
+            run += v;
+        }
+        cnt[c] = run;
+    }
+    __syncthreads();
+    // two consecutive clusters per thread (C <= 2048)
+    const int k0 = 2 * tid;
+    const int a0 = k0 < C ? cnt[k0] : 0;
+    const int a1 = k0 + 1 < C ? cnt[k0 + 1] : 0;
+    int total;
+    const int ex = block_excl_scan(a0 + a1, wsum, &total);
+    int32_t *off = offsets + (int64_t)h * (c_cap + 1) + c_base;
+    if (k0 < C) off[k0] = (int32_t)(t_base + ex);
+    if (k0 + 1 < C) off[k0 + 1] = (int32_t)(t_base + ex + a0);
+    if (tid == 0) off[C] = (int32_t)(t_base + total);
+}
+
+__global__ __launch_bounds__(kCsrTile) void k_csr_scatter(
+    const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C,
+    int64_t ntiles, const int32_t *__restrict__ tile_base, const int32_t *__restrict__ tile_rank,
+    const int32_t *__restrict__ offsets, int c_base, int c_cap, int64_t t_base, int64_t t_cap,
+    int64_t token_base, int32_t *__restrict__ tokens) {
+    const int h = blockIdx.y;
+    const int64_t tile = blockIdx.x;
+    const int64_t i = tile * kCsrTile + threadIdx.x;
+    if (i >= Lp) return;
+    int a = assign[(int64_t)h * L + n_sink + i];
+    a = a < 0 ? 0 : (a >= C ? C - 1 : a);
+    const int64_t pos = (int64_t)(offsets[(int64_t)h * (c_cap + 1) + c_base + a] - t_base) +
+                        tile_base[((int64_t)h * ntiles + tile) * C + a] +
+                        tile_rank[(int64_t)h * Lp + i];
+    if (pos >= 0 && pos < Lp)
+        tokens[(int64_t)h * t_cap + t_base + pos] = (int32_t)(token_base + n_sink + i);
+}
+
+hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offsets,
+                      int32_t *tokens, hipStream_t s) {
+    int nbits = 1;
+    while ((1 << nbits) < p.C) ++nbits;
+    dim3 grid((unsigned)p.ntiles, p.H);
+    hipLaunchKernelGGL(k_csr_count, grid, dim3(kCsrTile), (size_t)8 * p.C * sizeof(int32_t), s,
+                       assign, p.L, p.n_sink, p.Lp, p.C, nbits, p.ntiles, p.tile_hist,
+                       p.tile_rank);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_csr_scan, dim3(p.H), dim3(1024), 0, s, p.tile_hist, p.ntiles, p.C,
+                       offsets, p.c_base, p.c_cap, p.t_base);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_csr_scatter, grid, dim3(kCsrTile), 0, s, assign, p.L, p.n_sink, p.Lp,
+                       p.C, p.ntiles, (const int32_t *)p.tile_hist,
+                       (const int32_t *)p.tile_rank, (const int32_t *)offsets, p.c_base,
+                       p.c_cap, p.t_base, p.t_cap, p.token_base, tokens);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// update: one workgroup per cluster walks its CSR segment. 16 row slots x
+// 16 lanes: lane (slot, q) adds channels 8q..8q+7 of rows slot, slot+16, ...
+// into fp64 accumulators; slots are combined in a fixed order (lane
+// butterflies, then the four waves in order), so the sum is reproducible.
+// mean = sum / n in fp64, stored as fp32; an empty cluster keeps its
+// centroid. The unit centroid for the next assignment is written too.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_update(
+    const void *__restrict__ K, int64_t head_stride, int64_t L, int64_t token_base,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tokens, int c_base,
+    int c_cap, int64_t t_cap, float *__restrict__ cent, void *__restrict__ mt, int Cpad) {
+    __shared__ double red[4][kD];
+    __shared__ float sx[kD];
+    __shared__ double sinv;
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = tid >> 4, q = tid & 15;
+    const int32_t *off = offsets + (int64_t)h * (c_cap + 1) + c_base + c;
+    int64_t beg = off[0], end = off[1];
+    beg = beg < 0 ? 0 : (beg > t_cap ? t_cap : beg);
+    end = end < beg ? beg : (end > t_cap ? t_cap : end);
+    const int64_t n = end - beg;
+    const int32_t *tok = tokens + (int64_t)h * t_cap;
+
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int64_t r = beg + slot; r < end; r += 16) {
+        const int64_t row = (int64_t)tok[r] - token_base;
+        if (row < 0 || row >= L) continue;
+        float f[8];
+        if (BF16) {
+            const u32x4 w = *(const u32x4 *)((const uint16_t *)K + h * head_stride + row * kD + 8 * q);
+            unpack8(w, f);
+        } else {
+            const float *src = (const float *)K + h * head_stride + row * kD + 8 * q;
+            const u32x4 w0 = *(const u32x4 *)src, w1 = *(const u32x4 *)(src + 4);
+            f[0] = __uint_as_float(w0.x); f[1] = __uint_as_float(w0.y);
+            f[2] = __uint_as_float(w0.z); f[3] = __uint_as_float(w0.w);
+            f[4] = __uint_as_float(w1.x); f[5] = __uint_as_float(w1.y);
+            f[6] = __uint_as_float(w1.z); f[7] = __uint_as_float(w1.w);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        acc[e] += __shfl_xor(acc[e], 16);
+        acc[e] += __shfl_xor(acc[e], 32);
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
+    }
+    __syncthreads();
+    const bool act = tid < kD;
+    float mu = 0.f;
+    float *cp = cent + ((int64_t)h * c_cap + c_base + c) * kD;
+    if (act) {
+        const double ssum = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+        mu = (n > 0) ? (float)(ssum / (double)n) : cp[tid];
+        cp[tid] = mu;
+    }
+    const int64_t mrow = ((int64_t)h * Cpad + c) * kD;
+    void *out = BF16 ? (void *)((uint16_t *)mt + mrow) : (void *)((float *)mt + mrow);
+    block_unit_row<BF16>(mu, act, tid, out, sx, &sinv);
+}
+
+hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
+                         const int32_t *tokens, float *cent, hipStream_t s) {
+    dim3 grid(p.C, p.H);
+    if (p.dtype == 1)
+        hipLaunchKernelGGL(k_update<true>, grid, dim3(256), 0, s, K, p.k_head_stride, p.L,
+                           p.token_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap, cent,
+                           p.mt, p.Cpad);
+    else
+        hipLaunchKernelGGL(k_update<false>, grid, dim3(256), 0, s, K, p.k_head_stride, p.L,
+                           p.token_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap, cent,
+                           p.mt, p.Cpad);
+    return hipGetLastError();
+}
+
+}  // namespace ckv

@@ -1,0 +1,180 @@
+"""Host-only checks of the C ABI (no GPU, no kernel launch).
+
+* libckv.so loads and exports every function include/ckv.h declares;
+* the ctypes structures of the binding match the C layout gcc computes
+  from the header;
+* invalid descriptors, missing pointers and short workspaces return their
+  status code before anything is enqueued.
+"""
+import ctypes as ct
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_decode_attention_ckv_amd as ck
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ckv.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckv_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ck.load()
+    names = _declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ck.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ckv_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header(tmp_path):
+    structs = {"ckv_cluster_desc": ck.ClusterDesc, "ckv_select_desc": ck.SelectDesc,
+               "ckv_attn_desc": ck.AttnDesc}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ckv.h"', "int main(void){"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)],
+                   check=True)
+    got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    for line in got.splitlines():
+        cname, field, val = line.split()
+        py = structs[cname]
+        want = ct.sizeof(py) if field == "size" else getattr(py, field).offset
+        assert int(val) == want, line
+
+
+def test_status_strings():
+    for s in range(5):
+        assert ck.ckv_status_string(s)
+    assert ck.ckv_status_string(99) == "unknown status"
+    assert ck.ckv_abi_version() == 1
+
+
+def _cl(**kw):
+    base = dict(H=2, d=128, L=1000, k_head_stride=1000 * 128, token_base=0, n_sink=16, C=12,
+                iters=3, dtype=1, c_base=0, c_cap=12, t_base=0, t_cap=984)
+    base.update(kw)
+    return ck.ClusterDesc(**base)
+
+
+FAKE = ct.c_void_p(0x1000)   # never dereferenced: every case fails validation
+
+
+def _call_cluster(desc, ws_bytes=None, nullK=False):
+    lib = ck.load()
+    need = lib.ckv_cluster_workspace(ct.byref(desc))
+    ws = ws_bytes if ws_bytes is not None else need
+    return lib.ckv_cluster(ct.byref(desc), None if nullK else FAKE, FAKE, FAKE, FAKE, FAKE,
+                           FAKE if ws else None, ws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), ck.CKV_ERR_UNSUPPORTED),
+    (dict(d=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(C=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(C=985, c_cap=985), ck.CKV_ERR_INVALID_ARG),          # C > L - n_sink
+    (dict(L=5000, k_head_stride=5000 * 128, C=2049, c_cap=2049, t_cap=4984),
+     ck.CKV_ERR_UNSUPPORTED),
+    (dict(iters=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(n_sink=-1), ck.CKV_ERR_INVALID_ARG),
+    (dict(n_sink=1000), ck.CKV_ERR_INVALID_ARG),
+    (dict(k_head_stride=1000 * 128 - 1), ck.CKV_ERR_INVALID_ARG),
+    (dict(c_cap=11), ck.CKV_ERR_INVALID_ARG),
+    (dict(c_base=4, c_cap=15), ck.CKV_ERR_INVALID_ARG),
+    (dict(t_cap=983), ck.CKV_ERR_INVALID_ARG),
+    (dict(dtype=7), ck.CKV_ERR_INVALID_ARG),
+    (dict(H=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(token_base=-3), ck.CKV_ERR_INVALID_ARG),
+])
+def test_cluster_rejects_bad_descriptors(kw, status):
+    d = _cl(**kw)
+    assert ck.load().ckv_cluster_workspace(ct.byref(d)) == 0
+    assert _call_cluster(d, ws_bytes=0) == status
+
+
+def test_cluster_workspace_and_pointer_checks():
+    d = _cl()
+    need = ck.load().ckv_cluster_workspace(ct.byref(d))
+    # unit keys (bf16) + unit centroids + tile histograms + tile ranks
+    assert need >= 2 * 984 * 128 * 2 + 2 * 64 * 128 * 2 + 2 * 2 * 12 * 4 + 2 * 984 * 4
+    assert _call_cluster(d, ws_bytes=need - 1) == ck.CKV_ERR_WORKSPACE
+    assert _call_cluster(d, nullK=True) == ck.CKV_ERR_INVALID_ARG
+
+
+def _sel(**kw):
+    base = dict(H=2, G=4, d=128, C=10, c_cap=10, n_sink=16, t_cap=500, pending_begin=0,
+                n_pending=0, B=64, dtype=1)
+    base.update(kw)
+    return ck.SelectDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), ck.CKV_ERR_INVALID_ARG), (dict(G=9), ck.CKV_ERR_INVALID_ARG),
+    (dict(d=96), ck.CKV_ERR_UNSUPPORTED), (dict(C=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(C=11), ck.CKV_ERR_INVALID_ARG), (dict(B=15), ck.CKV_ERR_INVALID_ARG),
+    (dict(n_pending=60), ck.CKV_ERR_INVALID_ARG), (dict(pending_begin=-1), ck.CKV_ERR_INVALID_ARG),
+    (dict(C=2049, c_cap=4096), ck.CKV_ERR_UNSUPPORTED), (dict(t_cap=0), ck.CKV_ERR_INVALID_ARG),
+])
+def test_select_rejects_bad_descriptors(kw, status):
+    d = _sel(**kw)
+    lib = ck.load()
+    assert lib.ckv_select_workspace(ct.byref(d)) == 0
+    assert lib.ckv_select(ct.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == status
+
+
+def test_select_workspace_and_pointers():
+    d = _sel()
+    lib = ck.load()
+    need = lib.ckv_select_workspace(ct.byref(d))
+    assert need >= 2 * 10 * 8
+    assert lib.ckv_select(ct.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                          None) == ck.CKV_ERR_WORKSPACE
+    assert lib.ckv_select(ct.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
+                          None) == ck.CKV_ERR_INVALID_ARG
+
+
+def _att(**kw):
+    base = dict(H=2, G=4, d=128, B=64, kv_head_stride=300 * 128, kv_rows=300, scale=0.0, dtype=1)
+    base.update(kw)
+    return ck.AttnDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), ck.CKV_ERR_INVALID_ARG), (dict(d=256), ck.CKV_ERR_UNSUPPORTED),
+    (dict(B=0), ck.CKV_ERR_INVALID_ARG), (dict(kv_rows=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(kv_head_stride=100), ck.CKV_ERR_INVALID_ARG), (dict(dtype=2), ck.CKV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ck.CKV_ERR_INVALID_ARG),
+])
+def test_attn_rejects_bad_descriptors(kw, status):
+    d = _att(**kw)
+    lib = ck.load()
+    assert lib.ckv_attn_workspace(ct.byref(d)) == 0
+    assert lib.ckv_sparse_attn(ct.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                               None) == status
+
+
+def test_attn_workspace_and_pointers():
+    d = _att()
+    lib = ck.load()
+    need = lib.ckv_attn_workspace(ct.byref(d))
+    assert need >= 2 * 4 * 2 * 130 * 4
+    assert lib.ckv_sparse_attn(ct.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                               None) == ck.CKV_ERR_WORKSPACE
+    assert lib.ckv_sparse_attn(ct.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need,
+                               None) == ck.CKV_ERR_INVALID_ARG
