@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of cluster-granular KV selection on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input
+(the Llama-3.1-8B-shaped 32k layer by default): ckv_cluster over the prompt
+(cosine K-means, 10 iterations) followed by the workload's decode steps,
+each a ckv_select + ckv_sparse_attn with a fresh query. Inputs are resident
+in HBM before timing starts. The clustering call and the decode loop are
+each captured once as a HIP graph and replayed; every replay's results are
+checked bitwise against an eager run before timing.
+
+Prints one JSON line. `value` is the decode-step latency (select + sparse
+attention, microseconds per step); the clustering time per layer and the
+whole-step time are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("ms per layer ckv_cluster at L=32k; µs/decode step select+sparse attn; "
+          "% roofline")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed steps")
+    ap.add_argument("--workload", default="llama8b_layer_32k")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="decode steps per step (default: the workload's)")
+    ap.add_argument("--reps", type=int, default=256,
+                    help="back-to-back launches per live per-call timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Case:
+    """Device-resident inputs and preallocated outputs/workspaces."""
+
+    def __init__(self, wl, T, dev):
+        import numpy as np
+        import torch
+
+        import sparse_decode_attention_ckv_amd as ck
+        import synth
+        self.wl, self.T = wl, T
+        t0 = time.time()
+        K, V, _ = synth.make_kv(wl)
+        Q, _ = synth.make_query_steps(wl, T)
+        log(f"inputs drawn in {time.time() - t0:.1f}s")
+
+        def bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        assert wl.dtype == "bf16"
+        self.K, self.V, self.Q = bf(K), bf(V), bf(Q)
+        H, G, L, d, C, B = wl.H, wl.G, wl.L, wl.d, wl.C, wl.B
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.cent = torch.empty((H, C, d), dtype=torch.float32, device=dev)
+        self.asg = torch.empty((H, L), **i32)
+        self.off = torch.empty((H, C + 1), **i32)
+        self.tok = torch.empty((H, L - wl.n_sink), **i32)
+        self.idx = torch.empty((T, H, B), **i32)
+        self.nsel = torch.empty((T, H), **i32)
+        self.O = torch.empty((T, H * G, d), dtype=torch.float32, device=dev)
+        cd = ck.ClusterDesc(H=H, d=d, L=L, k_head_stride=L * d, token_base=0,
+                            n_sink=wl.n_sink, C=C, iters=wl.iters, dtype=ck.CKV_BF16,
+                            c_base=0, c_cap=C, t_base=0, t_cap=L - wl.n_sink)
+        sd = ck.SelectDesc(H=H, G=G, d=d, C=C, c_cap=C, n_sink=wl.n_sink,
+                           t_cap=L - wl.n_sink, pending_begin=0, n_pending=0, B=B,
+                           dtype=ck.CKV_BF16)
+        ad = ck.AttnDesc(H=H, G=G, d=d, B=B, kv_head_stride=L * d, kv_rows=L, scale=0.0,
+                         dtype=ck.CKV_BF16)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.ws_c = torch.empty(ck.ckv_cluster_workspace(cd), **u8)
+        self.ws_s = torch.empty(ck.ckv_select_workspace(sd), **u8)
+        self.ws_a = torch.empty(ck.ckv_attn_workspace(ad), **u8)
+        self.ck = ck
+
+    def cluster(self):
+        wl = self.wl
+        self.ck.ckv_cluster(self.K, wl.n_sink, wl.C, wl.iters, centroids=self.cent,
+                            assign=self.asg, csr_offsets=self.off, csr_tokens=self.tok,
+                            workspace=self.ws_c)
+
+    def select(self, t):
+        wl = self.wl
+        self.ck.ckv_select(self.Q[t], self.cent, self.off, self.tok, wl.C, wl.B,
+                           n_sink=wl.n_sink, idx=self.idx[t], n_sel=self.nsel[t],
+                           workspace=self.ws_s)
+
+    def attn(self, t):
+        self.ck.ckv_sparse_attn(self.Q[t], self.K, self.V, self.idx[t], self.nsel[t],
+                                out=self.O[t], workspace=self.ws_a)
+
+    def decode(self):
+        for t in range(self.T):
+            self.select(t)
+            self.attn(t)
+
+    def snapshot(self):
+        return [x.clone() for x in (self.cent, self.asg, self.off, self.tok, self.idx,
+                                    self.nsel, self.O)]
+
+
+def capture(fn):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def time_graph(g, reps=1):
+    """Average ms of `reps` back-to-back replays, HIP events on the stream the
+    graph is launched on (the current stream)."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def cpu_baseline(case, sample_steps, cluster_heads):
+    """The oracle as it stands, single-threaded, on a bounded sample of the
+    same workload: `sample_steps` decode steps (all KV heads, selection on the
+    GPU's centroids/CSR) and one K-means iteration on `cluster_heads` heads."""
+    import numpy as np
+    import torch
+
+    import oracle
+    wl = case.wl
+    mu = case.cent.double().cpu().numpy()
+    off = case.off.cpu().numpy()
+    tok = case.tok.cpu().numpy()
+    Kf = case.K.double().cpu().numpy()
+    Vf = case.V.double().cpu().numpy()
+    Qf = case.Q[:sample_steps].double().cpu().numpy()
+    oracle.select(Qf[0], mu, off, tok, wl.C, wl.n_sink, wl.B, G=wl.G)   # load the library
+    t0 = time.perf_counter()
+    for t in range(sample_steps):
+        idx, ns, _ = oracle.select(Qf[t], mu, off, tok, wl.C, wl.n_sink, wl.B, G=wl.G)
+        oracle.attn(Qf[t], Kf, Vf, idx, ns, G=wl.G)
+    dec_s = (time.perf_counter() - t0) / sample_steps
+    t0 = time.perf_counter()
+    for h in range(cluster_heads):
+        mu0 = oracle.init_centroids(Kf[h], wl.n_sink, wl.C)
+        a, _ = oracle.assign(Kf[h], wl.n_sink, mu0, mode=oracle.MIRROR)
+        oracle.update(Kf[h], wl.n_sink, a, mu0, mode=oracle.MIRROR)
+    it_s = (time.perf_counter() - t0) / cluster_heads
+    return {
+        "value": round(dec_s * 1e6, 1), "unit": "us/decode_step", "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{sample_steps} decode steps (select + sparse attention, all {wl.H} KV "
+                   f"heads) and 1 K-means iteration on {cluster_heads} of {wl.H} heads, "
+                   f"single-threaded C oracle (fp64)"),
+        "cluster_ms_per_layer_extrapolated": round(it_s * wl.H * wl.iters * 1e3, 1),
+        "host_cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): every KV head is an independent problem, so a multi-GPU run would "
+              "shard heads with no communication; it is not built or measured here.",
+              flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    wl = synth.workload(args.workload)
+    T = wl.steps if args.decode_steps is None else args.decode_steps
+    case = Case(wl, T, dev)
+
+    # eager reference run
+    case.cluster()
+    case.decode()
+    torch.cuda.synchronize()
+    ref = case.snapshot()
+
+    # graphs: the clustering call and the whole decode loop
+    g_cluster = capture(case.cluster)
+    g_decode = capture(case.decode)
+    for rep in range(2):
+        g_cluster.replay()
+        g_decode.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, case.snapshot()):
+            assert torch.equal(a, b), "graph replay differs from the eager run"
+        torch.cuda.synchronize()
+    log("graph replays match the eager run bitwise")
+
+    def step():
+        g_cluster.replay()
+        g_decode.replay()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    t_wall = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(args.steps):
+        ev[3 * k].record()
+        g_cluster.replay()
+        ev[3 * k + 1].record()
+        g_decode.replay()
+        ev[3 * k + 2].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / args.steps
+    cl_ms = sum(ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(args.steps)) / args.steps
+    dec_ms = sum(ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(args.steps)) / args.steps
+    dec_us = dec_ms * 1e3 / T
+    log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): cluster {cl_ms:.3f} ms, "
+        f"decode {dec_us:.2f} us/step")
+
+    # live per-call timings (back-to-back launches of one call, HIP events)
+    g_sel = capture(lambda: [case.select(0) for _ in range(args.reps)])
+    g_att = capture(lambda: [case.attn(0) for _ in range(args.reps)])
+    sel_us = time_graph(g_sel) * 1e3 / args.reps
+    att_us = time_graph(g_att) * 1e3 / args.reps
+    torch.cuda.synchronize()
+    H, G, d, C, B = wl.H, wl.G, wl.d, wl.C, wl.B
+    n_sel = case.nsel[0].cpu()
+    e = 2  # bf16 bytes
+    att_bytes = sum(2 * int(n) * d * e + 4 * B + G * d * e + G * d * 4 for n in n_sel)
+    sel_bytes = sum(C * d * 4 + 4 * (C + 1) + 4 * (int(n) - wl.n_sink) + 4 * B + G * d * e
+                    for n in n_sel)
+    Lp = wl.L - wl.n_sink
+    assign_flop = 2.0 * Lp * C * d * H * wl.iters
+    kernels = {
+        "ckv_sparse_attn": {"us_per_call": round(att_us, 3), "bytes": att_bytes,
+                            "GB/s": round(att_bytes / att_us / 1e3, 1),
+                            "calls_per_step": T},
+        "ckv_select": {"us_per_call": round(sel_us, 3), "bytes": sel_bytes,
+                       "GB/s": round(sel_bytes / sel_us / 1e3, 1), "calls_per_step": T},
+        "ckv_cluster": {"ms_per_call": round(cl_ms, 4), "assign_flop": assign_flop,
+                        "assign_TFLOP/s_over_whole_call": round(assign_flop / cl_ms / 1e9, 1),
+                        "calls_per_step": 1},
+    }
+    share = {"ckv_sparse_attn": att_us * T / 1e3, "ckv_select": sel_us * T / 1e3,
+             "ckv_cluster": cl_ms}
+    dom = max(share, key=share.get)
+    if dom == "ckv_cluster":
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(assign_flop / cl_ms / 1e9, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        k = kernels[dom]
+        roof = {"kernel": dom, "bound": "hbm", "achieved": k["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    log(f"per call: select {sel_us:.2f} us, attn {att_us:.2f} us; dominant {dom}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(case, sample_steps=min(T, 64), cluster_heads=1)
+
+    out = {
+        "metric": METRIC, "value": round(dec_us, 3), "unit": "us/decode_step",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "kv_heads": H, "q_heads_per_kv": G, "d": d, "L": wl.L,
+                   "n_sink": wl.n_sink, "C": C, "iters": wl.iters, "B": B,
+                   "decode_steps": T, "parallelism": "none (1 GPU)"},
+        "cluster_ms_per_layer": round(cl_ms, 4),
+        "decode_us_per_step": round(dec_us, 3),
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

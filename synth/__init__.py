@@ -34,13 +34,14 @@ reproducible on any host with the same numpy.
 from __future__ import annotations
 
 import dataclasses
+import functools
 from typing import Optional, Sequence
 
 import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "bf16_bits", "bf16_to_f32",
-    "KVHead", "make_head", "make_kv", "make_queries", "make_appended",
+    "KVHead", "make_head", "make_kv", "make_queries", "make_query_steps", "make_appended",
     "planted_head",
 ]
 
@@ -159,6 +160,11 @@ def _unit_dirs(rng, n: int, d: int) -> np.ndarray:
     return g / np.linalg.norm(g, axis=1, keepdims=True)
 
 
+@functools.lru_cache(maxsize=256)
+def _head_dirs(seed: int, head: int, n: int, d: int) -> np.ndarray:
+    return _unit_dirs(_rng(seed, head, _S_DIRS), n, d)
+
+
 def _draw_keys(rng, dirs: np.ndarray, n: int, outl: np.ndarray,
                amp_mean=4.0, amp_sd=0.5, noise_sd=0.3, gain=20.0):
     d = dirs.shape[1]
@@ -193,7 +199,7 @@ def _outliers(wl: Workload, head: int) -> np.ndarray:
 def make_head(wl: Workload, head: int, L: Optional[int] = None) -> KVHead:
     """Draw keys/values of one KV head (rows 0..L-1 of the prompt)."""
     L = wl.L if L is None else L
-    dirs = _unit_dirs(_rng(wl.seed, head, _S_DIRS), wl.n_dirs, wl.d)
+    dirs = _head_dirs(wl.seed, head, wl.n_dirs, wl.d)
     outl = _outliers(wl, head)
     k, z = _draw_keys(_rng(wl.seed, head, _S_KEYS), dirs, L, outl)
     v = _rng(wl.seed, head, _S_VALS).standard_normal((L, wl.d))
@@ -228,7 +234,7 @@ def make_queries(wl: Workload, step: int, heads: Optional[Sequence[int]] = None)
     hs = list(range(wl.H)) if heads is None else list(heads)
     rows = []
     for h in hs:
-        dirs = _unit_dirs(_rng(wl.seed, h, _S_DIRS), wl.n_dirs, wl.d)
+        dirs = _head_dirs(wl.seed, h, wl.n_dirs, wl.d)
         outl = _outliers(wl, h)
         k, _ = _draw_keys(_rng(wl.seed, h, _S_QUERY, step), dirs, wl.G, outl)
         rows.append(k)
@@ -236,11 +242,18 @@ def make_queries(wl: Workload, step: int, heads: Optional[Sequence[int]] = None)
     return _to_dtype(q, wl.dtype)
 
 
+def make_query_steps(wl: Workload, steps: int, heads: Optional[Sequence[int]] = None):
+    """Queries of decode steps 0..steps-1 stacked: ([steps][H*G][d] storage,
+    float32 values)."""
+    st, fv = zip(*(make_queries(wl, t, heads) for t in range(steps)))
+    return np.stack(st), np.stack(fv)
+
+
 def make_appended(wl: Workload, head: int, n: int):
     """Rows appended during decode for the incremental workload: keys drawn
     from the head's directions plus ``new_dirs`` new ones (uniform over
     all), values N(0, 1). Returns (K storage, V storage, Kf, Vf)."""
-    dirs = _unit_dirs(_rng(wl.seed, head, _S_DIRS), wl.n_dirs, wl.d)
+    dirs = _head_dirs(wl.seed, head, wl.n_dirs, wl.d)
     if wl.new_dirs:
         dirs = np.concatenate(
             [dirs, _unit_dirs(_rng(wl.seed, head, _S_APPDIRS), wl.new_dirs, wl.d)])
