@@ -39,7 +39,9 @@
  *   - sinks (and, for incremental decode, not-yet-clustered tokens) are always
  *     selected and count toward the budget B;
  *   - the last admitted cluster is trimmed to its lowest positions;
- *   - idx order: sinks, pending, then clusters in rank order, each ascending.
+ *   - idx order: sinks, pending, then the admitted clusters in ascending
+ *     cluster id, each ascending (the page fixes which tokens are selected,
+ *     not the order in which they are handed to attention).
  *   - fixed association of the selection score (see orc_score).
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -shared -fPIC ckv_oracle.c -lm
@@ -320,11 +322,12 @@ static int orc_rank_cmp(const void *pa, const void *pb)
  *   q_g   = sum of the G query rows of KV head g (fp64, in row order);
  *   s_c   = orc_score(q_g, mu_c);
  *   order = clusters by (s desc, c asc);
- *   walk the order taking each cluster's tokens (CSR segment, ascending)
- *   until B_eff = B - n_sink - n_pending tokens are taken; the last cluster
- *   taken is cut to the tokens that still fit (its lowest positions);
+ *   walk the order, taking each cluster's tokens until B_eff = B - n_sink -
+ *   n_pending tokens are taken; the last cluster taken is cut to the tokens
+ *   that still fit (the first ones of its CSR segment, its lowest positions);
  *   idx   = [0 .. n_sink) ++ [pending_begin .. pending_begin + n_pending)
- *           ++ walked tokens, then -1 up to B; n_sel = number written.
+ *           ++ the taken tokens of each cluster, clusters in ascending id,
+ *           then -1 up to B; n_sel = number written.
  * q: [H*G][d]; mu: [H][c_stride][d]; offsets: [H][c_stride+1] (absolute
  * positions into the head's token row); tokens: [H][t_stride]; idx [H][B].
  * If scores is not NULL it receives [H][C] scores. Returns 0, or -1 if
@@ -338,6 +341,7 @@ int orc_select(int H, int G, int d, const double *q, int C, int c_stride,
     if ((int64_t)B < n_sink + n_pending) return -1;
     double *qg = malloc(sizeof(double) * d);
     orc_rank_t *rk = malloc(sizeof(orc_rank_t) * (size_t)(C > 0 ? C : 1));
+    int64_t *take = malloc(sizeof(int64_t) * (size_t)(C > 0 ? C : 1));
     for (int g = 0; g < H; ++g) {
         for (int j = 0; j < d; ++j) {
             double a = 0.0;
@@ -354,22 +358,27 @@ int orc_select(int H, int G, int d, const double *q, int C, int c_stride,
         }
         qsort(rk, (size_t)C, sizeof(orc_rank_t), orc_rank_cmp);
 
+        /* walk the rank order: how many tokens each cluster gives */
+        int64_t budget = (int64_t)B - n_sink - n_pending;
+        int64_t filled = 0;
+        for (int c = 0; c < C; ++c) take[c] = 0;
+        for (int r = 0; r < C && filled < budget; ++r) {
+            int c = rk[r].c;
+            int64_t n = off[c + 1] - off[c];
+            take[c] = n < budget - filled ? n : budget - filled;
+            filled += take[c];
+        }
+        /* emit: sinks, pending, then clusters in ascending id */
         int32_t *out = idx + (int64_t)g * B;
         int64_t w = 0;
         for (int i = 0; i < n_sink; ++i) out[w++] = i;
         for (int64_t i = 0; i < n_pending; ++i) out[w++] = (int32_t)(pending_begin + i);
-        int64_t budget = (int64_t)B - n_sink - n_pending;
-        int64_t filled = 0;
-        for (int r = 0; r < C && filled < budget; ++r) {
-            int c = rk[r].c;
-            int64_t beg = off[c], n = off[c + 1] - off[c];
-            int64_t take = n < budget - filled ? n : budget - filled;
-            for (int64_t t = 0; t < take; ++t) out[w++] = tok[beg + t];
-            filled += take;
-        }
+        for (int c = 0; c < C; ++c)
+            for (int64_t t = 0; t < take[c]; ++t) out[w++] = tok[off[c] + t];
         n_sel[g] = (int32_t)w;
         while (w < B) out[w++] = -1;
     }
+    free(take);
     free(rk);
     free(qg);
     return 0;

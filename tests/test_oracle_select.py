@@ -42,7 +42,8 @@ def _int_mu_for_scores(scores, d=D):
 
 def _brute_greedy(scores, lists, n_sink, B, pending=()):
     """Enumerate all cluster orders, keep the one that is non-increasing in
-    score with ascending ids among equal scores, and walk it greedily."""
+    score with ascending ids among equal scores, walk it greedily, then list
+    sinks, pending and each admitted cluster's taken tokens by cluster id."""
     C = len(scores)
     chosen = None
     for perm in itertools.permutations(range(C)):
@@ -52,13 +53,16 @@ def _brute_greedy(scores, lists, n_sink, B, pending=()):
         if ok:
             assert chosen is None, "order must be unique"
             chosen = perm
-    out = list(range(n_sink)) + list(pending)
     budget = B - n_sink - len(pending)
+    taken = {}
     for c in chosen:
-        room = budget - (len(out) - n_sink - len(pending))
+        room = budget - sum(taken.values())
         if room <= 0:
             break
-        out += list(lists[c])[:room]
+        taken[c] = min(len(lists[c]), room)
+    out = list(range(n_sink)) + list(pending)
+    for c in sorted(taken):
+        out += list(lists[c])[:taken[c]]
     return out
 
 
@@ -118,7 +122,7 @@ def test_every_token_its_own_cluster_is_exact_topk():
     s = (K[n_sink:].astype(np.int64) @ q[0].astype(np.int64))  # exact
     top = np.lexsort((np.arange(Lp), -s))[:Bp] + n_sink          # ties -> lower
     assert list(idx[0, :n_sink]) == list(range(n_sink))
-    assert list(idx[0, n_sink:ns[0]]) == list(top)
+    assert list(idx[0, n_sink:ns[0]]) == sorted(top)              # cluster id = position
 
 
 def test_single_cluster_takes_first_positions():
@@ -155,6 +159,7 @@ def test_pending_tokens_always_selected_and_counted():
     q, mu = _int_mu_for_scores([1, 3, 2])
     idx, ns, _ = oracle.select(q, mu, off, tok, 3, 16, 16 + 3 + 4,
                                pending_begin=22, n_pending=3)
+    # ranks: cluster 1 (3 tokens), cluster 2 (1 token); emitted by cluster id
     want = list(range(16)) + [22, 23, 24] + [17, 19, 20, 21]
     assert list(idx[0, :ns[0]]) == want
 
