@@ -88,7 +88,7 @@ class Case:
                          dtype=ck.CKV_BF16)
         u8 = dict(dtype=torch.uint8, device=dev)
         self.ws_c = torch.empty(ck.ckv_cluster_workspace(cd), **u8)
-        self.ws_s = torch.empty(ck.ckv_select_workspace(sd), **u8)
+        self.ws_s = torch.empty(max(ck.ckv_select_workspace(sd), 1), **u8)
         self.ws_a = torch.empty(ck.ckv_attn_workspace(ad), **u8)
         self.ck = ck
 

@@ -14,6 +14,8 @@
  *   - Tensor pointers are DEVICE pointers owned by the caller. The library
  *     never allocates, frees or keeps them; the caller also provides the
  *     scratch workspace, sized by the matching *_workspace() query.
+ *   - A workspace serves one call at a time: calls sharing one must be
+ *     ordered on a stream. A zero-byte workspace may be passed as NULL.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Work is enqueued on it; no call synchronises the host. Calls on one
  *     stream run in order. Calls with distinct workspaces may run
@@ -173,7 +175,7 @@ typedef struct {
     int32_t H;              /* KV heads, >= 1 */
     int32_t G;              /* query heads per KV head, 1..8 */
     int32_t d;              /* must be 128 */
-    int32_t B;              /* idx row stride (max selected rows), >= 1 */
+    int32_t B;              /* idx row stride (max selected rows), 1..32768 */
     int64_t kv_head_stride; /* elements between heads of K and V, >= kv_rows*d */
     int64_t kv_rows;        /* valid rows per head, >= 1 */
     float scale;            /* softmax scale; <= 0 means 1/sqrt(d) */

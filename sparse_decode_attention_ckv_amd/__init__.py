@@ -140,10 +140,13 @@ def _check(status: int, where: str):
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    """Caller workspace, a fresh one, or None when the call needs none."""
     if ws is not None:
         _need(ws.is_cuda and ws.numel() * ws.element_size() >= nbytes, "workspace too small")
         return ws
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ calls --

@@ -62,6 +62,8 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     o += align_up((size_t)p->H * p->ntiles * p->C * sizeof(int32_t));
     p->tile_rank = ws ? (int32_t *)(ws + o) : nullptr;
     o += align_up((size_t)p->H * p->Lp * sizeof(int32_t));
+    p->counts = ws ? (int32_t *)(ws + o) : nullptr;
+    o += align_up((size_t)p->H * p->C * sizeof(int32_t));
     *bytes = o;
 }
 
@@ -78,22 +80,23 @@ int check_select(const ckv_select_desc *d) {
     return CKV_OK;
 }
 
-size_t select_bytes(const ckv_select_desc *d) {
-    return align_up((size_t)d->H * d->C * sizeof(double));
-}
+// selection keeps everything in LDS: no workspace
+size_t select_bytes(const ckv_select_desc *) { return 0; }
 
 int check_attn(const ckv_attn_desc *d) {
     if (!d) return CKV_ERR_INVALID_ARG;
     if (d->H < 1 || d->G < 1 || d->G > 8 || !dtype_ok(d->dtype)) return CKV_ERR_INVALID_ARG;
     if (d->d != kD) return d->d < 1 ? CKV_ERR_INVALID_ARG : CKV_ERR_UNSUPPORTED;
     if (d->B < 1 || d->kv_rows < 1) return CKV_ERR_INVALID_ARG;
+    if (d->B > kMaxSplits * kAttnSplitRows) return CKV_ERR_UNSUPPORTED;
     if (d->kv_head_stride < d->kv_rows * kD) return CKV_ERR_INVALID_ARG;
     if (!(d->scale == d->scale) || isinf(d->scale)) return CKV_ERR_INVALID_ARG;
     return CKV_OK;
 }
 
-int attn_splits(const ckv_attn_desc *d) { return (d->B + 31) / 32; }
+int attn_splits(const ckv_attn_desc *d) { return (d->B + kAttnSplitRows - 1) / kAttnSplitRows; }
 
+// workspace: split partials [H*G][S][2+d]
 size_t attn_bytes(const ckv_attn_desc *d) {
     const size_t es = d->dtype == CKV_BF16 ? sizeof(float) : sizeof(double);
     return align_up((size_t)d->H * d->G * attn_splits(d) * (kD + 2) * es);
@@ -169,7 +172,8 @@ int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroid
     if (!q || !centroids || !csr_offsets || !csr_tokens || !idx || !n_sel)
         return CKV_ERR_INVALID_ARG;
     if (!aligned16(centroids)) return CKV_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < select_bytes(desc)) return CKV_ERR_WORKSPACE;
+    if (workspace_bytes < select_bytes(desc) || (select_bytes(desc) > 0 && !workspace))
+        return CKV_ERR_WORKSPACE;
     SelectPlan p;
     p.H = desc->H;
     p.G = desc->G;
@@ -181,7 +185,6 @@ int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroid
     p.t_cap = desc->t_cap;
     p.pending_begin = desc->pending_begin;
     p.n_pending = desc->n_pending;
-    p.scores = (double *)workspace;
     return launch_status(launch_select(p, q, centroids, csr_offsets, csr_tokens, idx, n_sel,
                                        (hipStream_t)stream));
 }

@@ -5,19 +5,24 @@
 // (long-context inference and KV compression): the decode output is
 // approximated by softmax(q K_S^T / sqrt(d)) V_S over the B selected rows.
 //
-// The step is HBM-bound: every selected K and V row (256 B each in bf16) is
-// read once, and the G query heads of a KV head share that gather.
-//   partial  grid (splits, KV heads): a workgroup takes R = 32 consecutive
-//            entries of idx; 16 lanes per row, 16 bytes per lane; scores for
-//            the G heads, max, exp, weighted V sum -> (m, l, acc[d]) per head
-//   combine  one workgroup per query head merges the splits:
-//            o = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s
+// Two kernels per decode step, HBM-bound: every selected K and V row (256 B
+// each in bf16) is read once, and the G query heads of a KV head share that
+// gather.
+//  * partial, grid (splits, KV heads): a workgroup takes R = 64 consecutive
+//    entries of idx: 16 lanes per row, 16 bytes per lane, the idx, q and then
+//    all K/V loads of a thread in flight at once; scores for the G heads,
+//    split max, exp, weighted V sum -> (m, l, acc[d]) per query head;
+//  * combine, one workgroup per query head: o = sum_s e^{m_s - M} acc_s /
+//    sum_s e^{m_s - M} l_s, summed in split order.
+// A kernel boundary hands the partials over: on this multi-XCD part a
+// per-workgroup device-scope release fence costs more than a launch.
 // bf16 inputs compute in fp32; fp32 inputs compute in fp64.
 #include "ckv_dev.h"
 
 namespace ckv {
 
-constexpr int kAttnRows = 32;   // rows of idx per workgroup (split)
+constexpr int kAttnRows = kAttnSplitRows;   // rows of idx per workgroup (split)
+constexpr int kRowsPerSlot = kAttnRows / 16;
 
 template <typename T> struct Acc;
 template <> struct Acc<uint16_t> { typedef float type; };
@@ -26,67 +31,91 @@ template <> struct Acc<float> { typedef double type; };
 __device__ __forceinline__ float ex(float x) { return __expf(x); }
 __device__ __forceinline__ double ex(double x) { return exp(x); }
 
+// 8 consecutive elements held as 16-byte chunks (1 for bf16, 2 for fp32)
 template <typename T>
-__device__ __forceinline__ void load8(const T *p, typename Acc<T>::type *f);
-
+__device__ __forceinline__ void unpack_chunks(const u32x4 *w, typename Acc<T>::type *f);
 template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float *f) {
-    unpack8(*(const u32x4 *)p, f);
+__device__ __forceinline__ void unpack_chunks<uint16_t>(const u32x4 *w, float *f) {
+    unpack8(w[0], f);
 }
 template <>
-__device__ __forceinline__ void load8<float>(const float *p, double *f) {
-    const u32x4 a = *(const u32x4 *)p, b = *(const u32x4 *)(p + 4);
-    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
-    f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
-    f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y);
-    f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
+__device__ __forceinline__ void unpack_chunks<float>(const u32x4 *w, double *f) {
+    f[0] = __uint_as_float(w[0].x); f[1] = __uint_as_float(w[0].y);
+    f[2] = __uint_as_float(w[0].z); f[3] = __uint_as_float(w[0].w);
+    f[4] = __uint_as_float(w[1].x); f[5] = __uint_as_float(w[1].y);
+    f[6] = __uint_as_float(w[1].z); f[7] = __uint_as_float(w[1].w);
 }
 
 template <typename T, int G>
 __global__ __launch_bounds__(256) void k_attn_partial(
     const T *__restrict__ q, const T *__restrict__ K, const T *__restrict__ V,
     int64_t kv_head_stride, int64_t kv_rows, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ n_sel, int B, int S, double scale,
+    const int32_t *__restrict__ n_sel, int B, double scale,
     typename Acc<T>::type *__restrict__ part) {
     typedef typename Acc<T>::type A;
+    constexpr int PW = kD + 2;                    // partial record: m, l, acc[d]
     __shared__ A zs[G][kAttnRows];
     __shared__ A red[4][G][kD + 1];
-    const int s = blockIdx.x, h = blockIdx.y;
+    const int s = blockIdx.x, h = blockIdx.y, S = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = tid >> 4, q8 = tid & 15;
-    int n = n_sel[h];
-    n = n < 0 ? 0 : (n > B ? B : n);
     const int r0 = s * kAttnRows;
 
-    // rows slot and slot + 16 of this split
-    int64_t row[2];
-    bool ok[2];
-    A kf[2][8], vf[2][8];
+    // rows r0 + slot + 16k. Every load below is issued unconditionally from a
+    // valid address (clamped) and masked afterwards, so a thread's loads are
+    // all in flight together; idx is read without waiting for n_sel.
+    int tk[kRowsPerSlot];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kRowsPerSlot; ++k) {
         const int r = r0 + slot + 16 * k;
-        const int64_t t = (r < n) ? (int64_t)idx[(int64_t)h * B + r] : -1;
-        ok[k] = t >= 0 && t < kv_rows;
-        row[k] = ok[k] ? t : 0;
+        tk[k] = idx[(int64_t)h * B + (r < B ? r : B - 1)];
     }
+    int n = n_sel[h];
+    n = n < 0 ? 0 : (n > B ? B : n);
+    int64_t row[kRowsPerSlot];
+    bool ok[kRowsPerSlot];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (ok[k]) {
-            const int64_t base = (int64_t)h * kv_head_stride + row[k] * kD + 8 * q8;
-            load8<T>(K + base, kf[k]);
-            load8<T>(V + base, vf[k]);
-        } else {
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        const int r = r0 + slot + 16 * k;
+        ok[k] = r < n && tk[k] >= 0 && (int64_t)tk[k] < kv_rows;
+        row[k] = ok[k] ? tk[k] : 0;
+    }
+    // raw 16-byte chunks: K and V rows, then q; the scheduling barrier keeps
+    // every one of these loads ahead of the first use
+    constexpr int NV = sizeof(T) * 8 / 16;        // 16-byte chunks per 8 elements
+    u32x4 kr[kRowsPerSlot][NV], vr[kRowsPerSlot][NV], qr[G][NV];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kf[k][e] = vf[k][e] = (A)0;
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        const int64_t base = (int64_t)h * kv_head_stride + row[k] * kD + 8 * q8;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            kr[k][c] = *(const u32x4 *)(K + base + c * (16 / sizeof(T)));
+            vr[k][c] = *(const u32x4 *)(V + base + c * (16 / sizeof(T)));
         }
     }
-    A qf[G][8];
 #pragma unroll
-    for (int g = 0; g < G; ++g) load8<T>(q + ((int64_t)h * G + g) * kD + 8 * q8, qf[g]);
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+            qr[g][c] = *(const u32x4 *)(q + ((int64_t)h * G + g) * kD + 8 * q8 + c * (16 / sizeof(T)));
+    __builtin_amdgcn_sched_barrier(0);
+    A kf[kRowsPerSlot][8], vf[kRowsPerSlot][8], qf[G][8];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        unpack_chunks<T>(kr[k], kf[k]);
+        unpack_chunks<T>(vr[k], vf[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kf[k][e] = ok[k] ? kf[k][e] : (A)0;
+            vf[k][e] = ok[k] ? vf[k][e] : (A)0;
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) unpack_chunks<T>(qr[g], qf[g]);
 
-    A z[2][G];
+    A z[kRowsPerSlot][G];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < kRowsPerSlot; ++k)
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             A a = (A)0;
@@ -98,7 +127,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         }
     if (q8 == 0) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+        for (int k = 0; k < kRowsPerSlot; ++k)
 #pragma unroll
             for (int g = 0; g < G; ++g) zs[g][slot + 16 * k] = z[k][g];
     }
@@ -107,6 +136,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         A m = (A)(-INFINITY);
+#pragma unroll 8
         for (int r = 0; r < kAttnRows; ++r) m = zs[g][r] > m ? zs[g][r] : m;
         mx[g] = m;
     }
@@ -117,14 +147,14 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = (A)0;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kRowsPerSlot; ++k) {
             const A p = ok[k] ? ex(z[k][g] - mx[g]) : (A)0;
             l[g] += p;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[g][e] += p * vf[k][e];
         }
     }
-    // combine the 4 slots of the wave (lanes q8, q8+16, q8+32, q8+48)
+    // the 4 slots of a wave (lanes q8, q8+16, q8+32, q8+48), then the 4 waves
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         l[g] += __shfl_xor(l[g], 16);
@@ -144,11 +174,10 @@ __global__ __launch_bounds__(256) void k_attn_partial(
         }
     }
     __syncthreads();
-    // write (m, l, acc) per query head: thread j < d handles channel j
     for (int w = tid; w < G * (kD + 1); w += 256) {
         const int g = w / (kD + 1), j = w % (kD + 1);
         const A v = ((red[0][g][j] + red[1][g][j]) + red[2][g][j]) + red[3][g][j];
-        A *dst = part + (((int64_t)h * G + g) * S + s) * (kD + 2);
+        A *dst = part + (((int64_t)h * G + g) * S + s) * PW;
         if (j == kD) {
             dst[0] = mx[g];
             dst[1] = v;
@@ -156,59 +185,83 @@ __global__ __launch_bounds__(256) void k_attn_partial(
             dst[2 + j] = v;
         }
     }
+
 }
 
+// combine: one workgroup per query head, thread j owns channel j; the
+// split records are read in batches with every load of a batch in flight.
 template <typename A>
 __global__ __launch_bounds__(128) void k_attn_combine(const A *__restrict__ part, int S,
                                                       float *__restrict__ o) {
+    constexpr int PW = kD + 2;
+    constexpr int NB = 16;
     const int hq = blockIdx.x, j = threadIdx.x;
-    const A *p = part + (int64_t)hq * S * (kD + 2);
-    A M = (A)(-INFINITY);
-    for (int s = 0; s < S; ++s) M = p[s * (kD + 2)] > M ? p[s * (kD + 2)] : M;
-    float out = 0.f;
-    if (M > (A)(-INFINITY)) {
-        A Ls = (A)0, a = (A)0;
-        for (int s = 0; s < S; ++s) {
-            const A m = p[s * (kD + 2)];
-            const A w = (m > (A)(-INFINITY)) ? ex(m - M) : (A)0;
-            Ls += w * p[s * (kD + 2) + 1];
-            a += w * p[s * (kD + 2) + 2 + j];
+    const A *p = part + (int64_t)hq * S * PW;
+    // one pass: records in batches of NB, every load of a batch in flight
+    // (addresses clamped, values masked); the running max rescales the sums
+    // batch by batch, so the result equals the two-pass merge up to rounding
+    A M = (A)(-INFINITY), Ls = (A)0, a = (A)0;
+    for (int s0 = 0; s0 < S; s0 += NB) {
+        A m[NB], l[NB], v[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int sp = s0 + k < S ? s0 + k : S - 1;
+            const A *rec = p + (int64_t)sp * PW;
+            m[k] = rec[0];
+            l[k] = rec[1];
+            v[k] = rec[2 + j];
         }
-        out = (float)(a / Ls);
+        A bm = M;
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            if (s0 + k < S) bm = m[k] > bm ? m[k] : bm;
+        if (bm > (A)(-INFINITY)) {
+            const A sc = (M > (A)(-INFINITY)) ? ex(M - bm) : (A)0;
+            Ls *= sc;
+            a *= sc;
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const A w = (s0 + k < S && m[k] > (A)(-INFINITY)) ? ex(m[k] - bm) : (A)0;
+                Ls += w * l[k];
+                a += w * v[k];
+            }
+            M = bm;
+        }
     }
+    const float out = (Ls > (A)0) ? (float)(a / Ls) : 0.f;
     o[(int64_t)hq * kD + j] = out;
 }
 
 template <typename T, int G>
-static void launch_partial(const AttnPlan &p, const void *q, const void *K, const void *V,
-                           const int32_t *idx, const int32_t *n_sel, hipStream_t s) {
+static void launch_g(const AttnPlan &p, const void *q, const void *K, const void *V,
+                     const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s) {
     typedef typename Acc<T>::type A;
-    hipLaunchKernelGGL((k_attn_partial<T, G>), dim3(p.S, p.H), dim3(256), 0, s,
-                       (const T *)q, (const T *)K, (const T *)V, p.kv_head_stride, p.kv_rows,
-                       idx, n_sel, p.B, p.S, p.scale, (A *)p.partials);
+    hipLaunchKernelGGL((k_attn_partial<T, G>), dim3(p.S, p.H), dim3(256), 0, s, (const T *)q,
+                       (const T *)K, (const T *)V, p.kv_head_stride, p.kv_rows, idx, n_sel,
+                       p.B, p.scale, (A *)p.partials);
 }
 
 template <typename T>
-static void launch_partial_g(const AttnPlan &p, const void *q, const void *K, const void *V,
-                             const int32_t *idx, const int32_t *n_sel, hipStream_t s) {
+static void launch_t(const AttnPlan &p, const void *q, const void *K, const void *V,
+                     const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s) {
     switch (p.G) {
-        case 1: launch_partial<T, 1>(p, q, K, V, idx, n_sel, s); break;
-        case 2: launch_partial<T, 2>(p, q, K, V, idx, n_sel, s); break;
-        case 3: launch_partial<T, 3>(p, q, K, V, idx, n_sel, s); break;
-        case 4: launch_partial<T, 4>(p, q, K, V, idx, n_sel, s); break;
-        case 5: launch_partial<T, 5>(p, q, K, V, idx, n_sel, s); break;
-        case 6: launch_partial<T, 6>(p, q, K, V, idx, n_sel, s); break;
-        case 7: launch_partial<T, 7>(p, q, K, V, idx, n_sel, s); break;
-        default: launch_partial<T, 8>(p, q, K, V, idx, n_sel, s); break;
+        case 1: launch_g<T, 1>(p, q, K, V, idx, n_sel, o, s); break;
+        case 2: launch_g<T, 2>(p, q, K, V, idx, n_sel, o, s); break;
+        case 3: launch_g<T, 3>(p, q, K, V, idx, n_sel, o, s); break;
+        case 4: launch_g<T, 4>(p, q, K, V, idx, n_sel, o, s); break;
+        case 5: launch_g<T, 5>(p, q, K, V, idx, n_sel, o, s); break;
+        case 6: launch_g<T, 6>(p, q, K, V, idx, n_sel, o, s); break;
+        case 7: launch_g<T, 7>(p, q, K, V, idx, n_sel, o, s); break;
+        default: launch_g<T, 8>(p, q, K, V, idx, n_sel, o, s); break;
     }
 }
 
 hipError_t launch_attn(const AttnPlan &p, const void *q, const void *K, const void *V,
                        const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s) {
     if (p.dtype == 1)
-        launch_partial_g<uint16_t>(p, q, K, V, idx, n_sel, s);
+        launch_t<uint16_t>(p, q, K, V, idx, n_sel, o, s);
     else
-        launch_partial_g<float>(p, q, K, V, idx, n_sel, s);
+        launch_t<float>(p, q, K, V, idx, n_sel, o, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.dtype == 1)

@@ -9,6 +9,8 @@ namespace ckv {
 
 constexpr int kD = 128;               // supported head dimension
 constexpr int kMaxC = 2048;           // max clusters per call (LDS-sized kernels)
+constexpr int kAttnSplitRows = 64;    // idx entries per attention workgroup
+constexpr int kMaxSplits = 512;       // attention splits per head -> B <= 32768
 
 // ---- element types ------------------------------------------------------
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -43,6 +45,36 @@ __device__ __forceinline__ uint32_t xcd_linear(uint32_t bid, uint32_t n) {
     return (bid & 7u) * (n >> 3) + (bid >> 3);
 }
 
+// Exclusive scan over a block of up to 1024 threads (every thread calls it);
+// returns this thread's exclusive prefix; *total receives the block sum.
+// wsum: 17 ints of LDS.
+__device__ inline int block_excl_scan(int v, int *wsum, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = (blockDim.x + 63) >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int t = wsum[w];
+            wsum[w] = run;
+            run += t;
+        }
+        wsum[16] = run;
+    }
+    __syncthreads();
+    const int r = wsum[wave] + x - v;
+    *total = wsum[16];
+    __syncthreads();
+    return r;
+}
+
 // ---- launchers (defined in the .hip files) ------------------------------
 struct ClusterPlan {
     int H, C, Cpad, iters, n_sink, dtype, c_base, c_cap;
@@ -53,6 +85,7 @@ struct ClusterPlan {
     void *mt;                 // unit centroids [H][Cpad][d] (bf16 or f32)
     int32_t *tile_hist;       // [H][ntiles][C], then tile bases
     int32_t *tile_rank;       // [H][Lp]
+    int32_t *counts;          // [H][C] cluster sizes
 };
 
 constexpr int kCsrTile = 512;          // tokens per CSR tile (one workgroup)
@@ -69,7 +102,6 @@ hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *off
 struct SelectPlan {
     int H, G, C, c_cap, n_sink, B, dtype;
     int64_t t_cap, pending_begin, n_pending;
-    double *scores;           // [H][C]
 };
 hipError_t launch_select(const SelectPlan &p, const void *q, const float *cent,
                          const int32_t *offsets, const int32_t *tokens, int32_t *idx,

@@ -388,89 +388,106 @@ __global__ __launch_bounds__(kCsrTile) void k_csr_count(
     }
 }
 
-// Exclusive scan over a block of up to 1024 threads; returns this thread's
-// exclusive prefix; *total receives the block sum.
-__device__ int block_excl_scan(int v, int *wsum, int *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nw = (blockDim.x + 63) >> 6;
-    int x = v;
+// scan: per head, for every cluster, exclusive prefix of its tile counts over
+// the tiles (in tile order) and its total count. Workgroup = 64 clusters x 16
+// parts; part p owns the contiguous tiles [p*R, (p+1)*R), R = ceil(T/16);
+// lanes of a wave are consecutive clusters, so the loads coalesce.
+constexpr int kScanParts = 16;
+constexpr int kScanBatch = 16;
+
+__global__ __launch_bounds__(1024) void k_csr_scan(int32_t *__restrict__ tile_hist,
+                                                   int64_t ntiles, int C,
+                                                   int32_t *__restrict__ counts) {
+    __shared__ int psum[kScanParts][64];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int cl = tid & 63, part = tid >> 6;
+    const int c = blockIdx.x * 64 + cl;
+    const bool valid = c < C;
+    const int cc = valid ? c : C - 1;
+    const int64_t R = (ntiles + kScanParts - 1) / kScanParts;
+    const int64_t t0 = part * R, t1 = (t0 + R < ntiles) ? t0 + R : ntiles;
+    int32_t *col = tile_hist + (int64_t)h * ntiles * C + cc;
+    // pass 1: the part's sum (batches of loads in flight, clamped, masked)
+    int sum = 0;
+    for (int64_t tb = t0; tb < t1; tb += kScanBatch) {
+        int v[kScanBatch];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int w = 0; w < nw; ++w) {
-            const int t = wsum[w];
-            wsum[w] = run;
-            run += t;
+        for (int k = 0; k < kScanBatch; ++k) {
+            const int64_t t = tb + k;
+            v[k] = col[(t < t1 ? t : t0) * C];
         }
-        wsum[16] = run;
+#pragma unroll
+        for (int k = 0; k < kScanBatch; ++k) sum += (tb + k < t1) ? v[k] : 0;
     }
+    psum[part][cl] = sum;
     __syncthreads();
-    const int r = wsum[wave] + x - v;
-    *total = wsum[16];
-    __syncthreads();
-    return r;
+    int base = 0;
+    for (int p = 0; p < part; ++p) base += psum[p][cl];
+    if (part == kScanParts - 1 && valid) counts[(int64_t)h * C + c] = base + sum;
+    // pass 2: rewrite the part's tiles with exclusive bases (values re-read:
+    // they are still in L2)
+    for (int64_t tb = t0; tb < t1; tb += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int k = 0; k < kScanBatch; ++k) {
+            const int64_t t = tb + k;
+            v[k] = col[(t < t1 ? t : t0) * C];
+        }
+#pragma unroll
+        for (int k = 0; k < kScanBatch; ++k) {
+            const int64_t t = tb + k;
+            if (t < t1 && valid) col[t * C] = base;
+            base += (t < t1) ? v[k] : 0;
+        }
+    }
 }
 
-__global__ __launch_bounds__(1024) void k_csr_scan(
-    int32_t *__restrict__ tile_hist, int64_t ntiles, int C, int32_t *__restrict__ offsets,
-    int c_base, int c_cap, int64_t t_base) {
-    __shared__ int32_t cnt[kMaxC];
-    __shared__ int wsum[17];
-    const int h = blockIdx.x, tid = threadIdx.x;
-    for (int c = tid; c < C; c += 1024) {
-        int32_t *colp = tile_hist + (int64_t)h * ntiles * C + c;
-        int run = 0;
-        int64_t t = 0;
-        for (; t + 4 <= ntiles; t += 4) {
-            const int v0 = colp[(t + 0) * C], v1 = colp[(t + 1) * C];
-            const int v2 = colp[(t + 2) * C], v3 = colp[(t + 3) * C];
-            colp[(t + 0) * C] = run;
-            colp[(t + 1) * C] = run + v0;
-            colp[(t + 2) * C] = run + v0 + v1;
-            colp[(t + 3) * C] = run + v0 + v1 + v2;
-            run += v0 + v1 + v2 + v3;
-        }
-        for (; t < ntiles; ++t) {
-            const int v = colp[t * C];
-            colp[t * C] = run;
-            run += v;
-        }
-        cnt[c] = run;
-    }
-    __syncthreads();
-    // two consecutive clusters per thread (C <= 2048)
-    const int k0 = 2 * tid;
-    const int a0 = k0 < C ? cnt[k0] : 0;
-    const int a1 = k0 + 1 < C ? cnt[k0 + 1] : 0;
-    int total;
-    const int ex = block_excl_scan(a0 + a1, wsum, &total);
-    int32_t *off = offsets + (int64_t)h * (c_cap + 1) + c_base;
-    if (k0 < C) off[k0] = (int32_t)(t_base + ex);
-    if (k0 + 1 < C) off[k0 + 1] = (int32_t)(t_base + ex + a0);
-    if (tid == 0) off[C] = (int32_t)(t_base + total);
-}
-
+// scatter: every workgroup first turns the cluster counts into offsets (an
+// exclusive scan over the clusters, in LDS; the tile-0 workgroup writes them
+// out), then token i of tile T with label a goes to
+// offsets[a] + base[T][a] + rank_i.
 __global__ __launch_bounds__(kCsrTile) void k_csr_scatter(
     const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C,
-    int64_t ntiles, const int32_t *__restrict__ tile_base, const int32_t *__restrict__ tile_rank,
-    const int32_t *__restrict__ offsets, int c_base, int c_cap, int64_t t_base, int64_t t_cap,
-    int64_t token_base, int32_t *__restrict__ tokens) {
-    const int h = blockIdx.y;
+    int64_t ntiles, const int32_t *__restrict__ counts, const int32_t *__restrict__ tile_base,
+    const int32_t *__restrict__ tile_rank, int32_t *__restrict__ offsets, int c_base,
+    int c_cap, int64_t t_base, int64_t t_cap, int64_t token_base, int32_t *__restrict__ tokens) {
+    __shared__ int excl[kMaxC];
+    __shared__ int wsum[17];
+    const int h = blockIdx.y, tid = threadIdx.x;
     const int64_t tile = blockIdx.x;
-    const int64_t i = tile * kCsrTile + threadIdx.x;
-    if (i >= Lp) return;
-    int a = assign[(int64_t)h * L + n_sink + i];
+    const int64_t i = tile * kCsrTile + tid;
+    const bool valid = i < Lp;
+    const int64_t ii = valid ? i : Lp - 1;
+    // this token's label and rank, and the counts, all in flight at once
+    int a = assign[(int64_t)h * L + n_sink + ii];
+    const int rk = tile_rank[(int64_t)h * Lp + ii];
+    constexpr int PER = kMaxC / kCsrTile;          // 4 counts per thread
+    int cv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int c = tid * PER + k;
+        cv[k] = counts[(int64_t)h * C + (c < C ? c : C - 1)];
+    }
+    int loc = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) loc += (tid * PER + k < C) ? cv[k] : 0;
+    int total;
+    int run = block_excl_scan(loc, wsum, &total);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int c = tid * PER + k;
+        if (c < C) excl[c] = run;
+        run += (c < C) ? cv[k] : 0;
+    }
+    __syncthreads();
+    if (tile == 0) {
+        int32_t *off = offsets + (int64_t)h * (c_cap + 1) + c_base;
+        for (int c = tid; c < C; c += kCsrTile) off[c] = (int32_t)(t_base + excl[c]);
+        if (tid == 0) off[C] = (int32_t)(t_base + total);
+    }
     a = a < 0 ? 0 : (a >= C ? C - 1 : a);
-    const int64_t pos = (int64_t)(offsets[(int64_t)h * (c_cap + 1) + c_base + a] - t_base) +
-                        tile_base[((int64_t)h * ntiles + tile) * C + a] +
-                        tile_rank[(int64_t)h * Lp + i];
-    if (pos >= 0 && pos < Lp)
+    const int64_t pos = (int64_t)excl[a] + tile_base[((int64_t)h * ntiles + tile) * C + a] + rk;
+    if (valid && pos >= 0 && pos < Lp)
         tokens[(int64_t)h * t_cap + t_base + pos] = (int32_t)(token_base + n_sink + i);
 }
 
@@ -484,14 +501,14 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
                        p.tile_rank);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_csr_scan, dim3(p.H), dim3(1024), 0, s, p.tile_hist, p.ntiles, p.C,
-                       offsets, p.c_base, p.c_cap, p.t_base);
+    hipLaunchKernelGGL(k_csr_scan, dim3((p.C + 63) / 64, p.H), dim3(1024), 0, s, p.tile_hist,
+                       p.ntiles, p.C, p.counts);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_csr_scatter, grid, dim3(kCsrTile), 0, s, assign, p.L, p.n_sink, p.Lp,
-                       p.C, p.ntiles, (const int32_t *)p.tile_hist,
-                       (const int32_t *)p.tile_rank, (const int32_t *)offsets, p.c_base,
-                       p.c_cap, p.t_base, p.t_cap, p.token_base, tokens);
+                       p.C, p.ntiles, (const int32_t *)p.counts, (const int32_t *)p.tile_hist,
+                       (const int32_t *)p.tile_rank, offsets, p.c_base, p.c_cap, p.t_base,
+                       p.t_cap, p.token_base, tokens);
     return hipGetLastError();
 }
 
@@ -523,23 +540,51 @@ __global__ __launch_bounds__(256) void k_update(
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    for (int64_t r = beg + slot; r < end; r += 16) {
-        const int64_t row = (int64_t)tok[r] - token_base;
-        if (row < 0 || row >= L) continue;
-        float f[8];
-        if (BF16) {
-            const u32x4 w = *(const u32x4 *)((const uint16_t *)K + h * head_stride + row * kD + 8 * q);
-            unpack8(w, f);
-        } else {
-            const float *src = (const float *)K + h * head_stride + row * kD + 8 * q;
-            const u32x4 w0 = *(const u32x4 *)src, w1 = *(const u32x4 *)(src + 4);
-            f[0] = __uint_as_float(w0.x); f[1] = __uint_as_float(w0.y);
-            f[2] = __uint_as_float(w0.z); f[3] = __uint_as_float(w0.w);
-            f[4] = __uint_as_float(w1.x); f[5] = __uint_as_float(w1.y);
-            f[6] = __uint_as_float(w1.z); f[7] = __uint_as_float(w1.w);
-        }
+    // rows beg + slot + 16k in batches of NB: the batch's token ids, then its
+    // key chunks, each set in flight at once (clamped addresses, masked values)
+    constexpr int NB = 8;
+    constexpr int NV = BF16 ? 1 : 2;              // 16-byte chunks per 8 channels
+    const int64_t last = end > beg ? end - 1 : beg;
+    for (int64_t r0 = beg + slot; r0 < end; r0 += 16 * NB) {
+        int32_t tk[NB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
+        for (int k = 0; k < NB; ++k) {
+            const int64_t r = r0 + 16 * k;
+            tk[k] = tok[r < end ? r : last];
+        }
+        int64_t row[NB];
+        bool ok[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            row[k] = (int64_t)tk[k] - token_base;
+            ok[k] = r0 + 16 * k < end && row[k] >= 0 && row[k] < L;
+            row[k] = ok[k] ? row[k] : 0;
+        }
+        u32x4 w[NB][NV];
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+#pragma unroll
+            for (int c = 0; c < NV; ++c)
+                w[k][c] = BF16 ? *(const u32x4 *)((const uint16_t *)K + h * head_stride +
+                                                  row[k] * kD + 8 * q)
+                               : *(const u32x4 *)((const float *)K + h * head_stride +
+                                                  row[k] * kD + 8 * q + 4 * c);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (!ok[k]) continue;
+            float f[8];
+            if (BF16) {
+                unpack8(w[k][0], f);
+            } else {
+                f[0] = __uint_as_float(w[k][0].x); f[1] = __uint_as_float(w[k][0].y);
+                f[2] = __uint_as_float(w[k][0].z); f[3] = __uint_as_float(w[k][0].w);
+                f[4] = __uint_as_float(w[k][NV - 1].x); f[5] = __uint_as_float(w[k][NV - 1].y);
+                f[6] = __uint_as_float(w[k][NV - 1].z); f[7] = __uint_as_float(w[k][NV - 1].w);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
+        }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

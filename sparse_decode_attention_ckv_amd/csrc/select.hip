@@ -2,174 +2,303 @@
 //
 // Method: "ClusterKV: Manipulating LLM KV Cache in Semantic Space for
 // Recallable Compression", section 核心方法细节 / 语义聚类粒度的选择
-// (cluster-granular selection: score q.mu_i, sort descending, admit the
-// clusters' tokens until the budget B is reached) and section 选择与索引机制
-// (selection and indexing, Fig. 8: sort, gather and reorder the cluster
-// sizes, prefix-sum them, find where the budget falls, trim the last
-// cluster, emit the token indices).
+// (cluster-granular selection: score q.mu_i, take the clusters in descending
+// score order until the budget B is reached) and section 选择与索引机制
+// (selection and indexing, Fig. 8: cluster sizes, prefix sums, where the
+// budget falls, trim of the last cluster, token indices).
 //
-// Two kernels per step:
-//   score      s_c = q_g . mu_c in fp64, many workgroups per head (the
-//              centroids are the bytes that matter: HBM-bound GEMV)
-//   sort_cut   one workgroup per head: bitonic sort of (s desc, id asc) in
-//              LDS, prefix sum of the sizes in rank order, cut at the budget,
-//              and a parallel emission of idx (binary search per slot).
+// One kernel per decode step, one 1024-thread workgroup per KV head, no
+// cross-workgroup handoff:
+//  1. score every cluster, s_c = q_g . mu_c in fp64 with the fixed
+//     association of the definition (32 fma chains of 4 channels, pairwise
+//     tree r + r+16, +8, +4, +2, +1). Four lanes share a cluster: lane l holds
+//     the runs r = l (mod 4), so the first three tree levels stay inside the
+//     lane and only the last two cross lanes. Every centroid load of a batch
+//     is in flight at once.
+//  2. the clusters admitted "in descending score until the budget" are found
+//     without sorting: a weighted radix select over the rank key (score
+//     descending, then id ascending) finds the cluster at which the running
+//     size total first reaches the budget (the cut), 8-bit digits from the
+//     most significant, histograms of sizes in LDS.
+//  3. every cluster ranked before the cut gives all its tokens, the cut
+//     cluster gives what still fits; tokens are emitted by cluster id
+//     (prefix sum in id order, one output slot per thread, binary search).
 #include "ckv_dev.h"
 
 namespace ckv {
 
-// score: a half-wave (32 lanes) per cluster; lane r holds channels
-// 4r..4r+3 (one 16-byte fp32 load), runs a 4-step fp64 fma chain from 0,
-// and the 32 run sums are added pairwise (lane r + lane r+16, +8, ..., +1)
-// with xor shuffles; lane 0 then holds the score. q_g is the fp64 sum of the
-// G query rows in row order.
-constexpr int kScoreClusters = 32;   // clusters per workgroup (4 passes of 8)
+constexpr int kSelThreads = 1024;
+constexpr int kSelLanes = 4;                        // lanes per cluster while scoring
+constexpr int kSelPass = kSelThreads / kSelLanes;   // clusters per scoring pass
+constexpr int kSelInFlight = 2;                     // passes whose loads fly together
+constexpr int kSelPer = kMaxC / kSelThreads;        // clusters per thread later (2)
+
+// Order-preserving 64-bit image of a finite double, inverted so that a larger
+// score gives a smaller key; -0 and +0 map to the same key.
+__device__ __forceinline__ uint64_t rank_key(double s) {
+    s = s + 0.0;
+    uint64_t u = (uint64_t)__double_as_longlong(s);
+    u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+    return ~u;
+}
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_score(const void *__restrict__ q, int G,
-                                               const float *__restrict__ cent, int C,
-                                               int c_cap, double *__restrict__ scores) {
-    const int h = blockIdx.y;
-    const int tid = threadIdx.x, half = tid >> 5, r = tid & 31;
-    double qg[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        double a = 0.0;
-        for (int g = 0; g < G; ++g) {
-            const int64_t idx = ((int64_t)h * G + g) * kD + 4 * r + e;
-            a += BF16 ? (double)bf16_to_f32(((const uint16_t *)q)[idx])
-                      : (double)((const float *)q)[idx];
-        }
-        qg[e] = a;
-    }
-#pragma unroll
-    for (int k = 0; k < kScoreClusters / 8; ++k) {
-        const int c = blockIdx.x * kScoreClusters + 8 * k + half;
-        double a = 0.0;
-        if (c < C) {
-            const u32x4 w = *(const u32x4 *)(cent + ((int64_t)h * c_cap + c) * kD + 4 * r);
-            a = __fma_rn(qg[0], (double)__uint_as_float(w.x), a);
-            a = __fma_rn(qg[1], (double)__uint_as_float(w.y), a);
-            a = __fma_rn(qg[2], (double)__uint_as_float(w.z), a);
-            a = __fma_rn(qg[3], (double)__uint_as_float(w.w), a);
-        }
-#pragma unroll
-        for (int w = 16; w >= 1; w >>= 1) a = a + __shfl_xor(a, w, 32);
-        if (c < C && r == 0) scores[(int64_t)h * C + c] = a;
-    }
-}
-
-// "a comes before b" in rank order
-__device__ __forceinline__ bool before(double sa, int ia, double sb, int ib) {
-    return sa > sb || (sa == sb && ia < ib);
-}
-
-// sort_cut: P = power of two >= C, T = P/2 threads (at least 64).
-__global__ __launch_bounds__(1024) void k_sort_cut(
-    const double *__restrict__ scores, int C, int P, const int32_t *__restrict__ offsets,
-    int c_cap, const int32_t *__restrict__ tokens, int64_t t_cap, int n_sink,
-    int64_t pending_begin, int64_t n_pending, int B, int32_t *__restrict__ idx,
+__global__ __launch_bounds__(kSelThreads) void k_select(
+    const void *__restrict__ q, int G, const float *__restrict__ cent, int C, int c_cap,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tokens, int64_t t_cap,
+    int n_sink, int64_t pending_begin, int64_t n_pending, int B, int32_t *__restrict__ idx,
     int32_t *__restrict__ n_sel) {
-    extern __shared__ double smem[];
-    double *sc = smem;                           // [P]
-    int32_t *id = (int32_t *)(sc + P);           // [P]
-    int32_t *sz = id + P;                        // [P]  sizes in rank order
-    int32_t *inc = sz + P;                       // [P]  inclusive prefix
+    __shared__ double qg[kD];
+    __shared__ uint64_t rkey[kMaxC];
+    __shared__ int wt[kMaxC];          // cluster sizes, later the tokens each gives
+    __shared__ int off[kMaxC + 1];     // clamped offsets
+    __shared__ int inc[kMaxC];         // inclusive prefix of the taken counts, id order
+    __shared__ int hw[256], hn[256];   // radix histograms: sizes and counts
     __shared__ int wsum[17];
-    const int h = blockIdx.x, tid = threadIdx.x, T = blockDim.x;
-    const int32_t *off = offsets + (int64_t)h * (c_cap + 1);
-    const int32_t *tok = tokens + (int64_t)h * t_cap;
+    __shared__ int s_bucket, s_rem, s_cnt, s_cut;
+    const int T = kSelThreads, tid = threadIdx.x;
+    const int h = blockIdx.x;
 
-    for (int e = tid; e < P; e += T) {
-        sc[e] = (e < C) ? scores[(int64_t)h * C + e] : -INFINITY;
-        id[e] = e;
+    // ---- offsets and q_g (all loads of a thread in flight at once) --------
+    const int32_t *offh = offsets + (int64_t)h * (c_cap + 1);
+    {
+        constexpr int NO = (kMaxC + kSelThreads) / kSelThreads;
+        int64_t v[NO];
+#pragma unroll
+        for (int k = 0; k < NO; ++k) {
+            const int c = tid + k * T;
+            v[k] = offh[c <= C ? c : C];
+        }
+        float qv[8];
+        if (tid < kD) {
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const int64_t qi = ((int64_t)h * G + (g < G ? g : G - 1)) * kD + tid;
+                qv[g] = BF16 ? bf16_to_f32(((const uint16_t *)q)[qi]) : ((const float *)q)[qi];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NO; ++k) {
+            const int c = tid + k * T;
+            if (c <= C) off[c] = (int)(v[k] < 0 ? 0 : (v[k] > t_cap ? t_cap : v[k]));
+        }
+        if (tid < kD) {
+            double a = 0.0;               // fp64 sum of the group's rows, in row order
+#pragma unroll
+            for (int g = 0; g < 8; ++g)
+                if (g < G) a += (double)qv[g];
+            qg[tid] = a;
+        }
     }
     __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int pr = tid; pr < (P >> 1); pr += T) {
-                const int i = 2 * pr - (pr & (j - 1));
-                const int l = i + j;
-                const bool up = (i & k) == 0;
-                const double si = sc[i], sl = sc[l];
-                const int ii = id[i], il = id[l];
-                const bool sw = up ? before(sl, il, si, ii) : before(si, ii, sl, il);
-                if (sw) {
-                    sc[i] = sl; sc[l] = si;
-                    id[i] = il; id[l] = ii;
+
+    // ---- 1. scores -> rank keys; sizes ------------------------------------
+    {
+        const int lam = tid & (kSelLanes - 1), slot = tid >> 2;
+        const float *ch = cent + (int64_t)h * c_cap * kD;
+        for (int p0 = 0; p0 < C; p0 += kSelPass * kSelInFlight) {
+            u32x4 w[kSelInFlight][8];
+#pragma unroll
+            for (int pi = 0; pi < kSelInFlight; ++pi) {
+                const int c = p0 + pi * kSelPass + slot;
+                const float *row = ch + (int64_t)(c < C ? c : C - 1) * kD;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[pi][i] = *(const u32x4 *)(row + 4 * (lam + 4 * i));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int pi = 0; pi < kSelInFlight; ++pi) {
+                const int c = p0 + pi * kSelPass + slot;
+                double run[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const double *qr = qg + 4 * (lam + 4 * i);
+                    double a = 0.0;
+                    a = __fma_rn(qr[0], (double)__uint_as_float(w[pi][i].x), a);
+                    a = __fma_rn(qr[1], (double)__uint_as_float(w[pi][i].y), a);
+                    a = __fma_rn(qr[2], (double)__uint_as_float(w[pi][i].z), a);
+                    a = __fma_rn(qr[3], (double)__uint_as_float(w[pi][i].w), a);
+                    run[i] = a;
+                }
+                // levels r + r+16, r + r+8, r + r+4 (runs lam + 4i of this lane)
+                const double t0 = run[0] + run[4], t1 = run[1] + run[5];
+                const double t2 = run[2] + run[6], t3 = run[3] + run[7];
+                double v = (t0 + t2) + (t1 + t3);
+                // levels r + r+2 and r + r+1 across the four lanes
+                v = v + __shfl_xor(v, 2);
+                v = v + __shfl_xor(v, 1);
+                if (lam == 0 && c < C) rkey[c] = rank_key(v);
+            }
+        }
+        for (int c = tid; c < C; c += T) {
+            const int n = off[c + 1] - off[c];
+            wt[c] = n > 0 ? n : 0;
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. the cut: first cluster (rank order) where the sizes reach B_eff
+    const int64_t beff64 = (int64_t)B - n_sink - n_pending;
+    const int beff = (int)(beff64 > 0 ? beff64 : 0);
+    int loc = 0;
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int c = kSelPer * tid + u;
+        loc += c < C ? wt[c] : 0;
+    }
+    int total;
+    block_excl_scan(loc, wsum, &total);
+    int cut = -1, rem = 0;                 // no cut: every cluster gives all
+    if (beff == 0) {
+        cut = -2;                          // nothing is taken
+    } else if (total > beff) {
+        bool cand[kSelPer];
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) cand[u] = kSelPer * tid + u < C;
+        int R = beff;
+        for (int pos = 0; pos < 10; ++pos) {
+            // digits 0..7: bytes of the rank key, high first; 8..9: id bytes
+            if (tid < 256) {
+                hw[tid] = 0;
+                hn[tid] = 0;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kSelPer; ++u) {
+                const int c = kSelPer * tid + u;
+                if (cand[u]) {
+                    const int d = pos < 8 ? (int)((rkey[c] >> (56 - 8 * pos)) & 0xFF)
+                                          : (pos == 8 ? (c >> 8) & 0xFF : c & 0xFF);
+                    atomicAdd(&hw[d], wt[c]);
+                    atomicAdd(&hn[d], 1);
                 }
             }
             __syncthreads();
-        }
-    }
-    // sizes in rank order, clamped offsets
-    for (int e = tid; e < P; e += T) {
-        const int c = id[e];
-        int n = 0;
-        if (c < C) {
-            int64_t b0 = off[c], b1 = off[c + 1];
-            b0 = b0 < 0 ? 0 : (b0 > t_cap ? t_cap : b0);
-            b1 = b1 < b0 ? b0 : (b1 > t_cap ? t_cap : b1);
-            n = (int)(b1 - b0);
-        }
-        sz[e] = n;
-    }
-    __syncthreads();
-    // inclusive prefix of sz: each thread owns P/T consecutive entries
-    const int per = P / T;
-    int loc = 0;
-    for (int u = 0; u < per; ++u) loc += sz[tid * per + u];
-    const int lane = tid & 63, wave = tid >> 6, nw = (T + 63) >> 6;
-    int x = loc;
+            if (tid < 64) {
+                // buckets 4*lane .. 4*lane+3, ascending = rank order
+                int bw[4], lsum = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63 || tid == T - 1) wsum[wave] = x;
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int w = 0; w < nw; ++w) {
-            const int t = wsum[w];
-            wsum[w] = run;
-            run += t;
+                for (int k = 0; k < 4; ++k) {
+                    bw[k] = hw[4 * tid + k];
+                    lsum += bw[k];
+                }
+                int x = lsum;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(x, o);
+                    if (tid >= o) x += y;
+                }
+                const int before_lane = x - lsum;
+                // the lane holding the bucket where the running total reaches R
+                if (before_lane < R && x >= R) {
+                    int run = before_lane, b = 0;
+                    bool found = false;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (!found && run + bw[k] >= R) {
+                            b = k;
+                            found = true;
+                        } else if (!found) {
+                            run += bw[k];
+                        }
+                    }
+                    s_bucket = 4 * tid + b;
+                    s_rem = R - run;
+                    s_cnt = hn[4 * tid + b];
+                }
+            }
+            __syncthreads();
+            const int bsel = s_bucket;
+            R = s_rem;
+#pragma unroll
+            for (int u = 0; u < kSelPer; ++u) {
+                const int c = kSelPer * tid + u;
+                if (cand[u]) {
+                    const int d = pos < 8 ? (int)((rkey[c] >> (56 - 8 * pos)) & 0xFF)
+                                          : (pos == 8 ? (c >> 8) & 0xFF : c & 0xFF);
+                    cand[u] = d == bsel;
+                }
+            }
+            const bool done = s_cnt == 1;  // uniform
+            __syncthreads();
+            if (done) break;
         }
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u)
+            if (cand[u]) s_cut = kSelPer * tid + u;
+        __syncthreads();
+        cut = s_cut;
+        rem = R;
     }
-    __syncthreads();
-    int run = wsum[wave] + x - loc;
-    for (int u = 0; u < per; ++u) {
-        run += sz[tid * per + u];
-        inc[tid * per + u] = run;
+    // ---- 3. tokens each cluster gives, prefix in id order, emission --------
+    const uint64_t ck = cut >= 0 ? rkey[cut] : 0;
+    int tk[kSelPer];
+    loc = 0;
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int c = kSelPer * tid + u;
+        int t = 0;
+        if (c < C) {
+            if (cut == -1) {
+                t = wt[c];
+            } else if (cut >= 0) {
+                const uint64_t k = rkey[c];
+                if (k < ck || (k == ck && c < cut)) t = wt[c];
+                else if (c == cut) t = rem;
+            }
+        }
+        tk[u] = t;
+        loc += t;
+    }
+    int ntake;
+    int run = block_excl_scan(loc, wsum, &ntake);
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int c = kSelPer * tid + u;
+        run += tk[u];
+        if (c < C) {
+            inc[c] = run;
+            wt[c] = tk[u];
+        }
     }
     __syncthreads();
 
-    const int64_t beff = (int64_t)B - n_sink - n_pending;
-    const int64_t total = inc[P - 1];
-    const int64_t ntake = beff < total ? beff : total;
     const int64_t head = (int64_t)n_sink + n_pending;
+    const int32_t *tok = tokens + (int64_t)h * t_cap;
     int32_t *out = idx + (int64_t)h * B;
-    for (int e = tid; e < B; e += T) {
-        int32_t v;
-        if (e < n_sink) {
-            v = e;
-        } else if (e < head) {
-            v = (int32_t)(pending_begin + (e - n_sink));
-        } else if (e - head < ntake) {
-            const int p = (int)(e - head);
-            int lo = 0, hi = P - 1;        // smallest rank with inc > p
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (inc[mid] > p) hi = mid; else lo = mid + 1;
+    // output slots in batches: positions first (LDS only), then every token
+    // load of the batch in flight, then the stores
+    constexpr int NE = 8;
+    for (int e0 = tid; e0 < B; e0 += NE * T) {
+        int src[NE];
+        int32_t val[NE];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const int64_t e = e0 + (int64_t)k * T;
+            src[k] = -1;
+            val[k] = -1;
+            if (e < n_sink) {
+                val[k] = (int32_t)e;
+            } else if (e < head) {
+                val[k] = (int32_t)(pending_begin + (e - n_sink));
+            } else if (e - head < ntake) {
+                const int p = (int)(e - head);
+                int lo = 0, hi = C - 1;        // first cluster whose inclusive prefix exceeds p
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (inc[mid] > p) hi = mid; else lo = mid + 1;
+                }
+                src[k] = off[lo] + (p - (inc[lo] - wt[lo]));
             }
-            const int c = id[lo];
-            int64_t b0 = off[c];
-            b0 = b0 < 0 ? 0 : (b0 > t_cap ? t_cap : b0);
-            v = tok[b0 + (p - (inc[lo] - sz[lo]))];
-        } else {
-            v = -1;
         }
-        out[e] = v;
+        int32_t t[NE];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) t[k] = tok[src[k] >= 0 ? src[k] : 0];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const int64_t e = e0 + (int64_t)k * T;
+            if (e < B) out[e] = src[k] >= 0 ? t[k] : val[k];
+        }
     }
     if (tid == 0) n_sel[h] = (int32_t)(head + ntake);
 }
@@ -177,22 +306,14 @@ __global__ __launch_bounds__(1024) void k_sort_cut(
 hipError_t launch_select(const SelectPlan &p, const void *q, const float *cent,
                          const int32_t *offsets, const int32_t *tokens, int32_t *idx,
                          int32_t *n_sel, hipStream_t s) {
-    dim3 g1((p.C + kScoreClusters - 1) / kScoreClusters, p.H);
     if (p.dtype == 1)
-        hipLaunchKernelGGL(k_score<true>, g1, dim3(256), 0, s, q, p.G, cent, p.C, p.c_cap,
-                           p.scores);
+        hipLaunchKernelGGL(k_select<true>, dim3(p.H), dim3(kSelThreads), 0, s, q, p.G, cent,
+                           p.C, p.c_cap, offsets, tokens, p.t_cap, p.n_sink, p.pending_begin,
+                           p.n_pending, p.B, idx, n_sel);
     else
-        hipLaunchKernelGGL(k_score<false>, g1, dim3(256), 0, s, q, p.G, cent, p.C, p.c_cap,
-                           p.scores);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    int P = 128;
-    while (P < p.C) P <<= 1;
-    const int T = P / 2;
-    const size_t lds = (size_t)P * (sizeof(double) + 3 * sizeof(int32_t));
-    hipLaunchKernelGGL(k_sort_cut, dim3(p.H), dim3(T), lds, s, p.scores, p.C, P, offsets,
-                       p.c_cap, tokens, p.t_cap, p.n_sink, p.pending_begin, p.n_pending, p.B,
-                       idx, n_sel);
+        hipLaunchKernelGGL(k_select<false>, dim3(p.H), dim3(kSelThreads), 0, s, q, p.G, cent,
+                           p.C, p.c_cap, offsets, tokens, p.t_cap, p.n_sink, p.pending_begin,
+                           p.n_pending, p.B, idx, n_sel);
     return hipGetLastError();
 }
 

@@ -141,12 +141,11 @@ def test_select_rejects_bad_descriptors(kw, status):
 def test_select_workspace_and_pointers():
     d = _sel()
     lib = ck.load()
-    need = lib.ckv_select_workspace(ct.byref(d))
-    assert need >= 2 * 10 * 8
-    assert lib.ckv_select(ct.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
-                          None) == ck.CKV_ERR_WORKSPACE
-    assert lib.ckv_select(ct.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
-                          None) == ck.CKV_ERR_INVALID_ARG
+    assert lib.ckv_select_workspace(ct.byref(d)) == 0       # everything stays in LDS
+    for k in range(6):                                       # any missing pointer is rejected
+        args = [FAKE] * 6
+        args[k] = None
+        assert lib.ckv_select(ct.byref(d), *args, None, 0, None) == ck.CKV_ERR_INVALID_ARG
 
 
 def _att(**kw):
@@ -173,7 +172,7 @@ def test_attn_workspace_and_pointers():
     d = _att()
     lib = ck.load()
     need = lib.ckv_attn_workspace(ct.byref(d))
-    assert need >= 2 * 4 * 2 * 130 * 4
+    assert need >= 2 * 4 * 1 * 130 * 4 + 2 * 4   # one 64-row split per head + counters
     assert lib.ckv_sparse_attn(ct.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
                                None) == ck.CKV_ERR_WORKSPACE
     assert lib.ckv_sparse_attn(ct.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need,

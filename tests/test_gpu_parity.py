@@ -178,6 +178,15 @@ def test_select_exact_ties_go_to_lower_id():
         torch.cuda.synchronize()
         o_idx, o_ns, _ = oracle.select(qf, mu.astype(np.float64), off, tok, C, 16, B, G=G)
         assert np.array_equal(idx.cpu().numpy(), o_idx), B
+    # q = 0: every score is exactly zero, the cluster id alone decides
+    qz = torch.zeros_like(qd)
+    for B in (17, 200, 416):
+        idx, ns = ck.ckv_select(qz, torch.from_numpy(mu).to(DEV), torch.from_numpy(off).to(DEV),
+                                torch.from_numpy(tok).to(DEV), C, B)
+        torch.cuda.synchronize()
+        o_idx, o_ns, _ = oracle.select(np.zeros_like(qf), mu.astype(np.float64), off, tok, C, 16,
+                                       B, G=G)
+        assert np.array_equal(idx.cpu().numpy(), o_idx), ("q=0", B)
 
 
 # ------------------------------------------------------------- clustering --
