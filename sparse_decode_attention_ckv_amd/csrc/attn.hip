@@ -9,9 +9,10 @@
 // each in bf16) is read once, and the G query heads of a KV head share that
 // gather.
 //  * partial, grid (splits, KV heads): a workgroup takes R = 64 consecutive
-//    entries of idx: 16 lanes per row, 16 bytes per lane, the idx, q and then
-//    all K/V loads of a thread in flight at once; scores for the G heads,
-//    split max, exp, weighted V sum -> (m, l, acc[d]) per query head;
+//    entries of idx, the idx and then all K/V/q loads of a thread in flight
+//    at once; scores for the G heads (bf16: one MFMA tile per wave; fp32:
+//    16 lanes per row), split max, exp, weighted V sum (16 lanes per row) ->
+//    (m, l, acc[d]) per query head;
 //  * combine, one workgroup per query head: o = sum_s e^{m_s - M} acc_s /
 //    sum_s e^{m_s - M} l_s, summed in split order.
 // A kernel boundary hands the partials over: on this multi-XCD part a
@@ -188,6 +189,143 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 
 }
 
+// partial, bf16: the scores of the split come from one MFMA tile per wave.
+// v_mfma_f32_16x16x32_bf16 with the query heads on M (rows 0..G-1 of the A
+// tile, the rest zero) and the wave's 16 rows of the split on N: lane l
+// supplies, for k step t, channels 32t + 8(l>>4) .. +7 of head (l & 15) (A) and
+// of row 16*wave + (l & 15) (B), and receives the scores of heads
+// 4(l>>4) + i, i = 0..3, for that row. No cross-lane reduction is needed.
+// V is accumulated as in the generic kernel (16 lanes per row, fp32).
+template <int G>
+__global__ __launch_bounds__(256) void k_attn_partial_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int64_t kv_head_stride, int64_t kv_rows,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ n_sel, int B, double scale,
+    float *__restrict__ part) {
+    constexpr int PW = kD + 2;
+    __shared__ float zs[G][kAttnRows];
+    __shared__ float red[4][G][kD + 1];
+    const int s = blockIdx.x, h = blockIdx.y, S = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kq = lane >> 4;    // MFMA fragment coordinates
+    const int slot = tid >> 4, q8 = tid & 15;     // V layout: row slot, channel chunk
+    const int r0 = s * kAttnRows;
+    const int32_t *ih = idx + (int64_t)h * B;
+
+    // idx of this lane's score row and of its 4 V rows (clamped, not waiting
+    // for n_sel)
+    const int rK = r0 + 16 * wave + col;
+    const int tkK = ih[rK < B ? rK : B - 1];
+    int tkV[kRowsPerSlot];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        const int r = r0 + slot + 16 * k;
+        tkV[k] = ih[r < B ? r : B - 1];
+    }
+    int n = n_sel[h];
+    n = n < 0 ? 0 : (n > B ? B : n);
+    const bool okK = rK < n && tkK >= 0 && (int64_t)tkK < kv_rows;
+    const int64_t rowK = okK ? tkK : 0;
+    bool okV[kRowsPerSlot];
+    int64_t rowV[kRowsPerSlot];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        const int r = r0 + slot + 16 * k;
+        okV[k] = r < n && tkV[k] >= 0 && (int64_t)tkV[k] < kv_rows;
+        rowV[k] = okV[k] ? tkV[k] : 0;
+    }
+    // every K fragment, V chunk and q fragment of this thread in flight
+    const uint16_t *Kh = K + (int64_t)h * kv_head_stride;
+    const uint16_t *Vh = V + (int64_t)h * kv_head_stride;
+    const uint16_t *qrow = q + ((int64_t)h * G + (col < G ? col : 0)) * kD;
+    u32x4 kb[4], qa[4], vr[kRowsPerSlot];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kb[t] = *(const u32x4 *)(Kh + rowK * kD + 32 * t + 8 * kq);
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) vr[k] = *(const u32x4 *)(Vh + rowV[k] * kD + 8 * q8);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[t] = *(const u32x4 *)(qrow + 32 * t + 8 * kq);
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const u32x4 a = col < G ? qa[t] : (u32x4){0u, 0u, 0u, 0u};
+        acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, kb[t]), acc4,
+                                                       0, 0, 0);
+    }
+    const float fscale = (float)scale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = 4 * kq + i;
+        if (g < G) zs[g][16 * wave + col] = okK ? acc4[i] * fscale : -INFINITY;
+    }
+    __syncthreads();
+
+    float vf[kRowsPerSlot][8];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        unpack8(vr[k], vf[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[k][e] = okV[k] ? vf[k][e] : 0.f;
+    }
+    float mx[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float m = -INFINITY;
+#pragma unroll 8
+        for (int r = 0; r < kAttnRows; ++r) m = zs[g][r] > m ? zs[g][r] : m;
+        mx[g] = m;
+    }
+    float acc[G][8], l[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+#pragma unroll
+        for (int k = 0; k < kRowsPerSlot; ++k) {
+            const float z = zs[g][slot + 16 * k];
+            const float p = okV[k] ? __expf(z - mx[g]) : 0.f;
+            l[g] += p;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] += p * vf[k][e];
+        }
+    }
+    // the 4 slots of a wave (lanes q8, q8+16, q8+32, q8+48), then the 4 waves
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] += __shfl_xor(l[g], 16);
+        l[g] += __shfl_xor(l[g], 32);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[g][e] += __shfl_xor(acc[g][e], 16);
+            acc[g][e] += __shfl_xor(acc[g][e], 32);
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wave][g][8 * lane + e] = acc[g][e];
+            if (lane == 0) red[wave][g][kD] = l[g];
+        }
+    }
+    __syncthreads();
+    for (int w = tid; w < G * (kD + 1); w += 256) {
+        const int g = w / (kD + 1), j = w % (kD + 1);
+        const float v = ((red[0][g][j] + red[1][g][j]) + red[2][g][j]) + red[3][g][j];
+        float *dst = part + (((int64_t)h * G + g) * S + s) * PW;
+        if (j == kD) {
+            dst[0] = mx[g];
+            dst[1] = v;
+        } else {
+            dst[2 + j] = v;
+        }
+    }
+}
+
 // combine: one workgroup per query head, thread j owns channel j; the
 // split records are read in batches with every load of a batch in flight.
 template <typename A>
@@ -236,9 +374,15 @@ template <typename T, int G>
 static void launch_g(const AttnPlan &p, const void *q, const void *K, const void *V,
                      const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s) {
     typedef typename Acc<T>::type A;
-    hipLaunchKernelGGL((k_attn_partial<T, G>), dim3(p.S, p.H), dim3(256), 0, s, (const T *)q,
-                       (const T *)K, (const T *)V, p.kv_head_stride, p.kv_rows, idx, n_sel,
-                       p.B, p.scale, (A *)p.partials);
+    if (sizeof(T) == 2)
+        hipLaunchKernelGGL((k_attn_partial_bf16<G>), dim3(p.S, p.H), dim3(256), 0, s,
+                           (const uint16_t *)q, (const uint16_t *)K, (const uint16_t *)V,
+                           p.kv_head_stride, p.kv_rows, idx, n_sel, p.B, p.scale,
+                           (float *)p.partials);
+    else
+        hipLaunchKernelGGL((k_attn_partial<T, G>), dim3(p.S, p.H), dim3(256), 0, s,
+                           (const T *)q, (const T *)K, (const T *)V, p.kv_head_stride,
+                           p.kv_rows, idx, n_sel, p.B, p.scale, (A *)p.partials);
 }
 
 template <typename T>

@@ -18,7 +18,7 @@
 //  2. the clusters admitted "in descending score until the budget" are found
 //     without sorting: a weighted radix select over the rank key (score
 //     descending, then id ascending) finds the cluster at which the running
-//     size total first reaches the budget (the cut), 8-bit digits from the
+//     size total first reaches the budget (the cut), 11-bit digits from the
 //     most significant, histograms of sizes in LDS.
 //  3. every cluster ranked before the cut gives all its tokens, the cut
 //     cluster gives what still fits; tokens are emitted by cluster id
@@ -32,6 +32,13 @@ constexpr int kSelLanes = 4;                        // lanes per cluster while s
 constexpr int kSelPass = kSelThreads / kSelLanes;   // clusters per scoring pass
 constexpr int kSelInFlight = 2;                     // passes whose loads fly together
 constexpr int kSelPer = kMaxC / kSelThreads;        // clusters per thread later (2)
+
+// Radix select on the 75-bit rank key (64-bit score key, then the 11-bit
+// cluster id), 11-bit digits from the most significant; the last pass is the
+// id itself (ids < kMaxC = 2^11).
+constexpr int kRadixBuckets = 2048;
+constexpr int kRadixPasses = 7;     // key bits 63..53, 52..42, 41..31, 30..20, 19..9, 10..0; id
+static_assert(kMaxC <= kRadixBuckets, "the id digit must fit one pass");
 
 // Order-preserving 64-bit image of a finite double, inverted so that a larger
 // score gives a smaller key; -0 and +0 map to the same key.
@@ -53,7 +60,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     __shared__ int wt[kMaxC];          // cluster sizes, later the tokens each gives
     __shared__ int off[kMaxC + 1];     // clamped offsets
     __shared__ int inc[kMaxC];         // inclusive prefix of the taken counts, id order
-    __shared__ int hw[256], hn[256];   // radix histograms: sizes and counts
+    __shared__ int hw[kRadixBuckets], hn[kRadixBuckets];   // radix histograms: sizes, counts
     __shared__ int wsum[17];
     __shared__ int s_bucket, s_rem, s_cnt, s_cut;
     const int T = kSelThreads, tid = threadIdx.x;
@@ -156,56 +163,36 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 #pragma unroll
         for (int u = 0; u < kSelPer; ++u) cand[u] = kSelPer * tid + u < C;
         int R = beff;
-        for (int pos = 0; pos < 10; ++pos) {
-            // digits 0..7: bytes of the rank key, high first; 8..9: id bytes
-            if (tid < 256) {
-                hw[tid] = 0;
-                hn[tid] = 0;
+        for (int pos = 0; pos < kRadixPasses; ++pos) {
+            // 11-bit digits of (rank key, id), most significant first
+            const bool in_id = pos == kRadixPasses - 1;
+            const int sh = pos < 5 ? 53 - 11 * pos : 0;   // last key digit overlaps 2 fixed bits
+#pragma unroll
+            for (int u = 0; u < kRadixBuckets / kSelThreads; ++u) {
+                hw[tid + u * kSelThreads] = 0;
+                hn[tid + u * kSelThreads] = 0;
             }
             __syncthreads();
 #pragma unroll
             for (int u = 0; u < kSelPer; ++u) {
                 const int c = kSelPer * tid + u;
                 if (cand[u]) {
-                    const int d = pos < 8 ? (int)((rkey[c] >> (56 - 8 * pos)) & 0xFF)
-                                          : (pos == 8 ? (c >> 8) & 0xFF : c & 0xFF);
+                    const int d = in_id ? c : (int)((rkey[c] >> sh) & (kRadixBuckets - 1));
                     atomicAdd(&hw[d], wt[c]);
                     atomicAdd(&hn[d], 1);
                 }
             }
             __syncthreads();
-            if (tid < 64) {
-                // buckets 4*lane .. 4*lane+3, ascending = rank order
-                int bw[4], lsum = 0;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    bw[k] = hw[4 * tid + k];
-                    lsum += bw[k];
-                }
-                int x = lsum;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const int y = __shfl_up(x, o);
-                    if (tid >= o) x += y;
-                }
-                const int before_lane = x - lsum;
-                // the lane holding the bucket where the running total reaches R
-                if (before_lane < R && x >= R) {
-                    int run = before_lane, b = 0;
-                    bool found = false;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        if (!found && run + bw[k] >= R) {
-                            b = k;
-                            found = true;
-                        } else if (!found) {
-                            run += bw[k];
-                        }
-                    }
-                    s_bucket = 4 * tid + b;
-                    s_rem = R - run;
-                    s_cnt = hn[4 * tid + b];
-                }
+            // buckets in ascending order = rank order: 2 per thread, block scan
+            int b0 = hw[2 * tid], b1 = hw[2 * tid + 1];
+            int tot;
+            const int ex = block_excl_scan(b0 + b1, wsum, &tot);
+            if (ex < R && ex + b0 + b1 >= R) {
+                const int b = (ex + b0 >= R) ? 2 * tid : 2 * tid + 1;
+                const int before = (ex + b0 >= R) ? ex : ex + b0;
+                s_bucket = b;
+                s_rem = R - before;
+                s_cnt = hn[b];
             }
             __syncthreads();
             const int bsel = s_bucket;
@@ -214,8 +201,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
             for (int u = 0; u < kSelPer; ++u) {
                 const int c = kSelPer * tid + u;
                 if (cand[u]) {
-                    const int d = pos < 8 ? (int)((rkey[c] >> (56 - 8 * pos)) & 0xFF)
-                                          : (pos == 8 ? (c >> 8) & 0xFF : c & 0xFF);
+                    const int d = in_id ? c : (int)((rkey[c] >> sh) & (kRadixBuckets - 1));
                     cand[u] = d == bsel;
                 }
             }
