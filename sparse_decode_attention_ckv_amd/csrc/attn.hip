@@ -189,13 +189,15 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 
 }
 
-// partial, bf16: the scores of the split come from one MFMA tile per wave.
-// v_mfma_f32_16x16x32_bf16 with the query heads on M (rows 0..G-1 of the A
-// tile, the rest zero) and the wave's 16 rows of the split on N: lane l
-// supplies, for k step t, channels 32t + 8(l>>4) .. +7 of head (l & 15) (A) and
-// of row 16*wave + (l & 15) (B), and receives the scores of heads
-// 4(l>>4) + i, i = 0..3, for that row. No cross-lane reduction is needed.
-// V is accumulated as in the generic kernel (16 lanes per row, fp32).
+// partial, bf16. Scores: one MFMA tile per wave, v_mfma_f32_16x16x32_bf16
+// with the query heads on M (rows 0..G-1 of the A tile, the rest zero) and
+// the wave's 16 rows of the split on N: lane l supplies, for k step t,
+// channels 32t + 8(l>>4) .. +7 of head (l & 15) (A) and of row
+// 16*wave + (l & 15) (B), and receives the scores of heads 4(l>>4) + i for
+// that row. Softmax and V: wave w takes the heads g = w, w+4; lane l owns
+// channels 2l, 2l+1 and row l of the split, so the max and the sum of p are
+// 64-lane wave reductions and the V sum runs over the rows with p_r taken
+// from lane r (readlane): no cross-lane reduction of the accumulators.
 template <int G>
 __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
@@ -204,47 +206,39 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     float *__restrict__ part) {
     constexpr int PW = kD + 2;
     __shared__ float zs[G][kAttnRows];
-    __shared__ float red[4][G][kD + 1];
     const int s = blockIdx.x, h = blockIdx.y, S = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kq = lane >> 4;    // MFMA fragment coordinates
-    const int slot = tid >> 4, q8 = tid & 15;     // V layout: row slot, channel chunk
     const int r0 = s * kAttnRows;
     const int32_t *ih = idx + (int64_t)h * B;
 
-    // idx of this lane's score row and of its 4 V rows (clamped, not waiting
-    // for n_sel)
-    const int rK = r0 + 16 * wave + col;
+    // idx of this lane's V row (row `lane` of the split) and of its score row
+    // (clamped; not waiting for n_sel)
+    const int rV = r0 + lane, rK = r0 + 16 * wave + col;
+    const int tkV = ih[rV < B ? rV : B - 1];
     const int tkK = ih[rK < B ? rK : B - 1];
-    int tkV[kRowsPerSlot];
-#pragma unroll
-    for (int k = 0; k < kRowsPerSlot; ++k) {
-        const int r = r0 + slot + 16 * k;
-        tkV[k] = ih[r < B ? r : B - 1];
-    }
     int n = n_sel[h];
     n = n < 0 ? 0 : (n > B ? B : n);
     const bool okK = rK < n && tkK >= 0 && (int64_t)tkK < kv_rows;
-    const int64_t rowK = okK ? tkK : 0;
-    bool okV[kRowsPerSlot];
-    int64_t rowV[kRowsPerSlot];
-#pragma unroll
-    for (int k = 0; k < kRowsPerSlot; ++k) {
-        const int r = r0 + slot + 16 * k;
-        okV[k] = r < n && tkV[k] >= 0 && (int64_t)tkV[k] < kv_rows;
-        rowV[k] = okV[k] ? tkV[k] : 0;
-    }
-    // every K fragment, V chunk and q fragment of this thread in flight
+    const int rowK = okK ? tkK : 0;
+    const bool okV = rV < n && tkV >= 0 && (int64_t)tkV < kv_rows;
+    const int rowV = okV ? tkV : 0;
+
+    // every K fragment, q fragment and V word of this thread in flight
     const uint16_t *Kh = K + (int64_t)h * kv_head_stride;
     const uint16_t *Vh = V + (int64_t)h * kv_head_stride;
     const uint16_t *qrow = q + ((int64_t)h * G + (col < G ? col : 0)) * kD;
-    u32x4 kb[4], qa[4], vr[kRowsPerSlot];
+    u32x4 kb[4], qa[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) kb[t] = *(const u32x4 *)(Kh + rowK * kD + 32 * t + 8 * kq);
-#pragma unroll
-    for (int k = 0; k < kRowsPerSlot; ++k) vr[k] = *(const u32x4 *)(Vh + rowV[k] * kD + 8 * q8);
+    for (int t = 0; t < 4; ++t) kb[t] = *(const u32x4 *)(Kh + (int64_t)rowK * kD + 32 * t + 8 * kq);
 #pragma unroll
     for (int t = 0; t < 4; ++t) qa[t] = *(const u32x4 *)(qrow + 32 * t + 8 * kq);
+    uint32_t vv[kAttnRows];
+#pragma unroll
+    for (int r = 0; r < kAttnRows; ++r) {
+        const int row = __builtin_amdgcn_readlane(rowV, r);
+        vv[r] = *(const uint32_t *)(Vh + (int64_t)row * kD + 2 * lane);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
@@ -263,66 +257,31 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     }
     __syncthreads();
 
-    float vf[kRowsPerSlot][8];
+    for (int g = wave; g < G; g += 4) {
+        const float z = zs[g][lane];
+        float m = z;
 #pragma unroll
-    for (int k = 0; k < kRowsPerSlot; ++k) {
-        unpack8(vr[k], vf[k]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[k][e] = okV[k] ? vf[k][e] : 0.f;
-    }
-    float mx[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float m = -INFINITY;
-#pragma unroll 8
-        for (int r = 0; r < kAttnRows; ++r) m = zs[g][r] > m ? zs[g][r] : m;
-        mx[g] = m;
-    }
-    float acc[G][8], l[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-#pragma unroll
-        for (int k = 0; k < kRowsPerSlot; ++k) {
-            const float z = zs[g][slot + 16 * k];
-            const float p = okV[k] ? __expf(z - mx[g]) : 0.f;
-            l[g] += p;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] += p * vf[k][e];
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float y = __shfl_xor(m, o);
+            m = y > m ? y : m;
         }
-    }
-    // the 4 slots of a wave (lanes q8, q8+16, q8+32, q8+48), then the 4 waves
+        const float p = (z > -INFINITY) ? __expf(z - m) : 0.f;
+        float l = p;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] += __shfl_xor(l[g], 16);
-        l[g] += __shfl_xor(l[g], 32);
+        for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            acc[g][e] += __shfl_xor(acc[g][e], 16);
-            acc[g][e] += __shfl_xor(acc[g][e], 32);
+        for (int r = 0; r < kAttnRows; ++r) {
+            const float pr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p), r));
+            a0 += pr * bf16_lo(vv[r]);
+            a1 += pr * bf16_hi(vv[r]);
         }
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[wave][g][8 * lane + e] = acc[g][e];
-            if (lane == 0) red[wave][g][kD] = l[g];
-        }
-    }
-    __syncthreads();
-    for (int w = tid; w < G * (kD + 1); w += 256) {
-        const int g = w / (kD + 1), j = w % (kD + 1);
-        const float v = ((red[0][g][j] + red[1][g][j]) + red[2][g][j]) + red[3][g][j];
         float *dst = part + (((int64_t)h * G + g) * S + s) * PW;
-        if (j == kD) {
-            dst[0] = mx[g];
-            dst[1] = v;
-        } else {
-            dst[2 + j] = v;
+        if (lane == 0) {
+            dst[0] = m;
+            dst[1] = l;
         }
+        *(float2 *)(dst + 2 + 2 * lane) = make_float2(a0, a1);
     }
 }
 

@@ -7,7 +7,7 @@
 // (selection and indexing, Fig. 8: cluster sizes, prefix sums, where the
 // budget falls, trim of the last cluster, token indices).
 //
-// One kernel per decode step, one 1024-thread workgroup per KV head, no
+// One kernel per decode step, one 512-thread workgroup per KV head, no
 // cross-workgroup handoff:
 //  1. score every cluster, s_c = q_g . mu_c in fp64 with the fixed
 //     association of the definition (32 fma chains of 4 channels, pairwise
@@ -27,17 +27,16 @@
 
 namespace ckv {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 constexpr int kSelLanes = 4;                        // lanes per cluster while scoring
 constexpr int kSelPass = kSelThreads / kSelLanes;   // clusters per scoring pass
-constexpr int kSelInFlight = 2;                     // passes whose loads fly together
-constexpr int kSelPer = kMaxC / kSelThreads;        // clusters per thread later (2)
+constexpr int kSelInFlight = 4;                     // passes whose loads fly together
+constexpr int kSelPer = kMaxC / kSelThreads;        // clusters per thread later (4)
 
 // Radix select on the 75-bit rank key (64-bit score key, then the 11-bit
-// cluster id), 11-bit digits from the most significant; the last pass is the
-// id itself (ids < kMaxC = 2^11).
+// cluster id), 11-bit digits from the most significant differing bit; the
+// last pass is the id itself (ids < kMaxC = 2^11).
 constexpr int kRadixBuckets = 2048;
-constexpr int kRadixPasses = 7;     // key bits 63..53, 52..42, 41..31, 30..20, 19..9, 10..0; id
 static_assert(kMaxC <= kRadixBuckets, "the id digit must fit one pass");
 
 // Order-preserving 64-bit image of a finite double, inverted so that a larger
@@ -63,10 +62,25 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     __shared__ int hw[kRadixBuckets], hn[kRadixBuckets];   // radix histograms: sizes, counts
     __shared__ int wsum[17];
     __shared__ int s_bucket, s_rem, s_cnt, s_cut;
+    __shared__ uint64_t s_wmin[kSelThreads / 64], s_wmax[kSelThreads / 64];
     const int T = kSelThreads, tid = threadIdx.x;
     const int h = blockIdx.x;
 
-    // ---- offsets and q_g (all loads of a thread in flight at once) --------
+    // ---- loads: the first batch of centroid chunks, the offsets and q, all
+    // in flight together (the centroids do not wait for q) ------------------
+    const int lam = tid & (kSelLanes - 1), slot = tid >> 2;
+    const float *ch = cent + (int64_t)h * c_cap * kD;
+    u32x4 w[kSelInFlight][8];
+    auto load_batch = [&](int p0) {
+#pragma unroll
+        for (int pi = 0; pi < kSelInFlight; ++pi) {
+            const int c = p0 + pi * kSelPass + slot;
+            const float *row = ch + (int64_t)(c < C ? c : C - 1) * kD;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[pi][i] = *(const u32x4 *)(row + 4 * (lam + 4 * i));
+        }
+    };
+    load_batch(0);
     const int32_t *offh = offsets + (int64_t)h * (c_cap + 1);
     {
         constexpr int NO = (kMaxC + kSelThreads) / kSelThreads;
@@ -100,61 +114,75 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     __syncthreads();
 
     // ---- 1. scores -> rank keys; sizes ------------------------------------
-    {
-        const int lam = tid & (kSelLanes - 1), slot = tid >> 2;
-        const float *ch = cent + (int64_t)h * c_cap * kD;
-        for (int p0 = 0; p0 < C; p0 += kSelPass * kSelInFlight) {
-            u32x4 w[kSelInFlight][8];
+    for (int p0 = 0; p0 < C; p0 += kSelPass * kSelInFlight) {
+        if (p0 > 0) load_batch(p0);
 #pragma unroll
-            for (int pi = 0; pi < kSelInFlight; ++pi) {
-                const int c = p0 + pi * kSelPass + slot;
-                const float *row = ch + (int64_t)(c < C ? c : C - 1) * kD;
+        for (int pi = 0; pi < kSelInFlight; ++pi) {
+            const int c = p0 + pi * kSelPass + slot;
+            double run[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) w[pi][i] = *(const u32x4 *)(row + 4 * (lam + 4 * i));
+            for (int i = 0; i < 8; ++i) {
+                const double *qr = qg + 4 * (lam + 4 * i);
+                double a = 0.0;
+                a = __fma_rn(qr[0], (double)__uint_as_float(w[pi][i].x), a);
+                a = __fma_rn(qr[1], (double)__uint_as_float(w[pi][i].y), a);
+                a = __fma_rn(qr[2], (double)__uint_as_float(w[pi][i].z), a);
+                a = __fma_rn(qr[3], (double)__uint_as_float(w[pi][i].w), a);
+                run[i] = a;
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int pi = 0; pi < kSelInFlight; ++pi) {
-                const int c = p0 + pi * kSelPass + slot;
-                double run[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const double *qr = qg + 4 * (lam + 4 * i);
-                    double a = 0.0;
-                    a = __fma_rn(qr[0], (double)__uint_as_float(w[pi][i].x), a);
-                    a = __fma_rn(qr[1], (double)__uint_as_float(w[pi][i].y), a);
-                    a = __fma_rn(qr[2], (double)__uint_as_float(w[pi][i].z), a);
-                    a = __fma_rn(qr[3], (double)__uint_as_float(w[pi][i].w), a);
-                    run[i] = a;
-                }
-                // levels r + r+16, r + r+8, r + r+4 (runs lam + 4i of this lane)
-                const double t0 = run[0] + run[4], t1 = run[1] + run[5];
-                const double t2 = run[2] + run[6], t3 = run[3] + run[7];
-                double v = (t0 + t2) + (t1 + t3);
-                // levels r + r+2 and r + r+1 across the four lanes
-                v = v + __shfl_xor(v, 2);
-                v = v + __shfl_xor(v, 1);
-                if (lam == 0 && c < C) rkey[c] = rank_key(v);
-            }
+            // levels r + r+16, r + r+8, r + r+4 (runs lam + 4i of this lane)
+            const double t0 = run[0] + run[4], t1 = run[1] + run[5];
+            const double t2 = run[2] + run[6], t3 = run[3] + run[7];
+            double v = (t0 + t2) + (t1 + t3);
+            // levels r + r+2 and r + r+1 across the four lanes
+            v = v + __shfl_xor(v, 2);
+            v = v + __shfl_xor(v, 1);
+            if (lam == 0 && c < C) rkey[c] = rank_key(v);
         }
-        for (int c = tid; c < C; c += T) {
-            const int n = off[c + 1] - off[c];
-            wt[c] = n > 0 ? n : 0;
-        }
+    }
+    for (int c = tid; c < C; c += T) {
+        const int n = off[c + 1] - off[c];
+        wt[c] = n > 0 ? n : 0;
     }
     __syncthreads();
 
     // ---- 2. the cut: first cluster (rank order) where the sizes reach B_eff
     const int64_t beff64 = (int64_t)B - n_sink - n_pending;
     const int beff = (int)(beff64 > 0 ? beff64 : 0);
+    // total size and the smallest / largest rank key: per thread, then the
+    // wave (shuffles), then the waves (LDS)
     int loc = 0;
+    uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u) {
         const int c = kSelPer * tid + u;
-        loc += c < C ? wt[c] : 0;
+        if (c < C) {
+            loc += wt[c];
+            const uint64_t k = rkey[c];
+            kmin = k < kmin ? k : kmin;
+            kmax = k > kmax ? k : kmax;
+        }
     }
-    int total;
-    block_excl_scan(loc, wsum, &total);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        loc += __shfl_xor(loc, o);
+        const uint64_t a = __shfl_xor(kmin, o), b = __shfl_xor(kmax, o);
+        kmin = a < kmin ? a : kmin;
+        kmax = b > kmax ? b : kmax;
+    }
+    if ((tid & 63) == 0) {
+        wsum[tid >> 6] = loc;
+        s_wmin[tid >> 6] = kmin;
+        s_wmax[tid >> 6] = kmax;
+    }
+    __syncthreads();
+    int total = 0;
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+        total += wsum[w];
+        kmin = s_wmin[w] < kmin ? s_wmin[w] : kmin;
+        kmax = s_wmax[w] > kmax ? s_wmax[w] : kmax;
+    }
+    __syncthreads();
     int cut = -1, rem = 0;                 // no cut: every cluster gives all
     if (beff == 0) {
         cut = -2;                          // nothing is taken
@@ -163,10 +191,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 #pragma unroll
         for (int u = 0; u < kSelPer; ++u) cand[u] = kSelPer * tid + u < C;
         int R = beff;
-        for (int pos = 0; pos < kRadixPasses; ++pos) {
-            // 11-bit digits of (rank key, id), most significant first
-            const bool in_id = pos == kRadixPasses - 1;
-            const int sh = pos < 5 ? 53 - 11 * pos : 0;   // last key digit overlaps 2 fixed bits
+        // every key lies between the smallest and the largest, so all share
+        // the bits above the highest bit where those two differ: the digits
+        // start there (11 bits each, the last one may overlap fixed bits),
+        // then one pass on the cluster id breaks exact ties
+        const uint64_t kdiff = kmin ^ kmax;
+        const int hb = kdiff ? 63 - __clzll((long long)kdiff) : -1;
+        const int nkey = hb < 0 ? 0 : (hb + 11) / 11;       // key passes
+        for (int pos = 0; pos <= nkey; ++pos) {
+            const bool in_id = pos == nkey;
+            int sh = hb - 10 - 11 * pos;
+            sh = sh < 0 ? 0 : sh;
 #pragma unroll
             for (int u = 0; u < kRadixBuckets / kSelThreads; ++u) {
                 hw[tid + u * kSelThreads] = 0;
@@ -183,16 +218,32 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
                 }
             }
             __syncthreads();
-            // buckets in ascending order = rank order: 2 per thread, block scan
-            int b0 = hw[2 * tid], b1 = hw[2 * tid + 1];
+            // buckets in ascending order = rank order: NBK consecutive ones per
+            // thread, block scan; the thread whose range reaches R picks it
+            constexpr int NBK = kRadixBuckets / kSelThreads;
+            int bk[NBK], bsum = 0;
+#pragma unroll
+            for (int k = 0; k < NBK; ++k) {
+                bk[k] = hw[NBK * tid + k];
+                bsum += bk[k];
+            }
             int tot;
-            const int ex = block_excl_scan(b0 + b1, wsum, &tot);
-            if (ex < R && ex + b0 + b1 >= R) {
-                const int b = (ex + b0 >= R) ? 2 * tid : 2 * tid + 1;
-                const int before = (ex + b0 >= R) ? ex : ex + b0;
-                s_bucket = b;
+            const int ex = block_excl_scan(bsum, wsum, &tot);
+            if (ex < R && ex + bsum >= R) {
+                int before = ex, b = NBK - 1;
+                bool found = false;
+#pragma unroll
+                for (int k = 0; k < NBK; ++k) {
+                    if (!found && before + bk[k] >= R) {
+                        b = k;
+                        found = true;
+                    } else if (!found) {
+                        before += bk[k];
+                    }
+                }
+                s_bucket = NBK * tid + b;
                 s_rem = R - before;
-                s_cnt = hn[b];
+                s_cnt = hn[NBK * tid + b];
             }
             __syncthreads();
             const int bsel = s_bucket;
