@@ -45,34 +45,104 @@ __device__ __forceinline__ uint32_t xcd_linear(uint32_t bid, uint32_t n) {
     return (bid & 7u) * (n >> 3) + (bid >> 3);
 }
 
-// Exclusive scan over a block of up to 1024 threads (every thread calls it);
-// returns this thread's exclusive prefix; *total receives the block sum.
-// wsum: 17 ints of LDS.
-__device__ inline int block_excl_scan(int v, int *wsum, int *total) {
+// ---- wave- and block-wide scans (DPP, no LDS round trips inside a wave) --
+// DPP controls of the gfx9 family: row_shr:n shifts within a row of 16 lanes;
+// row_bcast:15 copies lane 15 of each row into the next row, row_bcast:31
+// copies lane 31 into rows 2 and 3.
+constexpr int kDppRowShr = 0x110, kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 1, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 2, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 4, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 8, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppBcast15, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppBcast31, 0xc, 0xf, false);
+    return x;
+}
+
+// Sum over the wave, the same value in every lane.
+__device__ __forceinline__ int wave_sum(int x) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+// One DPP step on a double: lanes whose source is outside the row mask or
+// the row read `id` instead.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double x, double id) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x), v = (uint64_t)__double_as_longlong(id);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)u,
+                                                               CTRL, ROWS, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32),
+                                                               (int)(uint32_t)(u >> 32), CTRL,
+                                                               ROWS, 0xf, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Largest and smallest value over the wave (uniform results). Finite or
+// infinite inputs; a NaN lane is ignored unless every lane is NaN.
+__device__ __forceinline__ void wave_minmax_f64(double &mn, double &mx) {
+    const double pinf = __longlong_as_double(0x7ff0000000000000ll), ninf = -pinf;
+#define CKV_MM_STEP(CTRL, ROWS)                               \
+    mn = fmin(mn, dpp_f64<CTRL, ROWS>(mn, pinf));            \
+    mx = fmax(mx, dpp_f64<CTRL, ROWS>(mx, ninf));
+    CKV_MM_STEP(kDppRowShr + 1, 0xf)
+    CKV_MM_STEP(kDppRowShr + 2, 0xf)
+    CKV_MM_STEP(kDppRowShr + 4, 0xf)
+    CKV_MM_STEP(kDppRowShr + 8, 0xf)
+    CKV_MM_STEP(kDppBcast15, 0xa)
+    CKV_MM_STEP(kDppBcast31, 0xc)
+#undef CKV_MM_STEP
+    const uint64_t a = (uint64_t)__double_as_longlong(mn), b = (uint64_t)__double_as_longlong(mx);
+    const uint32_t alo = __builtin_amdgcn_readlane((int)(uint32_t)a, 63);
+    const uint32_t ahi = __builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), 63);
+    const uint32_t blo = __builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+    const uint32_t bhi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+    mn = __longlong_as_double((long long)(((uint64_t)ahi << 32) | alo));
+    mx = __longlong_as_double((long long)(((uint64_t)bhi << 32) | blo));
+}
+
+// Exclusive scan over a block of NW full waves with one barrier: wave scans,
+// wave totals through LDS (wsum, NW ints), every thread adds the totals of
+// the waves before its own. The caller places a barrier before wsum is
+// written again.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan_nw(int v, int *wsum, int &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nw = (blockDim.x + 63) >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int w = 0; w < nw; ++w) {
-            const int t = wsum[w];
-            wsum[w] = run;
-            run += t;
-        }
-        wsum[16] = run;
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int t = wsum[w];
+        before += w < wave ? t : 0;
+        tot += t;
     }
+    total = tot;
+    return before + x - v;
+}
+
+// Exclusive scan over a block of up to 1024 threads, a multiple of 64
+// (every thread calls it); returns this thread's exclusive prefix; *total
+// receives the block sum. wsum: 17 ints of LDS. Ends with a barrier, so wsum
+// may be reused at once.
+__device__ inline int block_excl_scan(int v, int *wsum, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    const int x = wave_incl_scan(v);
+    if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    const int r = wsum[wave] + x - v;
-    *total = wsum[16];
+    int before = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int t = wsum[w];
+        before += w < wave ? t : 0;
+        tot += t;
+    }
+    *total = tot;
     __syncthreads();
-    return r;
+    return before + x - v;
 }
 
 // ---- launchers (defined in the .hip files) ------------------------------

@@ -16,10 +16,14 @@
 //     lane and only the last two cross lanes. Every centroid load of a batch
 //     is in flight at once.
 //  2. the clusters admitted "in descending score until the budget" are found
-//     without sorting: a weighted radix select over the rank key (score
-//     descending, then id ascending) finds the cluster at which the running
-//     size total first reaches the budget (the cut), 11-bit digits from the
-//     most significant, histograms of sizes in LDS.
+//     without sorting, by a weighted select over the rank order (score
+//     descending, then id ascending): the cut is the cluster at which the
+//     running size total first reaches the budget. A first pass histograms
+//     the sizes over 2048 equal-width score buckets between the smallest and
+//     the largest score (a monotone map, so bucket order is rank order); when
+//     the bucket that reaches the budget holds one cluster, that is the cut.
+//     Otherwise exact radix passes over the 75-bit rank key (64-bit score
+//     key, then the cluster id) of that bucket's clusters finish the job.
 //  3. every cluster ranked before the cut gives all its tokens, the cut
 //     cluster gives what still fits; tokens are emitted by cluster id
 //     (prefix sum in id order, one output slot per thread, binary search).
@@ -33,11 +37,11 @@ constexpr int kSelPass = kSelThreads / kSelLanes;   // clusters per scoring pass
 constexpr int kSelInFlight = 4;                     // passes whose loads fly together
 constexpr int kSelPer = kMaxC / kSelThreads;        // clusters per thread later (4)
 
-// Radix select on the 75-bit rank key (64-bit score key, then the 11-bit
-// cluster id), 11-bit digits from the most significant differing bit; the
-// last pass is the id itself (ids < kMaxC = 2^11).
+// Buckets of the score pass and of each exact pass (11-bit digits; the last
+// exact pass is the id itself, ids < kMaxC = 2^11).
 constexpr int kRadixBuckets = 2048;
 static_assert(kMaxC <= kRadixBuckets, "the id digit must fit one pass");
+constexpr int kCntBits = 12;            // histogram entry: size << 12 | count
 
 // Order-preserving 64-bit image of a finite double, inverted so that a larger
 // score gives a smaller key; -0 and +0 map to the same key.
@@ -54,15 +58,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ tokens, int64_t t_cap,
     int n_sink, int64_t pending_begin, int64_t n_pending, int B, int32_t *__restrict__ idx,
     int32_t *__restrict__ n_sel) {
+    constexpr int NW = kSelThreads / 64;
     __shared__ double qg[kD];
-    __shared__ uint64_t rkey[kMaxC];
-    __shared__ int wt[kMaxC];          // cluster sizes, later the tokens each gives
-    __shared__ int off[kMaxC + 1];     // clamped offsets
-    __shared__ int inc[kMaxC];         // inclusive prefix of the taken counts, id order
-    __shared__ int hw[kRadixBuckets], hn[kRadixBuckets];   // radix histograms: sizes, counts
-    __shared__ int wsum[17];
+    __shared__ double sc[kMaxC];           // scores
+    __shared__ int wt[kMaxC];              // tokens each cluster gives
+    __shared__ int off[kMaxC + 1];         // clamped offsets
+    __shared__ int inc[kMaxC];             // inclusive prefix of wt in id order;
+                                           // before that, a bucket's last cluster
+    __shared__ uint64_t hist[kRadixBuckets];
+    __shared__ int ws_a[NW], ws_b[NW], ws_c[NW];
+    __shared__ double s_mn[NW], s_mx[NW];
     __shared__ int s_bucket, s_rem, s_cnt, s_cut;
-    __shared__ uint64_t s_wmin[kSelThreads / 64], s_wmax[kSelThreads / 64];
+    __shared__ unsigned long long s_kmin, s_kmax;
     const int T = kSelThreads, tid = threadIdx.x;
     const int h = blockIdx.x;
 
@@ -137,138 +144,206 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
             // levels r + r+2 and r + r+1 across the four lanes
             v = v + __shfl_xor(v, 2);
             v = v + __shfl_xor(v, 1);
-            if (lam == 0 && c < C) rkey[c] = rank_key(v);
+            if (lam == 0 && c < C) sc[c] = v;
         }
     }
-    for (int c = tid; c < C; c += T) {
-        const int n = off[c + 1] - off[c];
-        wt[c] = n > 0 ? n : 0;
+    // the first histogram starts cleared
+#pragma unroll
+    for (int u = 0; u < kRadixBuckets / kSelThreads; ++u) hist[tid + u * kSelThreads] = 0;
+    if (tid == 0) {
+        s_kmin = ~0ull;
+        s_kmax = 0ull;
     }
     __syncthreads();
 
     // ---- 2. the cut: first cluster (rank order) where the sizes reach B_eff
     const int64_t beff64 = (int64_t)B - n_sink - n_pending;
     const int beff = (int)(beff64 > 0 ? beff64 : 0);
-    // total size and the smallest / largest rank key: per thread, then the
-    // wave (shuffles), then the waves (LDS)
+    const double pinf = __longlong_as_double(0x7ff0000000000000ll);
+    // this thread's clusters 4 tid .. 4 tid + 3: sizes, scores; the total size
+    // and the score range over the block
+    int wv[kSelPer];
+    double sv[kSelPer];
     int loc = 0;
-    uint64_t kmin = ~0ull, kmax = 0ull;
+    double smin = pinf, smax = -pinf;
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u) {
         const int c = kSelPer * tid + u;
+        wv[u] = 0;
+        sv[u] = 0.0;
         if (c < C) {
-            loc += wt[c];
-            const uint64_t k = rkey[c];
-            kmin = k < kmin ? k : kmin;
-            kmax = k > kmax ? k : kmax;
+            const int n = off[c + 1] - off[c];
+            wv[u] = n > 0 ? n : 0;
+            sv[u] = sc[c];
+            loc += wv[u];
+            smin = fmin(smin, sv[u]);
+            smax = fmax(smax, sv[u]);
         }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        loc += __shfl_xor(loc, o);
-        const uint64_t a = __shfl_xor(kmin, o), b = __shfl_xor(kmax, o);
-        kmin = a < kmin ? a : kmin;
-        kmax = b > kmax ? b : kmax;
-    }
+    loc = wave_sum(loc);
+    wave_minmax_f64(smin, smax);
     if ((tid & 63) == 0) {
-        wsum[tid >> 6] = loc;
-        s_wmin[tid >> 6] = kmin;
-        s_wmax[tid >> 6] = kmax;
+        ws_a[tid >> 6] = loc;
+        s_mn[tid >> 6] = smin;
+        s_mx[tid >> 6] = smax;
     }
     __syncthreads();
     int total = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-        total += wsum[w];
-        kmin = s_wmin[w] < kmin ? s_wmin[w] : kmin;
-        kmax = s_wmax[w] > kmax ? s_wmax[w] : kmax;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        total += ws_a[w];
+        smin = fmin(smin, s_mn[w]);
+        smax = fmax(smax, s_mx[w]);
     }
-    __syncthreads();
     int cut = -1, rem = 0;                 // no cut: every cluster gives all
     if (beff == 0) {
         cut = -2;                          // nothing is taken
     } else if (total > beff) {
-        bool cand[kSelPer];
+        // score pass: bucket = floor((smax - s) * 2047 / (smax - smin)), a
+        // non-increasing function of s, so lower buckets rank first
+        const double range = smax - smin;
+        double scale = range > 0.0 ? (double)(kRadixBuckets - 1) / range : 0.0;
+        if (!(scale < pinf)) scale = 0.0;  // range infinite or too small
+        int bk[kSelPer];
 #pragma unroll
-        for (int u = 0; u < kSelPer; ++u) cand[u] = kSelPer * tid + u < C;
+        for (int u = 0; u < kSelPer; ++u) {
+            const int c = kSelPer * tid + u;
+            bk[u] = -1;
+            if (c < C) {
+                const double x = (smax - sv[u]) * scale;
+                const int b = x >= (double)(kRadixBuckets - 1) ? kRadixBuckets - 1
+                                                               : (x > 0.0 ? (int)x : 0);
+                bk[u] = b;
+                atomicAdd((unsigned long long *)&hist[b],
+                          ((unsigned long long)wv[u] << kCntBits) | 1ull);
+                inc[b] = c;                // the bucket's cluster when it has one
+            }
+        }
+        __syncthreads();
+        // buckets 4 tid .. 4 tid + 3 in rank order; the thread whose range of
+        // the running size reaches R names the bucket
+        constexpr int NBK = kRadixBuckets / kSelThreads;
         int R = beff;
-        // every key lies between the smallest and the largest, so all share
-        // the bits above the highest bit where those two differ: the digits
-        // start there (11 bits each, the last one may overlap fixed bits),
-        // then one pass on the cluster id breaks exact ties
-        const uint64_t kdiff = kmin ^ kmax;
-        const int hb = kdiff ? 63 - __clzll((long long)kdiff) : -1;
-        const int nkey = hb < 0 ? 0 : (hb + 11) / 11;       // key passes
-        for (int pos = 0; pos <= nkey; ++pos) {
-            const bool in_id = pos == nkey;
-            int sh = hb - 10 - 11 * pos;
-            sh = sh < 0 ? 0 : sh;
-#pragma unroll
-            for (int u = 0; u < kRadixBuckets / kSelThreads; ++u) {
-                hw[tid + u * kSelThreads] = 0;
-                hn[tid + u * kSelThreads] = 0;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < kSelPer; ++u) {
-                const int c = kSelPer * tid + u;
-                if (cand[u]) {
-                    const int d = in_id ? c : (int)((rkey[c] >> sh) & (kRadixBuckets - 1));
-                    atomicAdd(&hw[d], wt[c]);
-                    atomicAdd(&hn[d], 1);
-                }
-            }
-            __syncthreads();
-            // buckets in ascending order = rank order: NBK consecutive ones per
-            // thread, block scan; the thread whose range reaches R picks it
-            constexpr int NBK = kRadixBuckets / kSelThreads;
-            int bk[NBK], bsum = 0;
+        {
+            uint64_t hv[NBK];
+            int bsum = 0;
 #pragma unroll
             for (int k = 0; k < NBK; ++k) {
-                bk[k] = hw[NBK * tid + k];
-                bsum += bk[k];
+                hv[k] = hist[NBK * tid + k];
+                bsum += (int)(hv[k] >> kCntBits);
             }
             int tot;
-            const int ex = block_excl_scan(bsum, wsum, &tot);
+            const int ex = block_excl_scan_nw<NW>(bsum, ws_b, tot);
             if (ex < R && ex + bsum >= R) {
                 int before = ex, b = NBK - 1;
                 bool found = false;
 #pragma unroll
                 for (int k = 0; k < NBK; ++k) {
-                    if (!found && before + bk[k] >= R) {
+                    const int wk = (int)(hv[k] >> kCntBits);
+                    if (!found && before + wk >= R) {
                         b = k;
                         found = true;
                     } else if (!found) {
-                        before += bk[k];
+                        before += wk;
                     }
                 }
-                s_bucket = NBK * tid + b;
+                const int bb = NBK * tid + b;
+                const int cnt = (int)(hv[b] & ((1u << kCntBits) - 1));
+                s_bucket = bb;
                 s_rem = R - before;
-                s_cnt = hn[NBK * tid + b];
+                s_cut = cnt == 1 ? inc[bb] : -1;
             }
-            __syncthreads();
-            const int bsel = s_bucket;
-            R = s_rem;
+        }
+        __syncthreads();
+        const int bsel = s_bucket;
+        R = s_rem;
+        cut = s_cut;
+        if (cut < 0) {
+            // several clusters share that bucket: exact radix passes over their
+            // rank keys, from the highest bit where those keys differ
+            bool cand[kSelPer];
+            uint64_t key[kSelPer];
 #pragma unroll
             for (int u = 0; u < kSelPer; ++u) {
-                const int c = kSelPer * tid + u;
+                cand[u] = bk[u] == bsel;
+                key[u] = rank_key(sv[u]);
                 if (cand[u]) {
-                    const int d = in_id ? c : (int)((rkey[c] >> sh) & (kRadixBuckets - 1));
-                    cand[u] = d == bsel;
+                    atomicMin(&s_kmin, (unsigned long long)key[u]);
+                    atomicMax(&s_kmax, (unsigned long long)key[u]);
                 }
             }
-            const bool done = s_cnt == 1;  // uniform
             __syncthreads();
-            if (done) break;
-        }
+            const uint64_t kdiff = s_kmin ^ s_kmax;
+            const int hb = kdiff ? 63 - __clzll((long long)kdiff) : -1;
+            const int nkey = hb < 0 ? 0 : (hb + 11) / 11;       // key passes
+            for (int pos = 0; pos <= nkey; ++pos) {
+                const bool in_id = pos == nkey;
+                int sh = hb - 10 - 11 * pos;
+                sh = sh < 0 ? 0 : sh;
 #pragma unroll
-        for (int u = 0; u < kSelPer; ++u)
-            if (cand[u]) s_cut = kSelPer * tid + u;
-        __syncthreads();
-        cut = s_cut;
+                for (int u = 0; u < NBK; ++u) hist[tid + u * kSelThreads] = 0;
+                __syncthreads();
+#pragma unroll
+                for (int u = 0; u < kSelPer; ++u) {
+                    const int c = kSelPer * tid + u;
+                    if (cand[u]) {
+                        const int d = in_id ? c : (int)((key[u] >> sh) & (kRadixBuckets - 1));
+                        atomicAdd((unsigned long long *)&hist[d],
+                                  ((unsigned long long)wv[u] << kCntBits) | 1ull);
+                    }
+                }
+                __syncthreads();
+                uint64_t hv[NBK];
+                int bsum = 0;
+#pragma unroll
+                for (int k = 0; k < NBK; ++k) {
+                    hv[k] = hist[NBK * tid + k];
+                    bsum += (int)(hv[k] >> kCntBits);
+                }
+                int tot;
+                const int ex = block_excl_scan_nw<NW>(bsum, pos & 1 ? ws_c : ws_b, tot);
+                if (ex < R && ex + bsum >= R) {
+                    int before = ex, b = NBK - 1;
+                    bool found = false;
+#pragma unroll
+                    for (int k = 0; k < NBK; ++k) {
+                        const int wk = (int)(hv[k] >> kCntBits);
+                        if (!found && before + wk >= R) {
+                            b = k;
+                            found = true;
+                        } else if (!found) {
+                            before += wk;
+                        }
+                    }
+                    s_bucket = NBK * tid + b;
+                    s_rem = R - before;
+                    s_cnt = (int)(hv[b] & ((1u << kCntBits) - 1));
+                }
+                __syncthreads();
+                const int bs = s_bucket;
+                R = s_rem;
+#pragma unroll
+                for (int u = 0; u < kSelPer; ++u) {
+                    const int c = kSelPer * tid + u;
+                    if (cand[u]) {
+                        const int d = in_id ? c : (int)((key[u] >> sh) & (kRadixBuckets - 1));
+                        cand[u] = d == bs;
+                    }
+                }
+                const bool done = s_cnt == 1;  // uniform
+                __syncthreads();
+                if (done) break;
+            }
+#pragma unroll
+            for (int u = 0; u < kSelPer; ++u)
+                if (cand[u]) s_cut = kSelPer * tid + u;
+            __syncthreads();
+            cut = s_cut;
+        }
         rem = R;
     }
     // ---- 3. tokens each cluster gives, prefix in id order, emission --------
-    const uint64_t ck = cut >= 0 ? rkey[cut] : 0;
+    const double cs = cut >= 0 ? sc[cut] : 0.0;
     int tk[kSelPer];
     loc = 0;
 #pragma unroll
@@ -277,10 +352,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         int t = 0;
         if (c < C) {
             if (cut == -1) {
-                t = wt[c];
+                t = wv[u];
             } else if (cut >= 0) {
-                const uint64_t k = rkey[c];
-                if (k < ck || (k == ck && c < cut)) t = wt[c];
+                if (sv[u] > cs || (sv[u] == cs && c < cut)) t = wv[u];
                 else if (c == cut) t = rem;
             }
         }
@@ -288,7 +362,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         loc += t;
     }
     int ntake;
-    int run = block_excl_scan(loc, wsum, &ntake);
+    int run = block_excl_scan_nw<NW>(loc, ws_c, ntake);
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u) {
         const int c = kSelPer * tid + u;

@@ -189,6 +189,32 @@ def test_select_exact_ties_go_to_lower_id():
         assert np.array_equal(idx.cpu().numpy(), o_idx), ("q=0", B)
 
 
+def test_select_crowded_score_bucket():
+    """One cluster's score dwarfs the rest, so the others crowd into a few of
+    the equal-width score buckets and the cut is found by the exact passes
+    over the rank key; also near-equal scores (relative spread about 1e-6)."""
+    say("select: crowded score buckets (outlier cluster, near-equal scores)")
+    rng = np.random.default_rng(17)
+    H, G, C, Lp = 3, 4, 300, 6000
+    off, tok = _random_csr(rng, H, C, Lp, 16)
+    qb = synth.bf16_bits(rng.standard_normal((H * G, D)))
+    qd, qf = to_dev(qb, "bf16"), synth.bf16_to_f32(qb).astype(np.float64)
+    mu_out = rng.standard_normal((H, C, D)).astype(np.float32)
+    for h in range(H):
+        mu_out[h, 5 + h] *= 3e6 * (1 if h != 1 else -1)    # top outlier, or bottom for h = 1
+    base = rng.standard_normal((H, 1, D))
+    mu_near = (base * (1 + 1e-6 * rng.standard_normal((H, C, D)))).astype(np.float32)
+    for mu in (mu_out, mu_near):
+        for B in (40, 333, 1500):
+            idx, ns = ck.ckv_select(qd, torch.from_numpy(mu).to(DEV),
+                                    torch.from_numpy(off).to(DEV), torch.from_numpy(tok).to(DEV),
+                                    C, B)
+            torch.cuda.synchronize()
+            o_idx, o_ns, _ = oracle.select(qf, mu.astype(np.float64), off, tok, C, 16, B, G=G)
+            assert np.array_equal(ns.cpu().numpy(), o_ns), B
+            assert np.array_equal(idx.cpu().numpy(), o_idx), B
+
+
 # ------------------------------------------------------------- clustering --
 
 def test_cluster_fp32_single_head_per_iteration():
