@@ -126,8 +126,13 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
  *   B_eff = B - n_sink - n_pending tokens are taken; the last admitted
  *   cluster is cut to its first (lowest-position) tokens that still fit.
  * idx[g] = [0 .. n_sink) ++ [pending_begin .. pending_begin + n_pending)
- *          ++ admitted tokens (rank order, each cluster ascending),
- * then -1 up to B; n_sel[g] = number of valid entries.
+ *          ++ the admitted clusters' tokens, clusters in ascending id,
+ *          each cluster's tokens in CSR order (ascending position; the
+ *          cut cluster only its first ones),
+ * then -1 up to B; n_sel[g] = number of valid entries. The pages fix which
+ * tokens are taken, not the order attention sees them in; emitting by
+ * cluster id lets the device find the cut cluster by a weighted select
+ * instead of a full sort of the C scores.
  * Pending tokens are decode tokens not yet clustered; they are always
  * selected and count toward the budget, like the sinks.
  *
