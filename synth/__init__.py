@@ -33,6 +33,7 @@ reproducible on any host with the same numpy.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import functools
 from typing import Optional, Sequence
@@ -219,12 +220,13 @@ def make_kv(wl: Workload, L: Optional[int] = None, L_cap: Optional[int] = None,
     st = np.float32 if wl.dtype == "f32" else np.uint16
     K = np.zeros((len(hs), L_cap, wl.d), dtype=st)
     V = np.zeros((len(hs), L_cap, wl.d), dtype=st)
-    out = []
-    for j, h in enumerate(hs):
-        hd = make_head(wl, h, L)
+    # every head has its own random streams, so drawing them on several
+    # threads gives the same arrays as drawing them one after another
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(hs))) as ex:
+        out = list(ex.map(lambda h: make_head(wl, h, L), hs))
+    for j, hd in enumerate(out):
         K[j, :L] = hd.K
         V[j, :L] = hd.V
-        out.append(hd)
     return K, V, out
 
 
