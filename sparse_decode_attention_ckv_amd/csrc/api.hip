@@ -6,10 +6,29 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "ckv.h"
 #include "ckv_dev.h"
 
 using namespace ckv;
+
+namespace ckv {
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+}  // namespace ckv
 
 namespace {
 
@@ -147,6 +166,7 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
     size_t need;
     plan_cluster(desc, &p, &need, (char *)workspace);
     if (!workspace || workspace_bytes < need) return CKV_ERR_WORKSPACE;
+    p.n_cu = device_cu_count();
     hipStream_t s = (hipStream_t)stream;
 
     hipError_t e = launch_normalize_keys(p, K, assign, s);

@@ -145,11 +145,15 @@ __device__ inline int block_excl_scan(int v, int *wsum, int *total) {
     return before + x - v;
 }
 
+// Compute units of the current device (queried once per device, cached).
+int device_cu_count();
+
 // ---- launchers (defined in the .hip files) ------------------------------
 struct ClusterPlan {
     int H, C, Cpad, iters, n_sink, dtype, c_base, c_cap;
     int64_t L, Lp, k_head_stride, token_base, t_base, t_cap;
     int64_t ntiles;           // CSR tiles per head
+    int n_cu;                 // compute units of the device (persistent grids)
     // workspace carve-up (device pointers)
     void *kt;                 // unit keys [H][Lp][d] (bf16 or f32)
     void *mt;                 // unit centroids [H][Cpad][d] (bf16 or f32)

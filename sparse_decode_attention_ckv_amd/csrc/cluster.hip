@@ -158,143 +158,155 @@ hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cen
 // assign (bf16): scores = Kt . Mt^T on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation, fused with a per-token argmax (ties -> lower cluster id).
 //
-// Tokens sit on the MFMA N dimension, clusters on M. A workgroup of 8 waves
-// owns 512 tokens (64 per wave = four 16-token N tiles whose B fragments stay
-// in registers for the whole kernel). Unit centroids stream through LDS in
-// chunks of 64 (four 16-row M tiles), double-buffered, XOR-swizzled so the
-// 16 lanes reading one 16-byte column of 16 rows hit distinct banks.
+// Persistent workgroups of 16 waves (four per SIMD, so one wave's argmax
+// VALU work and LDS reads overlap the others' MFMAs), one workgroup per CU,
+// each walking a contiguous range of 1024-token tiles (head-major, so
+// consecutive tiles share a head). Tokens sit on the MFMA N dimension,
+// clusters on M. Each wave owns 64 tokens of a tile: four 16-token N tiles
+// whose B fragments stay in registers while the wave sweeps every cluster.
+// The head's unit centroids sit in LDS, up to 512 clusters at a time (a
+// round), XOR-swizzled so the 16 lanes reading one 16-byte column of 16 rows
+// hit distinct banks; with a single round they are loaded once per head and
+// the waves then run without barriers. A tile's B fragments are requested
+// only after the centroids are in LDS: each wave then starts its MFMAs as
+// soon as its own rows arrive, instead of all waves waiting at the LDS
+// barrier for every wave's rows.
 //
 // MFMA 16x16x32 fragment layout (wave64): lane l supplies row/column
 // (l & 15) and the 8 consecutive k values 8*(l >> 4) .. +7 of a 32-wide k
 // step, for A and B alike; the 16x16 fp32 result gives lane l column
 // (l & 15) and rows 4*(l >> 4) + i, i = 0..3.
-constexpr int kAsWaves = 8;
-constexpr int kAsTok = 64 * kAsWaves;   // tokens per workgroup
-constexpr int kAsChunk = 64;            // clusters per LDS chunk
+constexpr int kAsWaves = 16;
+constexpr int kAsThreads = 64 * kAsWaves;
+constexpr int kAsTok = 64 * kAsWaves;   // tokens per tile
+constexpr int kAsRound = 512;           // clusters resident in LDS at a time
 
-__global__ __launch_bounds__(512) void k_assign_bf16(
-    const uint16_t *__restrict__ kt, const uint16_t *__restrict__ mt, int64_t Lp, int C,
-    int Cpad, int32_t *__restrict__ assign, int64_t L, int n_sink, int tiles_per_head) {
-    __shared__ u32x4 sA[2][kAsChunk * 16];
-    const uint32_t lin = xcd_linear(blockIdx.x, gridDim.x);
-    const int h = (int)(lin / tiles_per_head);
-    const int64_t tile = lin % tiles_per_head;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int col = lane & 15, kq = lane >> 4;
-    const int64_t tok0 = tile * kAsTok + wave * 64;
-    const u32x4 *K4 = (const u32x4 *)(kt + (int64_t)h * Lp * kD);
-    const u32x4 *M4 = (const u32x4 *)(mt + (int64_t)h * Cpad * kD);
-
-    // B fragments: N tile t = tokens tok0 + 16t + col, k step s = channels
-    // 32s + 8kq .. +7 (16-byte chunk 4s + kq of the row).
-    bf16x8 bfr[4][4];
+// B fragments of the wave's 64 tokens from row tok0 (rows past the window
+// read the last row; their results are not stored).
+__device__ __forceinline__ void as_load_b(const u32x4 *K4, int64_t Lp, int64_t tok0, int col,
+                                          int kq, bf16x8 (&b)[4][4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int64_t row = tok0 + 16 * t + col;
+        const int64_t rr = row < Lp ? row : Lp - 1;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row < Lp) v = K4[row * 16 + 4 * s + kq];
-            bfr[t][s] = __builtin_bit_cast(bf16x8, v);
-        }
+        for (int s = 0; s < 4; ++s) b[t][s] = __builtin_bit_cast(bf16x8, K4[rr * 16 + 4 * s + kq]);
     }
+}
 
-    const int nch = Cpad / kAsChunk;
-    // stage chunk 0
+// One 16-cluster M tile (LDS rows 16m ..) against the wave's 64 tokens, then
+// the running argmax over the lane's rows c0 .. c0+3 in ascending order
+// (strict >, so the first maximum stays); MASK drops ids >= C.
+template <bool MASK>
+__device__ __forceinline__ void as_mtile(const u32x4 *sA, int m, int col, int kq,
+                                         const bf16x8 (&b)[4][4], int c0, int C,
+                                         float (&best)[4], int (&bid)[4]) {
+    bf16x8 afr[4];
+    const int r = 16 * m + col;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int e = tid + 512 * i, r = e >> 4, q = e & 15;
-        sA[0][r * 16 + (q ^ (r & 15))] = M4[(int64_t)r * 16 + q];
-    }
-    __syncthreads();
+    for (int s = 0; s < 4; ++s)
+        afr[s] = __builtin_bit_cast(bf16x8, sA[r * 16 + ((4 * s + kq) ^ col)]);
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], b[t][s], acc[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (acc[t][i] > best[t] && (!MASK || c0 + i < C)) {
+                best[t] = acc[t][i];
+                bid[t] = c0 + i;
+            }
+}
 
-    float best[4];
-    int bid[4];
+__global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
+    const uint16_t *__restrict__ kt, const uint16_t *__restrict__ mt, int64_t Lp, int C,
+    int Cpad, int32_t *__restrict__ assign, int64_t L, int n_sink, int tiles_per_head,
+    int n_tiles) {
+    __shared__ u32x4 sA[kAsRound * 16];
+    const uint32_t w = xcd_linear(blockIdx.x, gridDim.x);
+    const int t_begin = (int)((int64_t)w * n_tiles / gridDim.x);
+    const int t_end = (int)((int64_t)(w + 1) * n_tiles / gridDim.x);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
+    const int col = lane & 15, kq = lane >> 4;
+    const int crows = (C + 15) / 16 * 16;                 // rows that hold real clusters
+    const int nr = (crows + kAsRound - 1) / kAsRound;     // rounds per tile
+    int loaded = -1;                                      // head of the resident round
+    int h = t_begin / tiles_per_head;
+    int tile = t_begin - h * tiles_per_head;
+    for (int t = t_begin; t < t_end; ++t) {
+        const int64_t tok0 = (int64_t)tile * kAsTok + wave * 64;
+        const u32x4 *M4 = (const u32x4 *)(mt + (int64_t)h * Cpad * kD);
+        bf16x8 b[4][4];
+        float best[4];
+        int bid[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        best[t] = -INFINITY;
-        bid[t] = 0;
+        for (int u = 0; u < 4; ++u) {
+            best[u] = -INFINITY;
+            bid[u] = 0;
+        }
+        for (int r = 0; r < nr; ++r) {
+            const int rb = r * kAsRound;
+            const int rows = (crows - rb < kAsRound) ? crows - rb : kAsRound;
+            if (nr > 1 || loaded != h) {
+                __syncthreads();                          // the previous round is done
+                for (int e0 = 0; e0 < rows * 16; e0 += kAsThreads * 4) {
+                    u32x4 v[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = e0 + tid + kAsThreads * k;
+                        v[k] = M4[(int64_t)rb * 16 + (e < rows * 16 ? e : 0)];
+                    }
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = e0 + tid + kAsThreads * k;
+                        const int rr = e >> 4, q = e & 15;
+                        if (e < rows * 16) sA[rr * 16 + (q ^ (rr & 15))] = v[k];
+                    }
+                }
+                __syncthreads();
+                loaded = h;
+            }
+            // the tile's B fragments after the first fill: each wave then
+            // starts on its MFMAs as soon as its own rows arrive
+            if (r == 0) as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, tok0, col, kq, b);
+            const int nm = rows / 16;
+            const int cl = rb + 4 * kq;                   // lane's first row of tile 0
+            for (int m = 0; m + 1 < nm; ++m)
+                as_mtile<false>(sA, m, col, kq, b, cl + 16 * m, C, best, bid);
+            as_mtile<true>(sA, nm - 1, col, kq, b, cl + 16 * (nm - 1), C, best, bid);
+        }
+        // merge the four row groups (lanes l, l^16, l^32, l^48) of each token
+        int res[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float bb = best[u];
+            int id = bid[u];
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float ob = __shfl_xor(bb, off);
+                const int oid = __shfl_xor(id, off);
+                if (ob > bb || (ob == bb && oid < id)) {
+                    bb = ob;
+                    id = oid;
+                }
+            }
+            res[u] = id;
+        }
+        const int64_t tok = tok0 + lane;
+        const int v = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];
+        if (tok < Lp) assign[(int64_t)h * L + n_sink + tok] = v;
+        if (++tile == tiles_per_head) {
+            tile = 0;
+            ++h;
+        }
     }
-
-    for (int ch = 0; ch < nch; ++ch) {
-        const int buf = ch & 1;
-        const bool more = (ch + 1 < nch);
-        u32x4 pf[2];
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int e = tid + 512 * i, r = e >> 4, q = e & 15;
-                pf[i] = M4[((int64_t)(ch + 1) * kAsChunk + r) * 16 + q];
-            }
-        }
-        const int cbase = ch * kAsChunk;
-        const bool last = !more;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            bf16x8 afr[4];
-            const int r = 16 * m + col;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                afr[s] = __builtin_bit_cast(bf16x8, sA[buf][r * 16 + ((4 * s + kq) ^ col)]);
-            f32x4 acc[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], bfr[t][s], acc[t], 0, 0, 0);
-            const int c0 = cbase + 16 * m + 4 * kq;
-            if (!last) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (acc[t][i] > best[t]) {
-                            best[t] = acc[t][i];
-                            bid[t] = c0 + i;
-                        }
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (acc[t][i] > best[t] && c0 + i < C) {
-                            best[t] = acc[t][i];
-                            bid[t] = c0 + i;
-                        }
-            }
-        }
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int e = tid + 512 * i, r = e >> 4, q = e & 15;
-                sA[buf ^ 1][r * 16 + (q ^ (r & 15))] = pf[i];
-            }
-        }
-        __syncthreads();
-    }
-
-    // merge the four row groups (lanes l, l^16, l^32, l^48) of each token
-    int res[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        float b = best[t];
-        int id = bid[t];
-#pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-            const float ob = __shfl_xor(b, off);
-            const int oid = __shfl_xor(id, off);
-            if (ob > b || (ob == b && oid < id)) {
-                b = ob;
-                id = oid;
-            }
-        }
-        res[t] = id;
-    }
-    const int64_t tok = tok0 + lane;
-    const int v = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];
-    if (tok < Lp) assign[(int64_t)h * L + n_sink + tok] = v;
 }
 
 // assign (fp32): one thread per token, fp32 unit vectors, fp32 dot product
@@ -327,9 +339,11 @@ __global__ __launch_bounds__(256) void k_assign_f32(
 hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s) {
     if (p.dtype == 1) {
         const int tph = (int)((p.Lp + kAsTok - 1) / kAsTok);
-        hipLaunchKernelGGL(k_assign_bf16, dim3((unsigned)(tph * p.H)), dim3(512), 0, s,
+        const int n_tiles = tph * p.H;
+        const int grid = n_tiles < p.n_cu ? n_tiles : p.n_cu;
+        hipLaunchKernelGGL(k_assign_bf16, dim3((unsigned)grid), dim3(kAsThreads), 0, s,
                            (const uint16_t *)p.kt, (const uint16_t *)p.mt, p.Lp, p.C,
-                           p.Cpad, assign, p.L, p.n_sink, tph);
+                           p.Cpad, assign, p.L, p.n_sink, tph, n_tiles);
     } else {
         dim3 grid((unsigned)((p.Lp + 255) / 256), p.H);
         hipLaunchKernelGGL(k_assign_f32, grid, dim3(256), 0, s, (const float *)p.kt,
