@@ -51,34 +51,56 @@ __device__ void block_unit_row(float x, bool active, int j, void *out_row,
 }
 
 // --------------------------------------------------------------------------
-// normalize_keys: one thread per key row (the fp64 norm is a sequential
-// chain, so a row is not split across lanes). bf16 rows are 16 x 16 B.
-__global__ __launch_bounds__(256) void k_normalize_keys_bf16(
+// normalize_keys: the fp64 norm is a sequential chain, so one thread owns a
+// row; the rows of a 256-row block are moved through LDS so that global
+// loads and stores stay coalesced (consecutive lanes, consecutive 16-byte
+// chunks). LDS rows are padded to 272 B to spread a column over the banks.
+constexpr int kNkRows = 256;             // rows per workgroup (one per thread)
+constexpr int kNkStride = 17;            // LDS row stride in 16-byte chunks
+
+__global__ __launch_bounds__(kNkRows) void k_normalize_keys_bf16(
     const uint16_t *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
     uint16_t *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
-    const int h = blockIdx.y;
+    __shared__ u32x4 rows[kNkRows * kNkStride];
+    const int h = blockIdx.y, tid = threadIdx.x;
     if (blockIdx.x == 0)   // sink rows are labelled -1
-        for (int i = threadIdx.x; i < n_sink; i += 256) assign[(int64_t)h * L + i] = -1;
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= Lp) return;
-    const u32x4 *src = (const u32x4 *)(K + h * head_stride + (n_sink + r) * kD);
-    u32x4 w[16];
+        for (int i = tid; i < n_sink; i += kNkRows) assign[(int64_t)h * L + i] = -1;
+    const int64_t r0 = (int64_t)blockIdx.x * kNkRows;
+    const int nrow = (int)(Lp - r0 < kNkRows ? Lp - r0 : kNkRows);
+    const u32x4 *src = (const u32x4 *)(K + h * head_stride + (n_sink + r0) * kD);
+    u32x4 *dst = (u32x4 *)(kt + ((int64_t)h * Lp + r0) * kD);
+    // coalesced loads: chunk e = 16 row + q
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = src[i];
+    for (int k0 = 0; k0 < 16; k0 += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = tid + kNkRows * (k0 + k);
+            v[k] = src[(e >> 4) < nrow ? e : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = tid + kNkRows * (k0 + k);
+            rows[(e >> 4) * kNkStride + (e & 15)] = v[k];
+        }
+    }
+    __syncthreads();
+    // thread tid: the chain over its row (chunks in order), then the unit row
+    // back into LDS
+    u32x4 *row = rows + tid * kNkStride;
     double ss = 0.0;
-#pragma unroll
+#pragma unroll 2
     for (int i = 0; i < 16; ++i) {
         float f[8];
-        unpack8(w[i], f);
+        unpack8(row[i], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = __fma_rn((double)f[e], (double)f[e], ss);
     }
     const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
-    u32x4 *dst = (u32x4 *)(kt + ((int64_t)h * Lp + r) * kD);
-#pragma unroll
+#pragma unroll 4
     for (int i = 0; i < 16; ++i) {
         float f[8];
-        unpack8(w[i], f);
+        unpack8(row[i], f);
         uint32_t o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne((float)((double)f[e] * inv));
@@ -87,7 +109,13 @@ __global__ __launch_bounds__(256) void k_normalize_keys_bf16(
         v.y = o[2] | (o[3] << 16);
         v.z = o[4] | (o[5] << 16);
         v.w = o[6] | (o[7] << 16);
-        dst[i] = v;
+        row[i] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int e = tid + kNkRows * k;
+        if ((e >> 4) < nrow) dst[e] = rows[(e >> 4) * kNkStride + (e & 15)];
     }
 }
 
@@ -110,8 +138,9 @@ __global__ __launch_bounds__(256) void k_normalize_keys_f32(
 hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *assign,
                                  hipStream_t s) {
     dim3 grid((unsigned)((p.Lp + 255) / 256), p.H);
+    static_assert(kNkRows == 256, "one grid for both element types");
     if (p.dtype == 1)
-        hipLaunchKernelGGL(k_normalize_keys_bf16, grid, dim3(256), 0, s,
+        hipLaunchKernelGGL(k_normalize_keys_bf16, grid, dim3(kNkRows), 0, s,
                            (const uint16_t *)K, p.k_head_stride, p.n_sink, p.Lp,
                            (uint16_t *)p.kt, assign, p.L);
     else
