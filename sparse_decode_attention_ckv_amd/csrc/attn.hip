@@ -52,12 +52,14 @@ __global__ __launch_bounds__(256) void k_attn_partial(
     const T *__restrict__ q, const T *__restrict__ K, const T *__restrict__ V,
     int64_t kv_head_stride, int64_t kv_rows, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ n_sel, int B, double scale,
-    typename Acc<T>::type *__restrict__ part) {
+    typename Acc<T>::type *__restrict__ part, int H, int S) {
     typedef typename Acc<T>::type A;
     constexpr int PW = kD + 2;                    // partial record: m, l, acc[d]
     __shared__ A zs[G][kAttnRows];
     __shared__ A red[4][G][kD + 1];
-    const int s = blockIdx.x, h = blockIdx.y, S = gridDim.x;
+    int h, s;
+    xcd_head_unit(blockIdx.x, S, h, s);
+    if (h >= H) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = tid >> 4, q8 = tid & 15;
     const int r0 = s * kAttnRows;
@@ -203,10 +205,12 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kv_head_stride, int64_t kv_rows,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ n_sel, int B, double scale,
-    float *__restrict__ part) {
+    float *__restrict__ part, int H, int S) {
     constexpr int PW = kD + 2;
     __shared__ float zs[G][kAttnRows];
-    const int s = blockIdx.x, h = blockIdx.y, S = gridDim.x;
+    int h, s;
+    xcd_head_unit(blockIdx.x, S, h, s);
+    if (h >= H) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kq = lane >> 4;    // MFMA fragment coordinates
     const int r0 = s * kAttnRows;
@@ -289,10 +293,13 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(
 // split records are read in batches with every load of a batch in flight.
 template <typename A>
 __global__ __launch_bounds__(128) void k_attn_combine(const A *__restrict__ part, int S,
-                                                      float *__restrict__ o) {
+                                                      float *__restrict__ o, int H, int G) {
     constexpr int PW = kD + 2;
     constexpr int NB = 16;
-    const int hq = blockIdx.x, j = threadIdx.x;
+    int h, g;
+    xcd_head_unit(blockIdx.x, G, h, g);
+    if (h >= H) return;
+    const int hq = h * G + g, j = threadIdx.x;
     const A *p = part + (int64_t)hq * S * PW;
     // one pass: records in batches of NB, every load of a batch in flight
     // (addresses clamped, values masked); the running max rescales the sums
@@ -334,14 +341,14 @@ static void launch_g(const AttnPlan &p, const void *q, const void *K, const void
                      const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s) {
     typedef typename Acc<T>::type A;
     if (sizeof(T) == 2)
-        hipLaunchKernelGGL((k_attn_partial_bf16<G>), dim3(p.S, p.H), dim3(256), 0, s,
-                           (const uint16_t *)q, (const uint16_t *)K, (const uint16_t *)V,
+        hipLaunchKernelGGL((k_attn_partial_bf16<G>), dim3(xcd_head_grid(p.H, p.S)), dim3(256),
+                           0, s, (const uint16_t *)q, (const uint16_t *)K, (const uint16_t *)V,
                            p.kv_head_stride, p.kv_rows, idx, n_sel, p.B, p.scale,
-                           (float *)p.partials);
+                           (float *)p.partials, p.H, p.S);
     else
-        hipLaunchKernelGGL((k_attn_partial<T, G>), dim3(p.S, p.H), dim3(256), 0, s,
-                           (const T *)q, (const T *)K, (const T *)V, p.kv_head_stride,
-                           p.kv_rows, idx, n_sel, p.B, p.scale, (A *)p.partials);
+        hipLaunchKernelGGL((k_attn_partial<T, G>), dim3(xcd_head_grid(p.H, p.S)), dim3(256), 0,
+                           s, (const T *)q, (const T *)K, (const T *)V, p.kv_head_stride,
+                           p.kv_rows, idx, n_sel, p.B, p.scale, (A *)p.partials, p.H, p.S);
 }
 
 template <typename T>
@@ -368,11 +375,11 @@ hipError_t launch_attn(const AttnPlan &p, const void *q, const void *K, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.dtype == 1)
-        hipLaunchKernelGGL(k_attn_combine<float>, dim3(p.H * p.G), dim3(128), 0, s,
-                           (const float *)p.partials, p.S, o);
+        hipLaunchKernelGGL(k_attn_combine<float>, dim3(xcd_head_grid(p.H, p.G)), dim3(128), 0,
+                           s, (const float *)p.partials, p.S, o, p.H, p.G);
     else
-        hipLaunchKernelGGL(k_attn_combine<double>, dim3(p.H * p.G), dim3(128), 0, s,
-                           (const double *)p.partials, p.S, o);
+        hipLaunchKernelGGL(k_attn_combine<double>, dim3(xcd_head_grid(p.H, p.G)), dim3(128), 0,
+                           s, (const double *)p.partials, p.S, o, p.H, p.G);
     return hipGetLastError();
 }
 

@@ -45,6 +45,21 @@ __device__ __forceinline__ uint32_t xcd_linear(uint32_t bid, uint32_t n) {
     return (bid & 7u) * (n >> 3) + (bid >> 3);
 }
 
+// Grids of per-head units placed by XCD: unit j (< n) of head h runs as block
+// b = (h / 8) * 8n + 8j + h % 8, so with blocks handed to the 8 XCDs round-
+// robin every unit of head h shares an XCD (and its L2) with block h of a
+// one-block-per-head grid (the selection that wrote the head's indices).
+// The grid has 8 ceil(H / 8) n blocks; blocks whose head is >= H have no
+// work and must return before any barrier.
+__host__ __device__ inline uint32_t xcd_head_grid(int H, int n) {
+    return (uint32_t)((H + 7) / 8) * 8u * (uint32_t)n;
+}
+__device__ __forceinline__ void xcd_head_unit(uint32_t b, int n, int &h, int &j) {
+    const uint32_t rest = b >> 3;
+    j = (int)(rest % (uint32_t)n);
+    h = (int)(rest / (uint32_t)n) * 8 + (int)(b & 7u);
+}
+
 // ---- wave- and block-wide scans (DPP, no LDS round trips inside a wave) --
 // DPP controls of the gfx9 family: row_shr:n shifts within a row of 16 lanes;
 // row_bcast:15 copies lane 15 of each row into the next row, row_bcast:31
