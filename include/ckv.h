@@ -155,6 +155,10 @@ typedef struct {
     int32_t dtype;          /* ckv_dtype of q */
 } ckv_select_desc;
 
+/* Bytes of workspace ckv_select needs: 0 for C <= 512 (one kernel keeps
+ * everything on chip); for more clusters the scores are computed by a wider
+ * kernel first and passed through H * C fp64 values of workspace (rounded up
+ * to 256 bytes). 0 also if desc is invalid. */
 size_t ckv_select_workspace(const ckv_select_desc *desc);
 
 int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroids,

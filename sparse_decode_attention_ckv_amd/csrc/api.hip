@@ -100,7 +100,9 @@ int check_select(const ckv_select_desc *d) {
 }
 
 // selection keeps everything in LDS: no workspace
-size_t select_bytes(const ckv_select_desc *) { return 0; }
+size_t select_bytes(const ckv_select_desc *d) {
+    return d->C > kSelOneKernelMaxC ? align_up((size_t)d->H * d->C * sizeof(double)) : 0;
+}
 
 int check_attn(const ckv_attn_desc *d) {
     if (!d) return CKV_ERR_INVALID_ARG;
@@ -205,6 +207,7 @@ int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroid
     p.t_cap = desc->t_cap;
     p.pending_begin = desc->pending_begin;
     p.n_pending = desc->n_pending;
+    p.scores = (double *)workspace;
     return launch_status(launch_select(p, q, centroids, csr_offsets, csr_tokens, idx, n_sel,
                                        (hipStream_t)stream));
 }

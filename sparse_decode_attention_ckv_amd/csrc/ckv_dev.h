@@ -188,9 +188,13 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
 hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
                          const int32_t *tokens, float *cent, hipStream_t s);
 
+// Up to this many clusters one workgroup per head scores and selects; above
+// it a wider scoring-only kernel writes the scores to the workspace first.
+constexpr int kSelOneKernelMaxC = 512;
 struct SelectPlan {
     int H, G, C, c_cap, n_sink, B, dtype;
     int64_t t_cap, pending_begin, n_pending;
+    double *scores;           // workspace [H][C] when C > kSelOneKernelMaxC
 };
 hipError_t launch_select(const SelectPlan &p, const void *q, const float *cent,
                          const int32_t *offsets, const int32_t *tokens, int32_t *idx,

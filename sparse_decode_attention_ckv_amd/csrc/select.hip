@@ -36,6 +36,7 @@ constexpr int kSelLanes = 4;                        // lanes per cluster while s
 constexpr int kSelPass = kSelThreads / kSelLanes;   // clusters per scoring pass
 constexpr int kSelInFlight = 4;                     // passes whose loads fly together
 constexpr int kSelPer = kMaxC / kSelThreads;        // clusters per thread later (4)
+constexpr int kSelChunk = 2 * kSelPass;             // clusters per scoring-only workgroup
 
 // Buckets of the score pass and of each exact pass (11-bit digits; the last
 // exact pass is the id itself, ids < kMaxC = 2^11).
@@ -52,12 +53,98 @@ __device__ __forceinline__ uint64_t rank_key(double s) {
     return ~u;
 }
 
+// q_g = sum of the G query rows of KV head h, fp64 in row order; thread
+// tid < kD handles channel tid (its loads first, the sum later).
 template <bool BF16>
+__device__ __forceinline__ void sel_q_load(const void *q, int G, int h, int tid, float (&qv)[8]) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        const int64_t qi = ((int64_t)h * G + (g < G ? g : G - 1)) * kD + tid;
+        qv[g] = BF16 ? bf16_to_f32(((const uint16_t *)q)[qi]) : ((const float *)q)[qi];
+    }
+}
+__device__ __forceinline__ double sel_q_sum(const float (&qv)[8], int G) {
+    double a = 0.0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+        if (g < G) a += (double)qv[g];
+    return a;
+}
+
+// Centroid chunks of the NP scoring passes from cluster p0: pass pi holds
+// cluster p0 + pi * kSelPass + slot (clamped to < c_hi), lane lam its
+// channels 4 (lam + 4i) .. +3.
+template <int NP>
+__device__ __forceinline__ void sel_load_cent(const float *ch, int p0, int c_hi, int lam, int slot,
+                                              u32x4 (&w)[NP][8]) {
+#pragma unroll
+    for (int pi = 0; pi < NP; ++pi) {
+        const int c = p0 + pi * kSelPass + slot;
+        const float *row = ch + (int64_t)(c < c_hi ? c : c_hi - 1) * kD;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[pi][i] = *(const u32x4 *)(row + 4 * (lam + 4 * i));
+    }
+}
+
+// s_c = q_g . mu_c for the clusters of those passes (c < c_hi), stored to
+// out[c]: 32 fma runs of 4 channels (lane lam holds runs lam + 4i), then the
+// pairwise tree r + r+16, +8, +4 inside the lane and +2, +1 across lanes.
+template <int NP>
+__device__ __forceinline__ void sel_score(const u32x4 (&w)[NP][8], const double *qg, int p0,
+                                          int c_hi, int lam, int slot, double *out) {
+#pragma unroll
+    for (int pi = 0; pi < NP; ++pi) {
+        const int c = p0 + pi * kSelPass + slot;
+        double run[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double *qr = qg + 4 * (lam + 4 * i);
+            double a = 0.0;
+            a = __fma_rn(qr[0], (double)__uint_as_float(w[pi][i].x), a);
+            a = __fma_rn(qr[1], (double)__uint_as_float(w[pi][i].y), a);
+            a = __fma_rn(qr[2], (double)__uint_as_float(w[pi][i].z), a);
+            a = __fma_rn(qr[3], (double)__uint_as_float(w[pi][i].w), a);
+            run[i] = a;
+        }
+        const double t0 = run[0] + run[4], t1 = run[1] + run[5];
+        const double t2 = run[2] + run[6], t3 = run[3] + run[7];
+        double v = (t0 + t2) + (t1 + t3);
+        v = v + __shfl_xor(v, 2);
+        v = v + __shfl_xor(v, 1);
+        if (lam == 0 && c < c_hi) out[c] = v;
+    }
+}
+
+// Scores only, for many clusters: workgroup (h, s) of a per-head XCD grid
+// scores clusters [s kSelChunk, (s + 1) kSelChunk) of KV head h into
+// scores[h][c] (fp64), every load of the workgroup in flight at once.
+template <bool BF16>
+__global__ __launch_bounds__(kSelThreads) void k_sel_score(
+    const void *__restrict__ q, int G, const float *__restrict__ cent, int C, int c_cap, int H,
+    int S, double *__restrict__ scores) {
+    __shared__ double qg[kD];
+    int h, s;
+    xcd_head_unit(blockIdx.x, S, h, s);
+    if (h >= H) return;
+    const int tid = threadIdx.x, lam = tid & (kSelLanes - 1), slot = tid >> 2;
+    const int p0 = s * kSelChunk, c_hi = (p0 + kSelChunk < C) ? p0 + kSelChunk : C;
+    u32x4 w[kSelChunk / kSelPass][8];
+    sel_load_cent<kSelChunk / kSelPass>(cent + (int64_t)h * c_cap * kD, p0, c_hi, lam, slot, w);
+    float qv[8];
+    if (tid < kD) sel_q_load<BF16>(q, G, h, tid, qv);
+    if (tid < kD) qg[tid] = sel_q_sum(qv, G);
+    __syncthreads();
+    sel_score<kSelChunk / kSelPass>(w, qg, p0, c_hi, lam, slot, scores + (int64_t)h * C);
+}
+
+// PRE: the scores come from k_sel_score (scores[h][c]) instead of being
+// computed here.
+template <bool BF16, bool PRE>
 __global__ __launch_bounds__(kSelThreads) void k_select(
     const void *__restrict__ q, int G, const float *__restrict__ cent, int C, int c_cap,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ tokens, int64_t t_cap,
     int n_sink, int64_t pending_begin, int64_t n_pending, int B, int32_t *__restrict__ idx,
-    int32_t *__restrict__ n_sel) {
+    int32_t *__restrict__ n_sel, const double *__restrict__ scores) {
     constexpr int NW = kSelThreads / 64;
     __shared__ double qg[kD];
     __shared__ double sc[kMaxC];           // scores
@@ -73,21 +160,22 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int T = kSelThreads, tid = threadIdx.x;
     const int h = blockIdx.x;
 
-    // ---- loads: the first batch of centroid chunks, the offsets and q, all
-    // in flight together (the centroids do not wait for q) ------------------
+    // ---- loads: the first batch of centroid chunks (or the scores), the
+    // offsets and q, all in flight together (the centroids do not wait for q)
     const int lam = tid & (kSelLanes - 1), slot = tid >> 2;
     const float *ch = cent + (int64_t)h * c_cap * kD;
     u32x4 w[kSelInFlight][8];
-    auto load_batch = [&](int p0) {
+    constexpr int NS = kMaxC / kSelThreads;
+    double pv[NS];
+    if (PRE) {
 #pragma unroll
-        for (int pi = 0; pi < kSelInFlight; ++pi) {
-            const int c = p0 + pi * kSelPass + slot;
-            const float *row = ch + (int64_t)(c < C ? c : C - 1) * kD;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w[pi][i] = *(const u32x4 *)(row + 4 * (lam + 4 * i));
+        for (int k = 0; k < NS; ++k) {
+            const int c = tid + k * T;
+            pv[k] = scores[(int64_t)h * C + (c < C ? c : C - 1)];
         }
-    };
-    load_batch(0);
+    } else {
+        sel_load_cent<kSelInFlight>(ch, 0, C, lam, slot, w);
+    }
     const int32_t *offh = offsets + (int64_t)h * (c_cap + 1);
     {
         constexpr int NO = (kMaxC + kSelThreads) / kSelThreads;
@@ -98,53 +186,26 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
             v[k] = offh[c <= C ? c : C];
         }
         float qv[8];
-        if (tid < kD) {
-#pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                const int64_t qi = ((int64_t)h * G + (g < G ? g : G - 1)) * kD + tid;
-                qv[g] = BF16 ? bf16_to_f32(((const uint16_t *)q)[qi]) : ((const float *)q)[qi];
-            }
-        }
+        if (!PRE && tid < kD) sel_q_load<BF16>(q, G, h, tid, qv);
 #pragma unroll
         for (int k = 0; k < NO; ++k) {
             const int c = tid + k * T;
             if (c <= C) off[c] = (int)(v[k] < 0 ? 0 : (v[k] > t_cap ? t_cap : v[k]));
         }
-        if (tid < kD) {
-            double a = 0.0;               // fp64 sum of the group's rows, in row order
-#pragma unroll
-            for (int g = 0; g < 8; ++g)
-                if (g < G) a += (double)qv[g];
-            qg[tid] = a;
-        }
+        if (!PRE && tid < kD) qg[tid] = sel_q_sum(qv, G);
     }
-    __syncthreads();
-
-    // ---- 1. scores -> rank keys; sizes ------------------------------------
-    for (int p0 = 0; p0 < C; p0 += kSelPass * kSelInFlight) {
-        if (p0 > 0) load_batch(p0);
+    if (PRE) {
 #pragma unroll
-        for (int pi = 0; pi < kSelInFlight; ++pi) {
-            const int c = p0 + pi * kSelPass + slot;
-            double run[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const double *qr = qg + 4 * (lam + 4 * i);
-                double a = 0.0;
-                a = __fma_rn(qr[0], (double)__uint_as_float(w[pi][i].x), a);
-                a = __fma_rn(qr[1], (double)__uint_as_float(w[pi][i].y), a);
-                a = __fma_rn(qr[2], (double)__uint_as_float(w[pi][i].z), a);
-                a = __fma_rn(qr[3], (double)__uint_as_float(w[pi][i].w), a);
-                run[i] = a;
-            }
-            // levels r + r+16, r + r+8, r + r+4 (runs lam + 4i of this lane)
-            const double t0 = run[0] + run[4], t1 = run[1] + run[5];
-            const double t2 = run[2] + run[6], t3 = run[3] + run[7];
-            double v = (t0 + t2) + (t1 + t3);
-            // levels r + r+2 and r + r+1 across the four lanes
-            v = v + __shfl_xor(v, 2);
-            v = v + __shfl_xor(v, 1);
-            if (lam == 0 && c < C) sc[c] = v;
+        for (int k = 0; k < NS; ++k) {
+            const int c = tid + k * T;
+            if (c < C) sc[c] = pv[k];
+        }
+    } else {
+        __syncthreads();
+        // ---- 1. scores ----------------------------------------------------
+        for (int p0 = 0; p0 < C; p0 += kSelPass * kSelInFlight) {
+            if (p0 > 0) sel_load_cent<kSelInFlight>(ch, p0, C, lam, slot, w);
+            sel_score<kSelInFlight>(w, qg, p0, C, lam, slot, sc);
         }
     }
     // the first histogram starts cleared
@@ -417,14 +478,29 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 hipError_t launch_select(const SelectPlan &p, const void *q, const float *cent,
                          const int32_t *offsets, const int32_t *tokens, int32_t *idx,
                          int32_t *n_sel, hipStream_t s) {
-    if (p.dtype == 1)
-        hipLaunchKernelGGL(k_select<true>, dim3(p.H), dim3(kSelThreads), 0, s, q, p.G, cent,
-                           p.C, p.c_cap, offsets, tokens, p.t_cap, p.n_sink, p.pending_begin,
-                           p.n_pending, p.B, idx, n_sel);
-    else
-        hipLaunchKernelGGL(k_select<false>, dim3(p.H), dim3(kSelThreads), 0, s, q, p.G, cent,
-                           p.C, p.c_cap, offsets, tokens, p.t_cap, p.n_sink, p.pending_begin,
-                           p.n_pending, p.B, idx, n_sel);
+    const bool pre = p.C > kSelOneKernelMaxC;
+    if (pre) {
+        const int S = (p.C + kSelChunk - 1) / kSelChunk;
+        if (p.dtype == 1)
+            hipLaunchKernelGGL(k_sel_score<true>, dim3(xcd_head_grid(p.H, S)), dim3(kSelThreads),
+                               0, s, q, p.G, cent, p.C, p.c_cap, p.H, S, p.scores);
+        else
+            hipLaunchKernelGGL(k_sel_score<false>, dim3(xcd_head_grid(p.H, S)),
+                               dim3(kSelThreads), 0, s, q, p.G, cent, p.C, p.c_cap, p.H, S,
+                               p.scores);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+#define CKV_SEL(BF, PR)                                                                      \
+    hipLaunchKernelGGL((k_select<BF, PR>), dim3(p.H), dim3(kSelThreads), 0, s, q, p.G, cent,  \
+                       p.C, p.c_cap, offsets, tokens, p.t_cap, p.n_sink, p.pending_begin,    \
+                       p.n_pending, p.B, idx, n_sel, (const double *)p.scores)
+    if (p.dtype == 1) {
+        if (pre) CKV_SEL(true, true); else CKV_SEL(true, false);
+    } else {
+        if (pre) CKV_SEL(false, true); else CKV_SEL(false, false);
+    }
+#undef CKV_SEL
     return hipGetLastError();
 }
 

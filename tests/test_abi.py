@@ -146,6 +146,13 @@ def test_select_workspace_and_pointers():
         args = [FAKE] * 6
         args[k] = None
         assert lib.ckv_select(ct.byref(d), *args, None, 0, None) == ck.CKV_ERR_INVALID_ARG
+    # many clusters: a scoring-only kernel first, its fp64 scores in the workspace
+    d = _sel(C=1000, c_cap=1000, t_cap=5000)
+    need = lib.ckv_select_workspace(ct.byref(d))
+    assert need >= 2 * 1000 * 8 and need % 256 == 0
+    assert lib.ckv_select(ct.byref(d), *[FAKE] * 6, None, need, None) == ck.CKV_ERR_WORKSPACE
+    assert lib.ckv_select(ct.byref(d), *[FAKE] * 6, FAKE, need - 1, None) == ck.CKV_ERR_WORKSPACE
+    assert lib.ckv_select_workspace(ct.byref(_sel(C=512, c_cap=512, t_cap=5000))) == 0
 
 
 def _att(**kw):
