@@ -77,6 +77,18 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
+// Inclusive prefix maximum over the 64 lanes of a wave (all lanes active).
+__device__ __forceinline__ int wave_incl_max(int x) {
+    constexpr int lo = -2147483647 - 1;
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, kDppRowShr + 1, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, kDppRowShr + 2, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, kDppRowShr + 4, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, kDppRowShr + 8, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, kDppBcast15, 0xa, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, kDppBcast31, 0xc, 0xf, false));
+    return x;
+}
+
 // Sum over the wave, the same value in every lane.
 __device__ __forceinline__ int wave_sum(int x) {
     return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);

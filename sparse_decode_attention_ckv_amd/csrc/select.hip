@@ -37,6 +37,8 @@ constexpr int kSelPass = kSelThreads / kSelLanes;   // clusters per scoring pass
 constexpr int kSelInFlight = 4;                     // passes whose loads fly together
 constexpr int kSelPer = kMaxC / kSelThreads;        // clusters per thread later (4)
 constexpr int kSelChunk = 2 * kSelPass;             // clusters per scoring-only workgroup
+constexpr int kSelMarks = 2048;                     // token slots found by a max-scan
+constexpr int kSelSlots = kSelMarks / kSelThreads;  // ... per thread (4)
 
 // Buckets of the score pass and of each exact pass (11-bit digits; the last
 // exact pass is the id itself, ids < kMaxC = 2^11).
@@ -91,7 +93,8 @@ __device__ __forceinline__ void sel_load_cent(const float *ch, int p0, int c_hi,
 // pairwise tree r + r+16, +8, +4 inside the lane and +2, +1 across lanes.
 template <int NP>
 __device__ __forceinline__ void sel_score(const u32x4 (&w)[NP][8], const double *qg, int p0,
-                                          int c_hi, int lam, int slot, double *out) {
+                                          int c_hi, int lam, int slot, double *out,
+                                          double (&vals)[NP]) {
 #pragma unroll
     for (int pi = 0; pi < NP; ++pi) {
         const int c = p0 + pi * kSelPass + slot;
@@ -112,6 +115,7 @@ __device__ __forceinline__ void sel_score(const u32x4 (&w)[NP][8], const double 
         v = v + __shfl_xor(v, 2);
         v = v + __shfl_xor(v, 1);
         if (lam == 0 && c < c_hi) out[c] = v;
+        vals[pi] = v;
     }
 }
 
@@ -134,7 +138,8 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_score(
     if (tid < kD) sel_q_load<BF16>(q, G, h, tid, qv);
     if (tid < kD) qg[tid] = sel_q_sum(qv, G);
     __syncthreads();
-    sel_score<kSelChunk / kSelPass>(w, qg, p0, c_hi, lam, slot, scores + (int64_t)h * C);
+    double vals[kSelChunk / kSelPass];
+    sel_score<kSelChunk / kSelPass>(w, qg, p0, c_hi, lam, slot, scores + (int64_t)h * C, vals);
 }
 
 // PRE: the scores come from k_sel_score (scores[h][c]) instead of being
@@ -153,6 +158,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     __shared__ int inc[kMaxC];             // inclusive prefix of wt in id order;
                                            // before that, a bucket's last cluster
     __shared__ uint64_t hist[kRadixBuckets];
+    __shared__ int mark[kSelMarks];        // first token slot of each taken cluster
     __shared__ int ws_a[NW], ws_b[NW], ws_c[NW];
     __shared__ double s_mn[NW], s_mx[NW];
     __shared__ int s_bucket, s_rem, s_cnt, s_cut;
@@ -194,51 +200,40 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         }
         if (!PRE && tid < kD) qg[tid] = sel_q_sum(qv, G);
     }
+    // the total size and the score range, gathered while the scores are made
+    // (each cluster counted once) and reduced before the barrier that ends
+    // this phase
+    const double pinf = __longlong_as_double(0x7ff0000000000000ll);
+    int loc = 0;
+    double smin = pinf, smax = -pinf;
+    auto take = [&](int c, double v) {
+        const int n = off[c + 1] - off[c];
+        loc += n > 0 ? n : 0;
+        smin = fmin(smin, v);
+        smax = fmax(smax, v);
+    };
     if (PRE) {
+        __syncthreads();                   // off[] complete
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
             const int c = tid + k * T;
-            if (c < C) sc[c] = pv[k];
+            if (c < C) {
+                sc[c] = pv[k];
+                take(c, pv[k]);
+            }
         }
     } else {
         __syncthreads();
         // ---- 1. scores ----------------------------------------------------
         for (int p0 = 0; p0 < C; p0 += kSelPass * kSelInFlight) {
             if (p0 > 0) sel_load_cent<kSelInFlight>(ch, p0, C, lam, slot, w);
-            sel_score<kSelInFlight>(w, qg, p0, C, lam, slot, sc);
-        }
-    }
-    // the first histogram starts cleared
+            double vals[kSelInFlight];
+            sel_score<kSelInFlight>(w, qg, p0, C, lam, slot, sc, vals);
 #pragma unroll
-    for (int u = 0; u < kRadixBuckets / kSelThreads; ++u) hist[tid + u * kSelThreads] = 0;
-    if (tid == 0) {
-        s_kmin = ~0ull;
-        s_kmax = 0ull;
-    }
-    __syncthreads();
-
-    // ---- 2. the cut: first cluster (rank order) where the sizes reach B_eff
-    const int64_t beff64 = (int64_t)B - n_sink - n_pending;
-    const int beff = (int)(beff64 > 0 ? beff64 : 0);
-    const double pinf = __longlong_as_double(0x7ff0000000000000ll);
-    // this thread's clusters 4 tid .. 4 tid + 3: sizes, scores; the total size
-    // and the score range over the block
-    int wv[kSelPer];
-    double sv[kSelPer];
-    int loc = 0;
-    double smin = pinf, smax = -pinf;
-#pragma unroll
-    for (int u = 0; u < kSelPer; ++u) {
-        const int c = kSelPer * tid + u;
-        wv[u] = 0;
-        sv[u] = 0.0;
-        if (c < C) {
-            const int n = off[c + 1] - off[c];
-            wv[u] = n > 0 ? n : 0;
-            sv[u] = sc[c];
-            loc += wv[u];
-            smin = fmin(smin, sv[u]);
-            smax = fmax(smax, sv[u]);
+            for (int pi = 0; pi < kSelInFlight; ++pi) {
+                const int c = p0 + pi * kSelPass + slot;
+                if (lam == 0 && c < C) take(c, vals[pi]);
+            }
         }
     }
     loc = wave_sum(loc);
@@ -248,7 +243,34 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         s_mn[tid >> 6] = smin;
         s_mx[tid >> 6] = smax;
     }
+    // the first histogram and the slot marks start cleared
+#pragma unroll
+    for (int u = 0; u < kRadixBuckets / kSelThreads; ++u) hist[tid + u * kSelThreads] = 0;
+#pragma unroll
+    for (int u = 0; u < kSelSlots; ++u) mark[tid + u * kSelThreads] = -1;
+    if (tid == 0) {
+        s_kmin = ~0ull;
+        s_kmax = 0ull;
+    }
     __syncthreads();
+
+    // ---- 2. the cut: first cluster (rank order) where the sizes reach B_eff
+    const int64_t beff64 = (int64_t)B - n_sink - n_pending;
+    const int beff = (int)(beff64 > 0 ? beff64 : 0);
+    // this thread's clusters 4 tid .. 4 tid + 3: sizes, scores
+    int wv[kSelPer];
+    double sv[kSelPer];
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+        const int c = kSelPer * tid + u;
+        wv[u] = 0;
+        sv[u] = 0.0;
+        if (c < C) {
+            const int n = off[c + 1] - off[c];
+            wv[u] = n > 0 ? n : 0;
+            sv[u] = sc[c];
+        }
+    }
     int total = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -427,6 +449,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 #pragma unroll
     for (int u = 0; u < kSelPer; ++u) {
         const int c = kSelPer * tid + u;
+        if (tk[u] > 0 && run < kSelMarks) mark[run] = c;
         run += tk[u];
         if (c < C) {
             inc[c] = run;
@@ -438,38 +461,83 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int64_t head = (int64_t)n_sink + n_pending;
     const int32_t *tok = tokens + (int64_t)h * t_cap;
     int32_t *out = idx + (int64_t)h * B;
-    // output slots in batches: positions first (LDS only), then every token
-    // load of the batch in flight, then the stores
-    constexpr int NE = 8;
-    for (int e0 = tid; e0 < B; e0 += NE * T) {
-        int src[NE];
-        int32_t val[NE];
-#pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            const int64_t e = e0 + (int64_t)k * T;
-            src[k] = -1;
-            val[k] = -1;
-            if (e < n_sink) {
-                val[k] = (int32_t)e;
-            } else if (e < head) {
-                val[k] = (int32_t)(pending_begin + (e - n_sink));
-            } else if (e - head < ntake) {
-                const int p = (int)(e - head);
-                int lo = 0, hi = C - 1;        // first cluster whose inclusive prefix exceeds p
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (inc[mid] > p) hi = mid; else lo = mid + 1;
-                }
-                src[k] = off[lo] + (p - (inc[lo] - wt[lo]));
-            }
+    if (ntake <= kSelMarks) {              // uniform
+        // sinks, pending tokens and the unused tail
+        for (int64_t e = tid; e < B; e += T) {
+            if (e < n_sink) out[e] = (int32_t)e;
+            else if (e < head) out[e] = (int32_t)(pending_begin + (e - n_sink));
+            else if (e - head >= ntake) out[e] = -1;
         }
-        int32_t t[NE];
+        // token slots p = 4 tid .. 4 tid + 3: the cluster of slot p is the
+        // largest marked id at or before p (ids rise with the slots), found by
+        // a running max inside the thread, then an exclusive max-scan over
+        // the threads before it
+        int cm[kSelSlots];
+        int mx = -1;
 #pragma unroll
-        for (int k = 0; k < NE; ++k) t[k] = tok[src[k] >= 0 ? src[k] : 0];
+        for (int k = 0; k < kSelSlots; ++k) {
+            const int p = kSelSlots * tid + k;
+            const int v = p < ntake ? mark[p] : -1;
+            mx = v > mx ? v : mx;
+            cm[k] = mx;
+        }
+        const int lane = tid & 63, wave = tid >> 6;
+        const int incl = wave_incl_max(mx);
+        int prev = __shfl_up(incl, 1);
+        prev = lane == 0 ? -1 : prev;
+        if (lane == 63) ws_b[wave] = incl;
+        __syncthreads();
 #pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            const int64_t e = e0 + (int64_t)k * T;
-            if (e < B) out[e] = src[k] >= 0 ? t[k] : val[k];
+        for (int w = 0; w < NW; ++w)
+            if (w < wave) prev = ws_b[w] > prev ? ws_b[w] : prev;
+        int src[kSelSlots];
+#pragma unroll
+        for (int k = 0; k < kSelSlots; ++k) {
+            const int p = kSelSlots * tid + k;
+            const int c = cm[k] > prev ? cm[k] : prev;
+            src[k] = (p < ntake && c >= 0) ? off[c] + (p - (inc[c] - wt[c])) : -1;
+        }
+        int32_t t[kSelSlots];
+#pragma unroll
+        for (int k = 0; k < kSelSlots; ++k) t[k] = tok[src[k] >= 0 ? src[k] : 0];
+#pragma unroll
+        for (int k = 0; k < kSelSlots; ++k)
+            if (src[k] >= 0) out[head + kSelSlots * tid + k] = t[k];
+    } else {
+        // many taken tokens: output slots in batches, each token slot's
+        // cluster by binary search over the id-order prefix, then every token
+        // load of the batch in flight, then the stores
+        constexpr int NE = 8;
+        for (int e0 = tid; e0 < B; e0 += NE * T) {
+            int src[NE];
+            int32_t val[NE];
+#pragma unroll
+            for (int k = 0; k < NE; ++k) {
+                const int64_t e = e0 + (int64_t)k * T;
+                src[k] = -1;
+                val[k] = -1;
+                if (e < n_sink) {
+                    val[k] = (int32_t)e;
+                } else if (e < head) {
+                    val[k] = (int32_t)(pending_begin + (e - n_sink));
+                } else if (e - head < ntake) {
+                    const int p = (int)(e - head);
+                    int lo = 0, hi = C - 1;    // first cluster whose inclusive prefix exceeds p
+                    while (lo < hi) {
+                        const int mid = (lo + hi) >> 1;
+                        if (inc[mid] > p) hi = mid; else lo = mid + 1;
+                    }
+                    src[k] = off[lo] + (p - (inc[lo] - wt[lo]));
+                }
+            }
+            int32_t t[NE];
+#pragma unroll
+            for (int k = 0; k < NE; ++k) t[k] = tok[src[k] >= 0 ? src[k] : 0];
+#pragma unroll
+            for (int k = 0; k < NE; ++k) {
+                const int64_t e = e0 + (int64_t)k * T;
+                if (e < B) out[e] = src[k] >= 0 ? t[k] : val[k];
+            }
         }
     }
     if (tid == 0) n_sel[h] = (int32_t)(head + ntake);
