@@ -561,15 +561,15 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
 // into fp64 accumulators; slots are combined in a fixed order (lane
 // butterflies, then the four waves in order), so the sum is reproducible.
 // mean = sum / n in fp64, stored as fp32; an empty cluster keeps its
-// centroid. The unit centroid for the next assignment is written too.
+// centroid. The unit centroid for the next assignment is written too, by
+// the first wave alone (no barrier after the reduction).
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_update(
     const void *__restrict__ K, int64_t head_stride, int64_t L, int64_t token_base,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ tokens, int c_base,
     int c_cap, int64_t t_cap, float *__restrict__ cent, void *__restrict__ mt, int Cpad) {
     __shared__ double red[4][kD];
-    __shared__ float sx[kD];
-    __shared__ double sinv;
+    __shared__ __align__(16) float sx[kD];
     const int c = blockIdx.x, h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = tid >> 4, q = tid & 15;
@@ -639,17 +639,47 @@ __global__ __launch_bounds__(256) void k_update(
         for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
     }
     __syncthreads();
-    const bool act = tid < kD;
-    float mu = 0.f;
+    if (wave != 0) return;
+    // wave 0 finishes: lane l owns channels l and l + 64. mean = sum / n in
+    // fp64, stored as fp32 (an empty cluster keeps its centroid); then the
+    // unit row: |mu|^2 as one fp64 fma chain over j = 0..127 in order,
+    // r = 1/sqrt(|mu|^2), channel j -> fp32(mu_j * r) (then bf16 when BF16);
+    // a zero row stays zero
     float *cp = cent + ((int64_t)h * c_cap + c_base + c) * kD;
-    if (act) {
-        const double ssum = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-        mu = (n > 0) ? (float)(ssum / (double)n) : cp[tid];
-        cp[tid] = mu;
+    float mu[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int j = lane + 64 * k;
+        const double ssum = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+        mu[k] = (n > 0) ? (float)(ssum / (double)n) : cp[j];
+        cp[j] = mu[k];
     }
+    // the row through LDS (one wave: its LDS accesses stay in order), then
+    // every lane runs the chain on broadcast reads
+    sx[lane] = mu[0];
+    sx[lane + 64] = mu[1];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    double ss = 0.0;
+#pragma unroll 4
+    for (int j4 = 0; j4 < kD / 4; ++j4) {
+        const f32x4 x = *(const f32x4 *)(sx + 4 * j4);
+        ss = __fma_rn((double)x[0], (double)x[0], ss);
+        ss = __fma_rn((double)x[1], (double)x[1], ss);
+        ss = __fma_rn((double)x[2], (double)x[2], ss);
+        ss = __fma_rn((double)x[3], (double)x[3], ss);
+    }
+    const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
     const int64_t mrow = ((int64_t)h * Cpad + c) * kD;
-    void *out = BF16 ? (void *)((uint16_t *)mt + mrow) : (void *)((float *)mt + mrow);
-    block_unit_row<BF16>(mu, act, tid, out, sx, &sinv);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float y = (float)((double)mu[k] * inv);
+        if (BF16)
+            ((uint16_t *)mt)[mrow + lane + 64 * k] = (uint16_t)f32_to_bf16_rne(y);
+        else
+            ((float *)mt)[mrow + lane + 64 * k] = y;
+    }
 }
 
 hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
