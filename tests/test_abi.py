@@ -166,6 +166,7 @@ def _att(**kw):
     (dict(B=0), ck.CKV_ERR_INVALID_ARG), (dict(kv_rows=0), ck.CKV_ERR_INVALID_ARG),
     (dict(kv_head_stride=100), ck.CKV_ERR_INVALID_ARG), (dict(dtype=2), ck.CKV_ERR_INVALID_ARG),
     (dict(scale=float("nan")), ck.CKV_ERR_INVALID_ARG),
+    (dict(B=32769, kv_rows=40000, kv_head_stride=40000 * 128), ck.CKV_ERR_UNSUPPORTED),
 ])
 def test_attn_rejects_bad_descriptors(kw, status):
     d = _att(**kw)

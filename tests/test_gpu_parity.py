@@ -337,3 +337,39 @@ def test_select_attention_on_gpu_clusters_full_size():
         o2 = ck.ckv_sparse_attn(qd, Kd, Vd, idx2, ns)
         torch.cuda.synchronize()
         assert torch.equal(idx, idx2) and torch.equal(o, o2)
+
+
+# ------------------------------------------------------------ limits --
+
+@pytest.mark.parametrize("L,C,iters", [(6160, 2048, 2), (3016, 600, 3)])
+def test_cluster_many_clusters_per_iteration(L, C, iters):
+    """The largest C (2048: four 512-cluster rounds of centroids in LDS) and a
+    C just past one round (600), per-iteration parity."""
+    wl = synth.workload(1)
+    say(f"cluster parity bf16 at many clusters: L={L} C={C}")
+    Kd, _, Kf, _ = _kv(wl, L, heads=range(1))
+    lloyd_parity(Kd, Kf, 16, C, iters, oracle.MIRROR)
+
+
+def test_attention_largest_budget_and_strided_cache():
+    """B = 32768 (512 splits, the largest supported), ragged n_sel, on K and V
+    that are views into a longer cache (head stride > rows x d)."""
+    wl = synth.workload(1)
+    say("attention at B=32768 on strided K/V views")
+    H, G, L, Lcap, B = 2, 4, 33000, 33100, 32768
+    K, V, hs = synth.make_kv(wl, L=L, L_cap=Lcap, heads=range(H))
+    Kd, Vd = to_dev(K, "bf16")[:, :L], to_dev(V, "bf16")[:, :L]
+    assert Kd.stride(0) == Lcap * D and not Kd.is_contiguous()
+    Kf = np.stack([h.Kf for h in hs]).astype(np.float64)
+    Vf = np.stack([h.Vf for h in hs]).astype(np.float64)
+    rng = np.random.default_rng(9)
+    qb = synth.bf16_bits(rng.standard_normal((H * G, D)) * 3)
+    qd, qf = to_dev(qb, "bf16"), synth.bf16_to_f32(qb).astype(np.float64)
+    n_sel = np.array([B, B - 77], np.int32)
+    idx = _random_idx(rng, H, B, L, 16, n_sel)
+    o = ck.ckv_sparse_attn(qd, Kd, Vd, torch.from_numpy(idx).to(DEV),
+                           torch.from_numpy(n_sel).to(DEV))
+    torch.cuda.synchronize()
+    err = rel_err(host_f64(o), oracle.attn(qf, Kf, Vf, idx, n_sel, G=G))
+    say(f"  rel err {err:.2e}")
+    assert err <= 2e-3
