@@ -7,14 +7,17 @@
 // (selection and indexing, Fig. 8: cluster sizes, prefix sums, where the
 // budget falls, trim of the last cluster, token indices).
 //
-// One kernel per decode step, one 512-thread workgroup per KV head, no
-// cross-workgroup handoff:
+// Up to 512 clusters: one kernel per decode step, one 512-thread workgroup
+// per KV head, no cross-workgroup handoff. Above 512 clusters the scores of
+// step 1 come from a wider scoring-only kernel (several workgroups per head)
+// through the workspace, and the same kernel then does steps 2 and 3.
 //  1. score every cluster, s_c = q_g . mu_c in fp64 with the fixed
 //     association of the definition (32 fma chains of 4 channels, pairwise
 //     tree r + r+16, +8, +4, +2, +1). Four lanes share a cluster: lane l holds
 //     the runs r = l (mod 4), so the first three tree levels stay inside the
 //     lane and only the last two cross lanes. Every centroid load of a batch
-//     is in flight at once.
+//     is in flight at once. The total size and the score range are gathered
+//     on the way.
 //  2. the clusters admitted "in descending score until the budget" are found
 //     without sorting, by a weighted select over the rank order (score
 //     descending, then id ascending): the cut is the cluster at which the
@@ -25,8 +28,11 @@
 //     Otherwise exact radix passes over the 75-bit rank key (64-bit score
 //     key, then the cluster id) of that bucket's clusters finish the job.
 //  3. every cluster ranked before the cut gives all its tokens, the cut
-//     cluster gives what still fits; tokens are emitted by cluster id
-//     (prefix sum in id order, one output slot per thread, binary search).
+//     cluster gives what still fits; tokens are emitted by cluster id: a
+//     prefix sum in id order gives each taken cluster its first output slot,
+//     marked in LDS, and a max-scan over the slots tells every slot its
+//     cluster (a binary search over the prefix when more than 2048 tokens
+//     are taken).
 #include "ckv_dev.h"
 
 namespace ckv {
