@@ -24,10 +24,10 @@
  *     error the call returns a non-zero ckv_status and has written nothing.
  *     A failure to launch returns CKV_ERR_LAUNCH. No C++ exception crosses
  *     this boundary.
- *   - Only head dimension d = 128 is supported (CKV_ERR_UNSUPPORTED
- *     otherwise). Element type: CKV_F32 or CKV_BF16 for keys, values and
- *     queries; centroids are always fp32, indices int32, the attention
- *     output fp32.
+ *   - Only head dimension d = 128 is supported, and at most 65535 heads per
+ *     call (CKV_ERR_UNSUPPORTED otherwise). Element type: CKV_F32 or
+ *     CKV_BF16 for keys, values and queries; centroids are always fp32,
+ *     indices int32, the attention output fp32.
  *   - Rows are row-major with d contiguous elements. "Head stride" is the
  *     number of ELEMENTS between row 0 of one head and row 0 of the next.
  *     K, V, q and centroid pointers must be 16-byte aligned and head strides

@@ -38,11 +38,15 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool dtype_ok(int32_t t) { return t == CKV_F32 || t == CKV_BF16; }
 
+// heads beyond this do not fit the second grid dimension of some launches
+constexpr int32_t kMaxHeads = 65535;
+
 // Returns CKV_OK or the reason the cluster descriptor is rejected.
 int check_cluster(const ckv_cluster_desc *d) {
     if (!d) return CKV_ERR_INVALID_ARG;
     if (d->H < 1 || !dtype_ok(d->dtype)) return CKV_ERR_INVALID_ARG;
     if (d->d != kD) return d->d < 1 ? CKV_ERR_INVALID_ARG : CKV_ERR_UNSUPPORTED;
+    if (d->H > kMaxHeads) return CKV_ERR_UNSUPPORTED;
     if (d->n_sink < 0 || d->L <= d->n_sink) return CKV_ERR_INVALID_ARG;
     const int64_t Lp = d->L - d->n_sink;
     if (d->C < 1 || d->C > Lp || d->iters < 1) return CKV_ERR_INVALID_ARG;
@@ -90,6 +94,7 @@ int check_select(const ckv_select_desc *d) {
     if (!d) return CKV_ERR_INVALID_ARG;
     if (d->H < 1 || d->G < 1 || d->G > 8 || !dtype_ok(d->dtype)) return CKV_ERR_INVALID_ARG;
     if (d->d != kD) return d->d < 1 ? CKV_ERR_INVALID_ARG : CKV_ERR_UNSUPPORTED;
+    if (d->H > kMaxHeads) return CKV_ERR_UNSUPPORTED;
     if (d->C < 1 || d->c_cap < d->C) return CKV_ERR_INVALID_ARG;
     if (d->C > kMaxC) return CKV_ERR_UNSUPPORTED;
     if (d->n_sink < 0 || d->n_pending < 0 || d->pending_begin < 0) return CKV_ERR_INVALID_ARG;
@@ -99,7 +104,8 @@ int check_select(const ckv_select_desc *d) {
     return CKV_OK;
 }
 
-// selection keeps everything in LDS: no workspace
+// up to kSelOneKernelMaxC clusters the selection keeps everything in LDS (no
+// workspace); above it the fp64 scores [H][C] pass through the workspace
 size_t select_bytes(const ckv_select_desc *d) {
     return d->C > kSelOneKernelMaxC ? align_up((size_t)d->H * d->C * sizeof(double)) : 0;
 }
@@ -109,6 +115,7 @@ int check_attn(const ckv_attn_desc *d) {
     if (d->H < 1 || d->G < 1 || d->G > 8 || !dtype_ok(d->dtype)) return CKV_ERR_INVALID_ARG;
     if (d->d != kD) return d->d < 1 ? CKV_ERR_INVALID_ARG : CKV_ERR_UNSUPPORTED;
     if (d->B < 1 || d->kv_rows < 1) return CKV_ERR_INVALID_ARG;
+    if (d->H > kMaxHeads) return CKV_ERR_UNSUPPORTED;
     if (d->B > kMaxSplits * kAttnSplitRows) return CKV_ERR_UNSUPPORTED;
     if (d->kv_head_stride < d->kv_rows * kD) return CKV_ERR_INVALID_ARG;
     if (!(d->scale == d->scale) || isinf(d->scale)) return CKV_ERR_INVALID_ARG;

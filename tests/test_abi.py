@@ -92,6 +92,7 @@ def _call_cluster(desc, ws_bytes=None, nullK=False):
     (dict(L=5000, k_head_stride=5000 * 128, C=2049, c_cap=2049, t_cap=4984),
      ck.CKV_ERR_UNSUPPORTED),
     (dict(iters=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(H=65536), ck.CKV_ERR_UNSUPPORTED),
     (dict(n_sink=-1), ck.CKV_ERR_INVALID_ARG),
     (dict(n_sink=1000), ck.CKV_ERR_INVALID_ARG),
     (dict(k_head_stride=1000 * 128 - 1), ck.CKV_ERR_INVALID_ARG),
@@ -130,6 +131,7 @@ def _sel(**kw):
     (dict(C=11), ck.CKV_ERR_INVALID_ARG), (dict(B=15), ck.CKV_ERR_INVALID_ARG),
     (dict(n_pending=60), ck.CKV_ERR_INVALID_ARG), (dict(pending_begin=-1), ck.CKV_ERR_INVALID_ARG),
     (dict(C=2049, c_cap=4096), ck.CKV_ERR_UNSUPPORTED), (dict(t_cap=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(H=65536), ck.CKV_ERR_UNSUPPORTED),
 ])
 def test_select_rejects_bad_descriptors(kw, status):
     d = _sel(**kw)
@@ -167,6 +169,7 @@ def _att(**kw):
     (dict(kv_head_stride=100), ck.CKV_ERR_INVALID_ARG), (dict(dtype=2), ck.CKV_ERR_INVALID_ARG),
     (dict(scale=float("nan")), ck.CKV_ERR_INVALID_ARG),
     (dict(B=32769, kv_rows=40000, kv_head_stride=40000 * 128), ck.CKV_ERR_UNSUPPORTED),
+    (dict(H=65536), ck.CKV_ERR_UNSUPPORTED),
 ])
 def test_attn_rejects_bad_descriptors(kw, status):
     d = _att(**kw)
