@@ -53,7 +53,13 @@ def log(msg):
 
 
 class Case:
-    """Device-resident inputs and preallocated outputs/workspaces."""
+    """Device-resident inputs and preallocated outputs/workspaces.
+
+    For the incremental workload the cache has room for the appended rows:
+    decode step s (counting from 1) writes row L + s - 1 of K and V, selects
+    with the rows not yet clustered as pending tokens, attends, and after
+    steps m, 2m, ... clusters the newest m rows into c_plus clusters that are
+    appended to the centroids and the CSR."""
 
     def __init__(self, wl, T, dev):
         import numpy as np
@@ -63,49 +69,87 @@ class Case:
         import synth
         self.wl, self.T = wl, T
         t0 = time.time()
-        K, V, _ = synth.make_kv(wl)
+        H, G, L, d, C, B = wl.H, wl.G, wl.L, wl.d, wl.C, wl.B
+        self.inc = wl.append_steps > 0
+        self.n_ev = T // wl.m_every if self.inc else 0
+        Lcap = L + T if self.inc else L
+        K, V, _ = synth.make_kv(wl, L=L, L_cap=Lcap)
         Q, _ = synth.make_query_steps(wl, T)
-        log(f"inputs drawn in {time.time() - t0:.1f}s")
 
         def bf(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
                 torch.bfloat16).to(dev)
         assert wl.dtype == "bf16"
-        self.K, self.V, self.Q = bf(K), bf(V), bf(Q)
-        H, G, L, d, C, B = wl.H, wl.G, wl.L, wl.d, wl.C, wl.B
+        # K and V as the two halves of one cache tensor (same strides), so an
+        # appended row of both is one copy
+        self.KV = bf(np.stack([K, V]))
+        self.K, self.V, self.Q = self.KV[0], self.KV[1], bf(Q)
+        if self.inc:
+            app = [synth.make_appended(wl, h, T) for h in range(H)]
+            self.KVa = bf(np.stack([np.stack([x[0] for x in app]), np.stack([x[1] for x in app])]))
+        log(f"inputs drawn in {time.time() - t0:.1f}s")
+        c_cap = C + (wl.c_plus * self.n_ev if self.inc else 0)
+        t_cap = (L - wl.n_sink) + (wl.m_every * self.n_ev if self.inc else 0)
         i32 = dict(dtype=torch.int32, device=dev)
-        self.cent = torch.empty((H, C, d), dtype=torch.float32, device=dev)
+        self.cent = torch.zeros((H, c_cap, d), dtype=torch.float32, device=dev)
         self.asg = torch.empty((H, L), **i32)
-        self.off = torch.empty((H, C + 1), **i32)
-        self.tok = torch.empty((H, L - wl.n_sink), **i32)
+        self.off = torch.zeros((H, c_cap + 1), **i32)
+        self.tok = torch.zeros((H, t_cap), **i32)
         self.idx = torch.empty((T, H, B), **i32)
         self.nsel = torch.empty((T, H), **i32)
         self.O = torch.empty((T, H * G, d), dtype=torch.float32, device=dev)
-        cd = ck.ClusterDesc(H=H, d=d, L=L, k_head_stride=L * d, token_base=0,
+        cd = ck.ClusterDesc(H=H, d=d, L=L, k_head_stride=Lcap * d, token_base=0,
                             n_sink=wl.n_sink, C=C, iters=wl.iters, dtype=ck.CKV_BF16,
-                            c_base=0, c_cap=C, t_base=0, t_cap=L - wl.n_sink)
-        sd = ck.SelectDesc(H=H, G=G, d=d, C=C, c_cap=C, n_sink=wl.n_sink,
-                           t_cap=L - wl.n_sink, pending_begin=0, n_pending=0, B=B,
+                            c_base=0, c_cap=c_cap, t_base=0, t_cap=t_cap)
+        sd = ck.SelectDesc(H=H, G=G, d=d, C=c_cap, c_cap=c_cap, n_sink=wl.n_sink,
+                           t_cap=t_cap, pending_begin=0, n_pending=0, B=B,
                            dtype=ck.CKV_BF16)
-        ad = ck.AttnDesc(H=H, G=G, d=d, B=B, kv_head_stride=L * d, kv_rows=L, scale=0.0,
-                         dtype=ck.CKV_BF16)
+        ad = ck.AttnDesc(H=H, G=G, d=d, B=B, kv_head_stride=Lcap * d, kv_rows=Lcap,
+                         scale=0.0, dtype=ck.CKV_BF16)
         u8 = dict(dtype=torch.uint8, device=dev)
         self.ws_c = torch.empty(ck.ckv_cluster_workspace(cd), **u8)
         self.ws_s = torch.empty(max(ck.ckv_select_workspace(sd), 1), **u8)
         self.ws_a = torch.empty(ck.ckv_attn_workspace(ad), **u8)
+        if self.inc:
+            m = wl.m_every
+            wd = ck.ClusterDesc(H=H, d=d, L=m, k_head_stride=Lcap * d, token_base=L,
+                                n_sink=0, C=wl.c_plus, iters=wl.iters, dtype=ck.CKV_BF16,
+                                c_base=C, c_cap=c_cap, t_base=L - wl.n_sink, t_cap=t_cap)
+            self.ws_w = torch.empty(ck.ckv_cluster_workspace(wd), **u8)
+            self.asg_w = torch.empty((H, m), **i32)
+        # per step (t = s - 1): clusters in use, first pending row, pending count
+        self.sched = []
+        for t in range(T):
+            ev = (t // wl.m_every) if self.inc else 0       # increments done before step t + 1
+            self.sched.append((C + wl.c_plus * ev if self.inc else C,
+                               L + wl.m_every * ev if self.inc else 0,
+                               (t + 1 - wl.m_every * ev) if self.inc else 0))
         self.ck = ck
 
     def cluster(self):
         wl = self.wl
-        self.ck.ckv_cluster(self.K, wl.n_sink, wl.C, wl.iters, centroids=self.cent,
+        self.ck.ckv_cluster(self.K[:, :wl.L], wl.n_sink, wl.C, wl.iters, centroids=self.cent,
                             assign=self.asg, csr_offsets=self.off, csr_tokens=self.tok,
                             workspace=self.ws_c)
 
+    def append(self, t):
+        self.KV[:, :, self.wl.L + t].copy_(self.KVa[:, :, t])
+
+    def increment(self, ev):
+        """Cluster rows L + m ev .. L + m (ev + 1) - 1 into c_plus clusters."""
+        wl = self.wl
+        m, base = wl.m_every, wl.L + wl.m_every * ev
+        self.ck.ckv_cluster(self.K[:, base:base + m], 0, wl.c_plus, wl.iters, token_base=base,
+                            centroids=self.cent, assign=self.asg_w, csr_offsets=self.off,
+                            csr_tokens=self.tok, c_base=wl.C + wl.c_plus * ev,
+                            t_base=base - wl.n_sink, workspace=self.ws_w)
+
     def select(self, t):
         wl = self.wl
-        self.ck.ckv_select(self.Q[t], self.cent, self.off, self.tok, wl.C, wl.B,
-                           n_sink=wl.n_sink, idx=self.idx[t], n_sel=self.nsel[t],
-                           workspace=self.ws_s)
+        C, pb, npend = self.sched[t]
+        self.ck.ckv_select(self.Q[t], self.cent, self.off, self.tok, C, wl.B,
+                           n_sink=wl.n_sink, pending_begin=pb, n_pending=npend,
+                           idx=self.idx[t], n_sel=self.nsel[t], workspace=self.ws_s)
 
     def attn(self, t):
         self.ck.ckv_sparse_attn(self.Q[t], self.K, self.V, self.idx[t], self.nsel[t],
@@ -113,8 +157,12 @@ class Case:
 
     def decode(self):
         for t in range(self.T):
+            if self.inc:
+                self.append(t)
             self.select(t)
             self.attn(t)
+            if self.inc and (t + 1) % self.wl.m_every == 0:
+                self.increment((t + 1) // self.wl.m_every - 1)
 
     def snapshot(self):
         return [x.clone() for x in (self.cent, self.asg, self.off, self.tok, self.idx,
@@ -305,6 +353,10 @@ def main():
     g_att = capture(lambda: [case.attn(0) for _ in range(args.reps)])
     sel_us = time_graph(g_sel) * 1e3 / args.reps
     att_us = time_graph(g_att) * 1e3 / args.reps
+    inc_ms = None
+    if case.inc:                          # one decode-time clustering event, back to back
+        g_inc = capture(lambda: [case.increment(0) for _ in range(16)])
+        inc_ms = time_graph(g_inc) / 16
     torch.cuda.synchronize()
     H, G, d, C, B = wl.H, wl.G, wl.d, wl.C, wl.B
     n_sel = case.nsel[0].cpu()
@@ -326,6 +378,9 @@ def main():
     }
     share = {"ckv_sparse_attn": att_us * T / 1e3, "ckv_select": sel_us * T / 1e3,
              "ckv_cluster": cl_ms}
+    if case.inc:
+        kernels["ckv_cluster_increment"] = {"ms_per_call": round(inc_ms, 4),
+                                            "calls_per_step": case.n_ev}
     dom = max(share, key=share.get)
     if dom == "ckv_cluster":
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(assign_flop / cl_ms / 1e9, 2),
@@ -336,7 +391,9 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = recorded_traffic(dom, wl.name)
-    log(f"per call: select {sel_us:.2f} us, attn {att_us:.2f} us; dominant {dom}")
+    log(f"per call: select {sel_us:.2f} us, attn {att_us:.2f} us"
+        + (f", decode-time clustering {inc_ms * 1e3:.1f} us per event" if case.inc else "")
+        + f"; dominant {dom}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -350,7 +407,9 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "kv_heads": H, "q_heads_per_kv": G, "d": d, "L": wl.L,
                    "n_sink": wl.n_sink, "C": C, "iters": wl.iters, "B": B,
-                   "decode_steps": T, "parallelism": "none (1 GPU)"},
+                   "decode_steps": T, "parallelism": "none (1 GPU)",
+                   **({"append_steps": T, "cluster_every": wl.m_every,
+                       "clusters_per_increment": wl.c_plus} if case.inc else {})},
         "cluster_ms_per_layer": round(cl_ms, 4),
         "decode_us_per_step": round(dec_us, 3),
         "roofline": roof,
