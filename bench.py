@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--reps", type=int, default=256,
                     help="back-to-back launches per live per-call timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode with ckv_select + ckv_sparse_attn instead of ckv_select_attn")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times and "
                          "exit: the kernel of known traffic that scales the HBM byte counters")
@@ -61,13 +63,13 @@ class Case:
     steps m, 2m, ... clusters the newest m rows into c_plus clusters that are
     appended to the centroids and the CSR."""
 
-    def __init__(self, wl, T, dev):
+    def __init__(self, wl, T, dev, fused=True):
         import numpy as np
         import torch
 
         import sparse_decode_attention_ckv_amd as ck
         import synth
-        self.wl, self.T = wl, T
+        self.wl, self.T, self.fused = wl, T, fused
         t0 = time.time()
         H, G, L, d, C, B = wl.H, wl.G, wl.L, wl.d, wl.C, wl.B
         self.inc = wl.append_steps > 0
@@ -110,6 +112,7 @@ class Case:
         self.ws_c = torch.empty(ck.ckv_cluster_workspace(cd), **u8)
         self.ws_s = torch.empty(max(ck.ckv_select_workspace(sd), 1), **u8)
         self.ws_a = torch.empty(ck.ckv_attn_workspace(ad), **u8)
+        self.ws_f = torch.empty(ck.ckv_select_attn_workspace(sd, ad), **u8)
         if self.inc:
             m = wl.m_every
             wd = ck.ClusterDesc(H=H, d=d, L=m, k_head_stride=Lcap * d, token_base=L,
@@ -155,12 +158,23 @@ class Case:
         self.ck.ckv_sparse_attn(self.Q[t], self.K, self.V, self.idx[t], self.nsel[t],
                                 out=self.O[t], workspace=self.ws_a)
 
+    def select_attn(self, t):
+        wl = self.wl
+        C, pb, npend = self.sched[t]
+        self.ck.ckv_select_attn(self.Q[t], self.cent, self.off, self.tok, C, wl.B, self.K, self.V,
+                                n_sink=wl.n_sink, pending_begin=pb, n_pending=npend,
+                                idx=self.idx[t], n_sel=self.nsel[t], out=self.O[t],
+                                workspace=self.ws_f)
+
     def decode(self):
         for t in range(self.T):
             if self.inc:
                 self.append(t)
-            self.select(t)
-            self.attn(t)
+            if self.fused:
+                self.select_attn(t)
+            else:
+                self.select(t)
+                self.attn(t)
             if self.inc and (t + 1) % self.wl.m_every == 0:
                 self.increment((t + 1) // self.wl.m_every - 1)
 
@@ -211,8 +225,10 @@ def copy_calibration(mib):
 # holds the hash of the kernel's sources at the time; once they change the
 # figure no longer applies and is reported as null.
 KERNEL_SOURCES = {
-    "ckv_select": ["select.hip", "ckv_dev.h"],
-    "ckv_sparse_attn": ["attn.hip", "ckv_dev.h"],
+    "ckv_select": ["select.hip", "sel_dev.h", "ckv_dev.h"],
+    "ckv_sparse_attn": ["attn.hip", "attn_dev.h", "ckv_dev.h"],
+    "ckv_select_attn": ["decode.hip", "select.hip", "sel_dev.h", "attn.hip", "attn_dev.h",
+                        "ckv_dev.h"],
     "ckv_cluster": ["cluster.hip", "ckv_dev.h"],
 }
 
@@ -300,7 +316,7 @@ def main():
     dev = "cuda:0"
     wl = synth.workload(args.workload)
     T = wl.steps if args.decode_steps is None else args.decode_steps
-    case = Case(wl, T, dev)
+    case = Case(wl, T, dev, fused=not args.separate)
 
     # eager reference run
     case.cluster()
@@ -351,8 +367,10 @@ def main():
     # live per-call timings (back-to-back launches of one call, HIP events)
     g_sel = capture(lambda: [case.select(0) for _ in range(args.reps)])
     g_att = capture(lambda: [case.attn(0) for _ in range(args.reps)])
+    g_fus = capture(lambda: [case.select_attn(0) for _ in range(args.reps)])
     sel_us = time_graph(g_sel) * 1e3 / args.reps
     att_us = time_graph(g_att) * 1e3 / args.reps
+    fus_us = time_graph(g_fus) * 1e3 / args.reps
     inc_ms = None
     if case.inc:                          # one decode-time clustering event, back to back
         g_inc = capture(lambda: [case.increment(0) for _ in range(16)])
@@ -364,6 +382,8 @@ def main():
     att_bytes = sum(2 * int(n) * d * e + 4 * B + G * d * e + G * d * 4 for n in n_sel)
     sel_bytes = sum(C * d * 4 + 4 * (C + 1) + 4 * (int(n) - wl.n_sink) + 4 * B + G * d * e
                     for n in n_sel)
+    # the fused step reads q once and never reads idx back
+    fus_bytes = sel_bytes + att_bytes - H * (G * d * e + 4 * B)
     Lp = wl.L - wl.n_sink
     assign_flop = 2.0 * Lp * C * d * H * wl.iters
     kernels = {
@@ -371,13 +391,21 @@ def main():
                             "GB/s": round(att_bytes / att_us / 1e3, 1),
                             "calls_per_step": T},
         "ckv_select": {"us_per_call": round(sel_us, 3), "bytes": sel_bytes,
-                       "GB/s": round(sel_bytes / sel_us / 1e3, 1), "calls_per_step": T},
+                       "GB/s": round(sel_bytes / sel_us / 1e3, 1),
+                       "calls_per_step": 0 if case.fused else T},
+        "ckv_select_attn": {"us_per_call": round(fus_us, 3), "bytes": fus_bytes,
+                            "GB/s": round(fus_bytes / fus_us / 1e3, 1),
+                            "calls_per_step": T if case.fused else 0},
         "ckv_cluster": {"ms_per_call": round(cl_ms, 4), "assign_flop": assign_flop,
                         "assign_TFLOP/s_over_whole_call": round(assign_flop / cl_ms / 1e9, 1),
                         "calls_per_step": 1},
     }
-    share = {"ckv_sparse_attn": att_us * T / 1e3, "ckv_select": sel_us * T / 1e3,
-             "ckv_cluster": cl_ms}
+    if case.fused:
+        kernels["ckv_sparse_attn"]["calls_per_step"] = 0
+        share = {"ckv_select_attn": fus_us * T / 1e3, "ckv_cluster": cl_ms}
+    else:
+        share = {"ckv_sparse_attn": att_us * T / 1e3, "ckv_select": sel_us * T / 1e3,
+                 "ckv_cluster": cl_ms}
     if case.inc:
         kernels["ckv_cluster_increment"] = {"ms_per_call": round(inc_ms, 4),
                                             "calls_per_step": case.n_ev}
@@ -391,7 +419,7 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = recorded_traffic(dom, wl.name)
-    log(f"per call: select {sel_us:.2f} us, attn {att_us:.2f} us"
+    log(f"per call: select {sel_us:.2f} us, attn {att_us:.2f} us, select_attn {fus_us:.2f} us"
         + (f", decode-time clustering {inc_ms * 1e3:.1f} us per event" if case.inc else "")
         + f"; dominant {dom}")
 
@@ -412,6 +440,7 @@ def main():
                        "clusters_per_increment": wl.c_plus} if case.inc else {})},
         "cluster_ms_per_layer": round(cl_ms, 4),
         "decode_us_per_step": round(dec_us, 3),
+        "decode_path": "ckv_select + ckv_sparse_attn" if args.separate else "ckv_select_attn",
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -132,7 +132,8 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
  * then -1 up to B; n_sel[g] = number of valid entries. The pages fix which
  * tokens are taken, not the order attention sees them in; emitting by
  * cluster id lets the device find the cut cluster by a weighted select
- * instead of a full sort of the C scores.
+ * instead of a full sort of the C scores, and lets every 64-slot window of
+ * the row be written independently.
  * Pending tokens are decode tokens not yet clustered; they are always
  * selected and count toward the budget, like the sinks.
  *
@@ -140,6 +141,9 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
  * int32 [H][c_cap+1] and csr_tokens int32 [H][t_cap] as written by
  * ckv_cluster. Offsets are clamped to [0, t_cap] on the device.
  * Outputs: idx int32 [H][B], n_sel int32 [H].
+ * Two launches: the scores (32 clusters per workgroup) go to the workspace,
+ * then one workgroup per 64 slots of each idx row finds the cut and writes
+ * its slots. B is at most 2^20 (CKV_ERR_UNSUPPORTED above).
  */
 typedef struct {
     int32_t H;              /* KV heads, >= 1 */
@@ -155,10 +159,8 @@ typedef struct {
     int32_t dtype;          /* ckv_dtype of q */
 } ckv_select_desc;
 
-/* Bytes of workspace ckv_select needs: 0 for C <= 512 (one kernel keeps
- * everything on chip); for more clusters the scores are computed by a wider
- * kernel first and passed through H * C fp64 values of workspace (rounded up
- * to 256 bytes). 0 also if desc is invalid. */
+/* Bytes of workspace ckv_select needs: H * C fp64 scores, rounded up to 256
+ * bytes (0 if desc is invalid). */
 size_t ckv_select_workspace(const ckv_select_desc *desc);
 
 int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroids,
@@ -196,6 +198,30 @@ size_t ckv_attn_workspace(const ckv_attn_desc *desc);
 int ckv_sparse_attn(const ckv_attn_desc *desc, const void *q, const void *K,
                     const void *V, const int32_t *idx, const int32_t *n_sel,
                     float *o, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* --------------------------------------------------------- select_attn --
+ * One decode step: ckv_select followed by ckv_sparse_attn on its output
+ * [Cluster-granular selection; Selection and indexing, Fig. 8; Long context
+ * & KV compression], with one launch and one round trip of idx through
+ * memory fewer: the workgroup that writes 64 slots of a head's idx row also
+ * runs the attention over those 64 rows. idx, n_sel and o are bitwise the
+ * values the two separate calls produce (same device code, same order).
+ * CKV_F32 runs the two separate calls' kernels.
+ *
+ * sdesc and adesc describe the same step: equal H, G, B and dtype
+ * (CKV_ERR_INVALID_ARG otherwise); each is also checked as by its own call.
+ * Inputs: those of ckv_select, plus K and V as in ckv_sparse_attn (q is read
+ * by both steps). Outputs: idx int32 [H][B], n_sel int32 [H], o fp32
+ * [H*G][d]. Workspace: ckv_select_attn_workspace() bytes (the selection's
+ * scores, then the attention's split partials).
+ */
+size_t ckv_select_attn_workspace(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc);
+
+int ckv_select_attn(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc, const void *q,
+                    const float *centroids, const int32_t *csr_offsets,
+                    const int32_t *csr_tokens, const void *K, const void *V, int32_t *idx,
+                    int32_t *n_sel, float *o, void *workspace, size_t workspace_bytes,
                     void *stream);
 
 #ifdef __cplusplus

@@ -25,7 +25,7 @@ __all__ = [
     "CKV_ERR_LAUNCH", "CKVError", "lib_path", "load", "ClusterDesc", "SelectDesc",
     "AttnDesc", "ckv_cluster", "ckv_select", "ckv_sparse_attn",
     "ckv_cluster_workspace", "ckv_select_workspace", "ckv_attn_workspace",
-    "ckv_status_string", "ckv_abi_version",
+    "ckv_status_string", "ckv_abi_version", "ckv_select_attn", "ckv_select_attn_workspace",
 ]
 
 CKV_OK, CKV_ERR_INVALID_ARG, CKV_ERR_UNSUPPORTED, CKV_ERR_WORKSPACE, CKV_ERR_LAUNCH = range(5)
@@ -73,6 +73,9 @@ _SIGS = {
     "ckv_select": (ct.c_int, [ct.POINTER(SelectDesc), _P, _P, _P, _P, _P, _P, _P, ct.c_size_t, _P]),
     "ckv_attn_workspace": (ct.c_size_t, [ct.POINTER(AttnDesc)]),
     "ckv_sparse_attn": (ct.c_int, [ct.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, ct.c_size_t, _P]),
+    "ckv_select_attn_workspace": (ct.c_size_t, [ct.POINTER(SelectDesc), ct.POINTER(AttnDesc)]),
+    "ckv_select_attn": (ct.c_int, [ct.POINTER(SelectDesc), ct.POINTER(AttnDesc), _P, _P, _P, _P,
+                                   _P, _P, _P, _P, _P, _P, ct.c_size_t, _P]),
 }
 
 
@@ -161,6 +164,10 @@ def ckv_select_workspace(desc: SelectDesc) -> int:
 
 def ckv_attn_workspace(desc: AttnDesc) -> int:
     return load().ckv_attn_workspace(ct.byref(desc))
+
+
+def ckv_select_attn_workspace(sdesc: SelectDesc, adesc: AttnDesc) -> int:
+    return load().ckv_select_attn_workspace(ct.byref(sdesc), ct.byref(adesc))
 
 
 def ckv_cluster(K: torch.Tensor, n_sink: int, C: int, iters: int, *, token_base: int = 0,
@@ -279,3 +286,54 @@ def ckv_sparse_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torc
                                _ptr(n_sel), _ptr(out), _ptr(ws), nb, _stream(stream)),
            "ckv_sparse_attn")
     return out
+
+
+def ckv_select_attn(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch.Tensor,
+                    csr_tokens: torch.Tensor, C: int, B: int, K: torch.Tensor, V: torch.Tensor,
+                    *, n_sink: int = 16, pending_begin: int = 0, n_pending: int = 0,
+                    kv_rows: Optional[int] = None, scale: float = 0.0,
+                    idx: Optional[torch.Tensor] = None, n_sel: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None):
+    """One decode step: ckv_select then ckv_sparse_attn on its output, fused.
+
+    Arguments as in those two calls. Returns (idx [H][B] int32, n_sel [H]
+    int32, o [H*G][d] fp32), bitwise what the separate calls return."""
+    lib = load()
+    H, c_cap, d = centroids.shape
+    hs = _rows(K, "K")
+    _need(V.shape == K.shape and V.stride() == K.stride() and V.dtype == K.dtype,
+          "V must match K in shape, strides and dtype")
+    _need(K.shape[0] == H and K.shape[2] == d, "K must be [H][rows][d] for the centroids' H, d")
+    _need(q.dim() == 2 and q.is_contiguous() and q.shape[1] == d and q.shape[0] % H == 0
+          and q.dtype == K.dtype, "q must be [H*G][d] contiguous, dtype of K")
+    _need(centroids.dtype == torch.float32 and centroids.is_contiguous(), "bad centroids")
+    _need(csr_offsets.dtype == torch.int32 and csr_offsets.is_contiguous()
+          and csr_offsets.shape == (H, c_cap + 1), "bad csr_offsets")
+    _need(csr_tokens.dtype == torch.int32 and csr_tokens.is_contiguous()
+          and csr_tokens.shape[0] == H, "bad csr_tokens")
+    G = q.shape[0] // H
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((H, B), dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty((H,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((H * G, d), dtype=torch.float32, device=dev)
+    _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.shape == (H, B), "bad idx")
+    _need(n_sel.dtype == torch.int32 and n_sel.numel() == H, "bad n_sel")
+    _need(out.dtype == torch.float32 and out.is_contiguous() and out.shape == (H * G, d),
+          "bad out")
+    sd = SelectDesc(H=H, G=G, d=d, C=C, c_cap=c_cap, n_sink=n_sink, t_cap=csr_tokens.shape[1],
+                    pending_begin=pending_begin, n_pending=n_pending, B=B,
+                    dtype=_dtype_code(q))
+    ad = AttnDesc(H=H, G=G, d=d, B=B, kv_head_stride=hs,
+                  kv_rows=K.shape[1] if kv_rows is None else kv_rows, scale=scale,
+                  dtype=_dtype_code(K))
+    nb = lib.ckv_select_attn_workspace(ct.byref(sd), ct.byref(ad))
+    ws = _workspace(nb, dev, workspace)
+    _check(lib.ckv_select_attn(ct.byref(sd), ct.byref(ad), _ptr(q), _ptr(centroids),
+                               _ptr(csr_offsets), _ptr(csr_tokens), _ptr(K), _ptr(V), _ptr(idx),
+                               _ptr(n_sel), _ptr(out), _ptr(ws), nb, _stream(stream)),
+           "ckv_select_attn")
+    return idx, n_sel, out

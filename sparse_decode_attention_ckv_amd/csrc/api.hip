@@ -100,14 +100,14 @@ int check_select(const ckv_select_desc *d) {
     if (d->n_sink < 0 || d->n_pending < 0 || d->pending_begin < 0) return CKV_ERR_INVALID_ARG;
     if (d->pending_begin + d->n_pending > INT32_MAX) return CKV_ERR_INVALID_ARG;
     if (d->B < 1 || (int64_t)d->B < d->n_sink + d->n_pending) return CKV_ERR_INVALID_ARG;
+    if (d->B > kMaxSelB) return CKV_ERR_UNSUPPORTED;
     if (d->t_cap < 1 || d->t_cap > INT32_MAX) return CKV_ERR_INVALID_ARG;
     return CKV_OK;
 }
 
-// up to kSelOneKernelMaxC clusters the selection keeps everything in LDS (no
-// workspace); above it the fp64 scores [H][C] pass through the workspace
+// the fp64 scores [H][C] pass from the scoring kernel to the cut kernel
 size_t select_bytes(const ckv_select_desc *d) {
-    return d->C > kSelOneKernelMaxC ? align_up((size_t)d->H * d->C * sizeof(double)) : 0;
+    return align_up((size_t)d->H * d->C * sizeof(double));
 }
 
 int check_attn(const ckv_attn_desc *d) {
@@ -132,6 +132,43 @@ size_t attn_bytes(const ckv_attn_desc *d) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? CKV_OK : CKV_ERR_LAUNCH; }
 
+void plan_select(const ckv_select_desc *d, SelectPlan *p, void *scores) {
+    p->H = d->H;
+    p->G = d->G;
+    p->C = d->C;
+    p->c_cap = d->c_cap;
+    p->n_sink = d->n_sink;
+    p->B = d->B;
+    p->dtype = d->dtype;
+    p->t_cap = d->t_cap;
+    p->pending_begin = d->pending_begin;
+    p->n_pending = d->n_pending;
+    p->scores = (double *)scores;
+}
+
+void plan_attn(const ckv_attn_desc *d, AttnPlan *p, void *partials) {
+    p->H = d->H;
+    p->G = d->G;
+    p->B = d->B;
+    p->dtype = d->dtype;
+    p->S = attn_splits(d);
+    p->kv_head_stride = d->kv_head_stride;
+    p->kv_rows = d->kv_rows;
+    p->scale = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)kD);
+    p->partials = partials;
+}
+
+// the two descriptors of one decode step describe the same problem
+int check_select_attn(const ckv_select_desc *s, const ckv_attn_desc *a) {
+    int st = check_select(s);
+    if (st != CKV_OK) return st;
+    st = check_attn(a);
+    if (st != CKV_OK) return st;
+    if (s->H != a->H || s->G != a->G || s->B != a->B || s->dtype != a->dtype)
+        return CKV_ERR_INVALID_ARG;
+    return CKV_OK;
+}
+
 // Kernels read rows with 16-byte vector loads.
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool stride_ok(int64_t elems, int32_t dtype) {
@@ -153,7 +190,7 @@ const char *ckv_status_string(int status) {
     }
 }
 
-int ckv_abi_version(void) { return 1; }
+int ckv_abi_version(void) { return 2; }
 
 size_t ckv_cluster_workspace(const ckv_cluster_desc *desc) {
     if (check_cluster(desc) != CKV_OK) return 0;
@@ -201,20 +238,9 @@ int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroid
     if (!q || !centroids || !csr_offsets || !csr_tokens || !idx || !n_sel)
         return CKV_ERR_INVALID_ARG;
     if (!aligned16(centroids)) return CKV_ERR_INVALID_ARG;
-    if (workspace_bytes < select_bytes(desc) || (select_bytes(desc) > 0 && !workspace))
-        return CKV_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < select_bytes(desc)) return CKV_ERR_WORKSPACE;
     SelectPlan p;
-    p.H = desc->H;
-    p.G = desc->G;
-    p.C = desc->C;
-    p.c_cap = desc->c_cap;
-    p.n_sink = desc->n_sink;
-    p.B = desc->B;
-    p.dtype = desc->dtype;
-    p.t_cap = desc->t_cap;
-    p.pending_begin = desc->pending_begin;
-    p.n_pending = desc->n_pending;
-    p.scores = (double *)workspace;
+    plan_select(desc, &p, workspace);
     return launch_status(launch_select(p, q, centroids, csr_offsets, csr_tokens, idx, n_sel,
                                        (hipStream_t)stream));
 }
@@ -235,16 +261,35 @@ int ckv_sparse_attn(const ckv_attn_desc *desc, const void *q, const void *K, con
         return CKV_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < attn_bytes(desc)) return CKV_ERR_WORKSPACE;
     AttnPlan p;
-    p.H = desc->H;
-    p.G = desc->G;
-    p.B = desc->B;
-    p.dtype = desc->dtype;
-    p.S = attn_splits(desc);
-    p.kv_head_stride = desc->kv_head_stride;
-    p.kv_rows = desc->kv_rows;
-    p.scale = desc->scale > 0.f ? (double)desc->scale : 1.0 / sqrt((double)kD);
-    p.partials = workspace;
+    plan_attn(desc, &p, workspace);
     return launch_status(launch_attn(p, q, K, V, idx, n_sel, o, (hipStream_t)stream));
+}
+
+size_t ckv_select_attn_workspace(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc) {
+    if (check_select_attn(sdesc, adesc) != CKV_OK) return 0;
+    return select_bytes(sdesc) + attn_bytes(adesc);
+}
+
+int ckv_select_attn(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc, const void *q,
+                    const float *centroids, const int32_t *csr_offsets,
+                    const int32_t *csr_tokens, const void *K, const void *V, int32_t *idx,
+                    int32_t *n_sel, float *o, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    const int st = check_select_attn(sdesc, adesc);
+    if (st != CKV_OK) return st;
+    if (!q || !centroids || !csr_offsets || !csr_tokens || !K || !V || !idx || !n_sel || !o)
+        return CKV_ERR_INVALID_ARG;
+    if (!aligned16(centroids) || !aligned16(q) || !aligned16(K) || !aligned16(V) ||
+        !stride_ok(adesc->kv_head_stride, adesc->dtype))
+        return CKV_ERR_INVALID_ARG;
+    const size_t sb = select_bytes(sdesc);
+    if (!workspace || workspace_bytes < sb + attn_bytes(adesc)) return CKV_ERR_WORKSPACE;
+    SelectPlan sp;
+    plan_select(sdesc, &sp, workspace);
+    AttnPlan ap;
+    plan_attn(adesc, &ap, (char *)workspace + sb);
+    return launch_status(launch_select_attn(sp, ap, q, centroids, csr_offsets, csr_tokens, K, V,
+                                            idx, n_sel, o, (hipStream_t)stream));
 }
 
 }  // extern "C"

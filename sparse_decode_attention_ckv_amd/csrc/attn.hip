@@ -18,11 +18,10 @@
 // A kernel boundary hands the partials over: on this multi-XCD part a
 // per-workgroup device-scope release fence costs more than a launch.
 // bf16 inputs compute in fp32; fp32 inputs compute in fp64.
-#include "ckv_dev.h"
+#include "attn_dev.h"
 
 namespace ckv {
 
-constexpr int kAttnRows = kAttnSplitRows;   // rows of idx per workgroup (split)
 constexpr int kRowsPerSlot = kAttnRows / 16;
 
 template <typename T> struct Acc;
@@ -191,102 +190,33 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 
 }
 
-// partial, bf16. Scores: one MFMA tile per wave, v_mfma_f32_16x16x32_bf16
-// with the query heads on M (rows 0..G-1 of the A tile, the rest zero) and
-// the wave's 16 rows of the split on N: lane l supplies, for k step t,
-// channels 32t + 8(l>>4) .. +7 of head (l & 15) (A) and of row
-// 16*wave + (l & 15) (B), and receives the scores of heads 4(l>>4) + i for
-// that row. Softmax and V: wave w takes the heads g = w, w+4; lane l owns
-// channels 2l, 2l+1 and row l of the split, so the max and the sum of p are
-// 64-lane wave reductions and the V sum runs over the rows with p_r taken
-// from lane r (readlane): no cross-lane reduction of the accumulators.
+// partial, bf16: the rows of split s come from idx (the V row of lane l is
+// split row l, the score row of lane l of wave w is split row 16w + (l & 15));
+// everything else is attn_rows_bf16.
 template <int G>
 __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kv_head_stride, int64_t kv_rows,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ n_sel, int B, double scale,
     float *__restrict__ part, int H, int S) {
-    constexpr int PW = kD + 2;
     __shared__ float zs[G][kAttnRows];
     int h, s;
     xcd_head_unit(blockIdx.x, S, h, s);
     if (h >= H) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, kq = lane >> 4;    // MFMA fragment coordinates
+    const int col = lane & 15;
     const int r0 = s * kAttnRows;
     const int32_t *ih = idx + (int64_t)h * B;
-
-    // idx of this lane's V row (row `lane` of the split) and of its score row
-    // (clamped; not waiting for n_sel)
+    // clamped reads, not waiting for n_sel
     const int rV = r0 + lane, rK = r0 + 16 * wave + col;
     const int tkV = ih[rV < B ? rV : B - 1];
     const int tkK = ih[rK < B ? rK : B - 1];
     int n = n_sel[h];
     n = n < 0 ? 0 : (n > B ? B : n);
     const bool okK = rK < n && tkK >= 0 && (int64_t)tkK < kv_rows;
-    const int rowK = okK ? tkK : 0;
     const bool okV = rV < n && tkV >= 0 && (int64_t)tkV < kv_rows;
-    const int rowV = okV ? tkV : 0;
-
-    // every K fragment, q fragment and V word of this thread in flight
-    const uint16_t *Kh = K + (int64_t)h * kv_head_stride;
-    const uint16_t *Vh = V + (int64_t)h * kv_head_stride;
-    const uint16_t *qrow = q + ((int64_t)h * G + (col < G ? col : 0)) * kD;
-    u32x4 kb[4], qa[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) kb[t] = *(const u32x4 *)(Kh + (int64_t)rowK * kD + 32 * t + 8 * kq);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) qa[t] = *(const u32x4 *)(qrow + 32 * t + 8 * kq);
-    uint32_t vv[kAttnRows];
-#pragma unroll
-    for (int r = 0; r < kAttnRows; ++r) {
-        const int row = __builtin_amdgcn_readlane(rowV, r);
-        vv[r] = *(const uint32_t *)(Vh + (int64_t)row * kD + 2 * lane);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const u32x4 a = col < G ? qa[t] : (u32x4){0u, 0u, 0u, 0u};
-        acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, kb[t]), acc4,
-                                                       0, 0, 0);
-    }
-    const float fscale = (float)scale;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int g = 4 * kq + i;
-        if (g < G) zs[g][16 * wave + col] = okK ? acc4[i] * fscale : -INFINITY;
-    }
-    __syncthreads();
-
-    for (int g = wave; g < G; g += 4) {
-        const float z = zs[g][lane];
-        float m = z;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float y = __shfl_xor(m, o);
-            m = y > m ? y : m;
-        }
-        const float p = (z > -INFINITY) ? __expf(z - m) : 0.f;
-        float l = p;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-        float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int r = 0; r < kAttnRows; ++r) {
-            const float pr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p), r));
-            a0 += pr * bf16_lo(vv[r]);
-            a1 += pr * bf16_hi(vv[r]);
-        }
-        float *dst = part + (((int64_t)h * G + g) * S + s) * PW;
-        if (lane == 0) {
-            dst[0] = m;
-            dst[1] = l;
-        }
-        *(float2 *)(dst + 2 + 2 * lane) = make_float2(a0, a1);
-    }
+    attn_rows_bf16<G>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK, okV ? tkV : 0,
+                      (float)scale, part, S, s, zs);
 }
 
 // combine: one workgroup per query head, thread j owns channel j; the
@@ -366,6 +296,16 @@ static void launch_t(const AttnPlan &p, const void *q, const void *K, const void
     }
 }
 
+hipError_t launch_attn_combine(const AttnPlan &p, float *o, hipStream_t s) {
+    if (p.dtype == 1)
+        hipLaunchKernelGGL(k_attn_combine<float>, dim3(xcd_head_grid(p.H, p.G)), dim3(128), 0,
+                           s, (const float *)p.partials, p.S, o, p.H, p.G);
+    else
+        hipLaunchKernelGGL(k_attn_combine<double>, dim3(xcd_head_grid(p.H, p.G)), dim3(128), 0,
+                           s, (const double *)p.partials, p.S, o, p.H, p.G);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnPlan &p, const void *q, const void *K, const void *V,
                        const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s) {
     if (p.dtype == 1)
@@ -374,13 +314,7 @@ hipError_t launch_attn(const AttnPlan &p, const void *q, const void *K, const vo
         launch_t<float>(p, q, K, V, idx, n_sel, o, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.dtype == 1)
-        hipLaunchKernelGGL(k_attn_combine<float>, dim3(xcd_head_grid(p.H, p.G)), dim3(128), 0,
-                           s, (const float *)p.partials, p.S, o, p.H, p.G);
-    else
-        hipLaunchKernelGGL(k_attn_combine<double>, dim3(xcd_head_grid(p.H, p.G)), dim3(128), 0,
-                           s, (const double *)p.partials, p.S, o, p.H, p.G);
-    return hipGetLastError();
+    return launch_attn_combine(p, o, s);
 }
 
 }  // namespace ckv

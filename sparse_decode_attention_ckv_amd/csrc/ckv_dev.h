@@ -200,14 +200,16 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
 hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
                          const int32_t *tokens, float *cent, hipStream_t s);
 
-// Up to this many clusters one workgroup per head scores and selects; above
-// it a wider scoring-only kernel writes the scores to the workspace first.
-constexpr int kSelOneKernelMaxC = 512;
+// Largest idx row (budget B) a selection call accepts: the cut kernel runs
+// one workgroup per 64 slots of every head.
+constexpr int kMaxSelB = 1 << 20;
 struct SelectPlan {
     int H, G, C, c_cap, n_sink, B, dtype;
     int64_t t_cap, pending_begin, n_pending;
-    double *scores;           // workspace [H][C] when C > kSelOneKernelMaxC
+    double *scores;           // workspace [H][C] fp64
 };
+hipError_t launch_sel_score(const SelectPlan &p, const void *q, const float *cent,
+                            hipStream_t s);
 hipError_t launch_select(const SelectPlan &p, const void *q, const float *cent,
                          const int32_t *offsets, const int32_t *tokens, int32_t *idx,
                          int32_t *n_sel, hipStream_t s);
@@ -220,5 +222,13 @@ struct AttnPlan {
 };
 hipError_t launch_attn(const AttnPlan &p, const void *q, const void *K, const void *V,
                        const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s);
+hipError_t launch_attn_combine(const AttnPlan &p, float *o, hipStream_t s);
+
+// One decode step, selection then attention (decode.hip); sp and ap describe
+// the same heads, query heads per KV head, budget and element type.
+hipError_t launch_select_attn(const SelectPlan &sp, const AttnPlan &ap, const void *q,
+                              const float *cent, const int32_t *offsets, const int32_t *tokens,
+                              const void *K, const void *V, int32_t *idx, int32_t *n_sel,
+                              float *o, hipStream_t s);
 
 }  // namespace ckv

@@ -63,7 +63,7 @@ def test_status_strings():
     for s in range(5):
         assert ck.ckv_status_string(s)
     assert ck.ckv_status_string(99) == "unknown status"
-    assert ck.ckv_abi_version() == 1
+    assert ck.ckv_abi_version() == 2
 
 
 def _cl(**kw):
@@ -143,18 +143,21 @@ def test_select_rejects_bad_descriptors(kw, status):
 def test_select_workspace_and_pointers():
     d = _sel()
     lib = ck.load()
-    assert lib.ckv_select_workspace(ct.byref(d)) == 0       # everything stays in LDS
+    need = lib.ckv_select_workspace(ct.byref(d))
+    assert need >= 2 * 10 * 8 and need % 256 == 0           # fp64 scores [H][C]
     for k in range(6):                                       # any missing pointer is rejected
         args = [FAKE] * 6
         args[k] = None
-        assert lib.ckv_select(ct.byref(d), *args, None, 0, None) == ck.CKV_ERR_INVALID_ARG
-    # many clusters: a scoring-only kernel first, its fp64 scores in the workspace
+        assert lib.ckv_select(ct.byref(d), *args, FAKE, need, None) == ck.CKV_ERR_INVALID_ARG
     d = _sel(C=1000, c_cap=1000, t_cap=5000)
     need = lib.ckv_select_workspace(ct.byref(d))
     assert need >= 2 * 1000 * 8 and need % 256 == 0
     assert lib.ckv_select(ct.byref(d), *[FAKE] * 6, None, need, None) == ck.CKV_ERR_WORKSPACE
     assert lib.ckv_select(ct.byref(d), *[FAKE] * 6, FAKE, need - 1, None) == ck.CKV_ERR_WORKSPACE
-    assert lib.ckv_select_workspace(ct.byref(_sel(C=512, c_cap=512, t_cap=5000))) == 0
+    # budgets beyond 2^20 slots per head are not supported
+    d = _sel(B=(1 << 20) + 1)
+    assert lib.ckv_select_workspace(ct.byref(d)) == 0
+    assert lib.ckv_select(ct.byref(d), *[FAKE] * 6, FAKE, 1 << 20, None) == ck.CKV_ERR_UNSUPPORTED
 
 
 def _att(**kw):
@@ -188,3 +191,27 @@ def test_attn_workspace_and_pointers():
                                None) == ck.CKV_ERR_WORKSPACE
     assert lib.ckv_sparse_attn(ct.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need,
                                None) == ck.CKV_ERR_INVALID_ARG
+
+
+def test_select_attn_checks():
+    lib = ck.load()
+    sd, ad = _sel(), _att()
+    need = lib.ckv_select_attn_workspace(ct.byref(sd), ct.byref(ad))
+    assert need == lib.ckv_select_workspace(ct.byref(sd)) + lib.ckv_attn_workspace(ct.byref(ad))
+    args = [FAKE] * 9
+    assert lib.ckv_select_attn(ct.byref(sd), ct.byref(ad), *args, FAKE, need - 1,
+                               None) == ck.CKV_ERR_WORKSPACE
+    for k in range(9):                                      # any missing pointer is rejected
+        a = list(args)
+        a[k] = None
+        assert lib.ckv_select_attn(ct.byref(sd), ct.byref(ad), *a, FAKE, need,
+                                   None) == ck.CKV_ERR_INVALID_ARG
+    # the two descriptors must describe the same step
+    for kw in (dict(H=3), dict(G=2), dict(B=128), dict(dtype=0)):
+        sd2 = _sel(**kw)
+        assert lib.ckv_select_attn_workspace(ct.byref(sd2), ct.byref(ad)) == 0
+        assert lib.ckv_select_attn(ct.byref(sd2), ct.byref(ad), *args, FAKE, need,
+                                   None) == ck.CKV_ERR_INVALID_ARG
+    # each descriptor is also checked on its own
+    assert lib.ckv_select_attn(ct.byref(_sel(d=64)), ct.byref(_att(d=64)), *args, FAKE, need,
+                               None) == ck.CKV_ERR_UNSUPPORTED

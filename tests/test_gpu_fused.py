@@ -1,0 +1,119 @@
+"""GPU parity of ckv_select_attn, the fused decode step: its idx, n_sel and o
+must be bitwise what ckv_select followed by ckv_sparse_attn produce on the
+same inputs, and match the oracle (selection bit-exact, attention within
+2e-3 for bf16 and 1e-5 for fp32 of the exact fp64 attention)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_decode_attention_ckv_amd as ck
+import synth
+from tests.gpu_helpers import DEV, gpu_cluster, host_f64, rel_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _random_csr(rng, H, C, Lp, n_sink):
+    off = np.zeros((H, C + 1), np.int32)
+    tok = np.zeros((H, Lp), np.int32)
+    for h in range(H):
+        a = rng.integers(0, C, size=n_sink + Lp).astype(np.int32)
+        a[:n_sink] = -1
+        off[h], tok[h] = oracle.csr(a, n_sink, C)
+    return off, tok
+
+
+@pytest.mark.parametrize("H,G,C,Lp,B,n_sink,n_pending,dtype", [
+    (8, 4, 409, 32752, 1024, 16, 0, "bf16"),     # llama8b 32k layer shape
+    (3, 4, 1638, 20000, 2048, 16, 0, "bf16"),    # 128k-layer cluster count
+    (2, 1, 57, 900, 200, 16, 0, "bf16"),         # G = 1, ragged last split
+    (2, 8, 130, 3000, 777, 0, 0, "bf16"),        # G = 8, no sinks
+    (4, 4, 421, 32752, 1024, 16, 64, "bf16"),    # pending decode tokens
+    (2, 4, 57, 900, 5000, 16, 0, "bf16"),        # B >= L: every row selected
+    (2, 4, 57, 900, 16, 16, 0, "bf16"),          # B = n_sink: sinks only
+    (9, 4, 64, 1000, 130, 16, 0, "bf16"),        # H not a multiple of 8
+    (2, 1, 25, 2032, 256, 16, 0, "f32"),         # fp32: the separate kernels
+])
+def test_fused_equals_separate_and_oracle(H, G, C, Lp, B, n_sink, n_pending, dtype):
+    say(f"fused decode step H={H} G={G} C={C} Lp={Lp} B={B} sink={n_sink} pend={n_pending} "
+        f"{dtype}")
+    rng = np.random.default_rng(C * 7 + B)
+    mu = (rng.standard_normal((H, C, D)) * 2).astype(np.float32)
+    mu[:, :, 7] *= 20
+    off, tok = _random_csr(rng, H, C, Lp, n_sink)
+    L = n_sink + Lp + n_pending
+    Ks = rng.standard_normal((H, L, D)) * 2
+    Vs = rng.standard_normal((H, L, D))
+    qs = rng.standard_normal((H * G, D)) * 3
+    if dtype == "bf16":
+        kb, vb, qb = synth.bf16_bits(Ks), synth.bf16_bits(Vs), synth.bf16_bits(qs)
+        Kd, Vd, qd = to_dev(kb, "bf16"), to_dev(vb, "bf16"), to_dev(qb, "bf16")
+        Kf, Vf, qf = (synth.bf16_to_f32(x).astype(np.float64) for x in (kb, vb, qb))
+        tol = 2e-3
+    else:
+        k32, v32, q32 = (x.astype(np.float32) for x in (Ks, Vs, qs))
+        Kd, Vd, qd = to_dev(k32, "f32"), to_dev(v32, "f32"), to_dev(q32, "f32")
+        Kf, Vf, qf = (x.astype(np.float64) for x in (k32, v32, q32))
+        tol = 1e-5
+    mud, offd, tokd = (torch.from_numpy(x).to(DEV) for x in (mu, off, tok))
+    pb = n_sink + Lp
+    idx, ns = ck.ckv_select(qd, mud, offd, tokd, C, B, n_sink=n_sink, pending_begin=pb,
+                            n_pending=n_pending)
+    o = ck.ckv_sparse_attn(qd, Kd, Vd, idx, ns)
+    fidx, fns, fo = ck.ckv_select_attn(qd, mud, offd, tokd, C, B, Kd, Vd, n_sink=n_sink,
+                                       pending_begin=pb, n_pending=n_pending)
+    torch.cuda.synchronize()
+    assert torch.equal(fidx, idx) and torch.equal(fns, ns)
+    assert torch.equal(fo, o)
+    o_idx, o_ns, _ = oracle.select(qf, mu.astype(np.float64), off, tok, C, n_sink, B, G=G,
+                                   pending_begin=pb, n_pending=n_pending)
+    assert np.array_equal(fidx.cpu().numpy(), o_idx)
+    assert np.array_equal(fns.cpu().numpy(), o_ns)
+    err = rel_err(host_f64(fo), oracle.attn(qf, Kf, Vf, o_idx, o_ns, G=G))
+    say(f"  rel err {err:.2e}")
+    assert err <= tol
+
+
+def test_fused_on_gpu_clusters_full_size_and_graph():
+    """The 32k layer: the fused step on the GPU's own clusters, eager and
+    replayed from a HIP graph (several replays, each checked), equal to the
+    separate calls."""
+    wl = synth.workload(1)
+    say("fused decode step on GPU clusters, 8 x 32768, C=409, B=1024, graph replays")
+    K, V, hs = synth.make_kv(wl, L=wl.L)
+    Kd, Vd = to_dev(K, "bf16"), to_dev(V, "bf16")
+    cent, asg, off, tok = gpu_cluster(Kd, 16, wl.C, wl.iters)
+    qs, _ = synth.make_queries(wl, 0)
+    qd = to_dev(qs, "bf16")
+    idx, ns = ck.ckv_select(qd, cent, off, tok, wl.C, wl.B)
+    o = ck.ckv_sparse_attn(qd, Kd, Vd, idx, ns)
+    torch.cuda.synchronize()
+    sd = ck.SelectDesc(H=wl.H, G=wl.G, d=D, C=wl.C, c_cap=wl.C, n_sink=16, t_cap=tok.shape[1],
+                       pending_begin=0, n_pending=0, B=wl.B, dtype=ck.CKV_BF16)
+    ad = ck.AttnDesc(H=wl.H, G=wl.G, d=D, B=wl.B, kv_head_stride=Kd.stride(0),
+                     kv_rows=Kd.shape[1], scale=0.0, dtype=ck.CKV_BF16)
+    ws = torch.empty(ck.ckv_select_attn_workspace(sd, ad), dtype=torch.uint8, device=DEV)
+    fidx = torch.empty_like(idx)
+    fns = torch.empty_like(ns)
+    fo = torch.empty_like(o)
+
+    def step():
+        ck.ckv_select_attn(qd, cent, off, tok, wl.C, wl.B, Kd, Vd, idx=fidx, n_sel=fns, out=fo,
+                           workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(fidx, idx) and torch.equal(fns, ns) and torch.equal(fo, o)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        fidx.fill_(-7)
+        fo.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(fidx, idx) and torch.equal(fns, ns) and torch.equal(fo, o), rep
