@@ -20,6 +20,8 @@
 //     slots of a head. Every workgroup of the head reads the same scores
 //     and offsets (a few KB) and finds the same cut on its own, so no
 //     workgroup waits for another; then it emits only its 64 slots.
+//     The sizes' total and the score range are reduced from the registers
+//     the loads land in, before the first barrier.
 //     The cut is the cluster at which the running size total, in rank order
 //     (score descending, then id ascending), first reaches the budget. It is
 //     found without sorting, by a weighted select: one histogram of the
@@ -77,6 +79,7 @@ template <int CMAX>
 struct SelLds {
     double sc[CMAX];                  // scores
     int off[CMAX + 1];                // clamped offsets
+    int w[CMAX];                      // sizes clamped to the budget
     int pre[CMAX];                    // a bucket's last cluster; later the
                                       // id-order exclusive prefix of taken tokens
     unsigned long long hist[CMAX];    // weight << kCntBits | count per bucket
@@ -136,29 +139,50 @@ __device__ __forceinline__ SelSlot sel_cut_emit(SelLds<CMAX> &S, const double *_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // ---- loads: scores and offsets of the head, all in flight at once
+    // (cluster c = tid + T k, coalesced); the weights (sizes clamped to the
+    // budget, which moves no cut), their total and the score range are
+    // reduced from these registers before the first barrier
+    const int64_t head = (int64_t)n_sink + n_pending;
+    const int64_t beff64 = (int64_t)B - head;
+    const int beff = (int)(beff64 > 0 ? beff64 : 0);
+    const double pinf = __longlong_as_double(0x7ff0000000000000ll);
+    double smin = pinf, smax = -pinf;
+    int loc = 0;
     {
         double v[PER];
-        int64_t o[PER + 1];
+        int64_t o0[PER], o1[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int c = tid + k * T;
             v[k] = scores[c < C ? c : C - 1];
+            o0[k] = offh[c < C ? c : C];
+            o1[k] = offh[c + 1 < C ? c + 1 : C];
         }
-#pragma unroll
-        for (int k = 0; k <= PER; ++k) {
-            const int c = tid + k * T;
-            o[k] = offh[c <= C ? c : C];
-        }
+        const int64_t oC = offh[C];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int c = tid + k * T;
-            if (c < C) S.sc[c] = v[k];
+            const int64_t a = o0[k] < 0 ? 0 : (o0[k] > t_cap ? t_cap : o0[k]);
+            const int64_t b = o1[k] < 0 ? 0 : (o1[k] > t_cap ? t_cap : o1[k]);
+            const int64_t n = b - a;
+            const int w = c < C ? (int)(n <= 0 ? 0 : (n < beff ? n : beff)) : 0;
+            loc += w;
+            smin = c < C ? fmin(smin, v[k]) : smin;
+            smax = c < C ? fmax(smax, v[k]) : smax;
+            if (c < C) {
+                S.sc[c] = v[k];
+                S.off[c] = (int)a;
+                S.w[c] = w;
+            }
         }
-#pragma unroll
-        for (int k = 0; k <= PER; ++k) {
-            const int c = tid + k * T;
-            if (c <= C) S.off[c] = (int)(o[k] < 0 ? 0 : (o[k] > t_cap ? t_cap : o[k]));
-        }
+        if (tid == 0) S.off[C] = (int)(oC < 0 ? 0 : (oC > t_cap ? t_cap : oC));
+    }
+    loc = wave_sum(loc);
+    wave_minmax_f64(smin, smax);
+    if (lane == 0) {
+        S.wsa[wave] = loc;
+        S.wmn[wave] = smin;
+        S.wmx[wave] = smax;
     }
     // the first histogram and the slot marks start cleared
 #pragma unroll
@@ -173,46 +197,21 @@ __device__ __forceinline__ SelSlot sel_cut_emit(SelLds<CMAX> &S, const double *_
         S.s_cnt = 0;
     }
     __syncthreads();
-
-    // ---- this thread's clusters PER tid .. PER tid + PER - 1: weights (sizes
-    // clamped to the budget, which moves no cut), scores, range, total
-    const int64_t head = (int64_t)n_sink + n_pending;
-    const int64_t beff64 = (int64_t)B - head;
-    const int beff = (int)(beff64 > 0 ? beff64 : 0);
-    const double pinf = __longlong_as_double(0x7ff0000000000000ll);
-    int wv[PER];
-    double sv[PER];
-    int loc = 0;
-    double smin = pinf, smax = -pinf;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int c = PER * tid + u;
-        wv[u] = 0;
-        sv[u] = 0.0;
-        if (c < C) {
-            int n = S.off[c + 1] - S.off[c];
-            n = n > 0 ? n : 0;
-            wv[u] = n < beff ? n : beff;
-            sv[u] = S.sc[c];
-            loc += wv[u];
-            smin = fmin(smin, sv[u]);
-            smax = fmax(smax, sv[u]);
-        }
-    }
-    loc = wave_sum(loc);
-    wave_minmax_f64(smin, smax);
-    if (lane == 0) {
-        S.wsa[wave] = loc;
-        S.wmn[wave] = smin;
-        S.wmx[wave] = smax;
-    }
-    __syncthreads();
     int total = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         total += S.wsa[w];
         smin = fmin(smin, S.wmn[w]);
         smax = fmax(smax, S.wmx[w]);
+    }
+    // this thread's clusters PER tid .. PER tid + PER - 1 (id order)
+    int wv[PER];
+    double sv[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int c = PER * tid + u;
+        wv[u] = c < C ? S.w[c] : 0;
+        sv[u] = c < C ? S.sc[c] : 0.0;
     }
 
     // ---- the cut: first cluster (rank order) where the weights reach beff
