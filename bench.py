@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="decode with ckv_select + ckv_sparse_attn instead of ckv_select_attn")
+    ap.add_argument("--async-cluster", type=int, default=None, metavar="D",
+                    help="incremental workload: run each decode-time clustering on a second "
+                         "stream, overlapping the next D decode steps, whose selection keeps "
+                         "the window's rows pending until the new clusters are in")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times and "
                          "exit: the kernel of known traffic that scales the HBM byte counters")
@@ -54,6 +58,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def decode_schedule(wl, T, lag=0):
+    """Per decode step t = s - 1 of T: (clusters in use, first pending row,
+    pending count). Increment k clusters rows L + m k .. L + m (k + 1) - 1,
+    which step m (k + 1) completes; its clusters are used from step
+    m (k + 1) + lag + 1 on. Until then the rows from the first not yet
+    clustered one up to the step's own row are pending."""
+    if wl.append_steps == 0:
+        assert lag == 0
+        return [(wl.C, 0, 0)] * T
+    m = wl.m_every
+    assert 0 <= lag < m, f"lag {lag} must be below the clustering period {m}"
+    assert wl.n_sink + m + lag <= wl.B, f"lag {lag}: n_sink + m + lag exceeds the budget"
+    sched = []
+    for t in range(T):
+        ev = (t - lag) // m if t >= lag else 0
+        sched.append((wl.C + wl.c_plus * ev, wl.L + m * ev, t + 1 - m * ev))
+    return sched
+
+
 class Case:
     """Device-resident inputs and preallocated outputs/workspaces.
 
@@ -61,9 +84,21 @@ class Case:
     decode step s (counting from 1) writes row L + s - 1 of K and V, selects
     with the rows not yet clustered as pending tokens, attends, and after
     steps m, 2m, ... clusters the newest m rows into c_plus clusters that are
-    appended to the centroids and the CSR."""
+    appended to the centroids and the CSR.
 
-    def __init__(self, wl, T, dev, fused=True):
+    With lag D > 0 the clusters of the rows completed by step m(k + 1) are
+    first used at step m(k + 1) + D + 1; until then those rows stay pending
+    (at most m + D pending rows, so n_sink + m + D <= B). With `side` set to a
+    stream, each increment runs there, forked after step m(k + 1) and joined
+    before step m(k + 1) + D + 1, overlapping the D decode steps between.
+    The two streams write disjoint memory: the increment writes centroid
+    slots, CSR offsets and token slots past those the decode steps read
+    (the one shared word, the offset that ends the last older cluster, is
+    rewritten with the value it holds), and reads K rows no step writes
+    after the fork. Without `side` the increment runs on the decode stream at
+    the fork point, which gives the same results in sequence."""
+
+    def __init__(self, wl, T, dev, fused=True, lag=0, side=None):
         import numpy as np
         import torch
 
@@ -120,14 +155,14 @@ class Case:
                                 c_base=C, c_cap=c_cap, t_base=L - wl.n_sink, t_cap=t_cap)
             self.ws_w = torch.empty(ck.ckv_cluster_workspace(wd), **u8)
             self.asg_w = torch.empty((H, m), **i32)
-        # per step (t = s - 1): clusters in use, first pending row, pending count
-        self.sched = []
-        for t in range(T):
-            ev = (t // wl.m_every) if self.inc else 0       # increments done before step t + 1
-            self.sched.append((C + wl.c_plus * ev if self.inc else C,
-                               L + wl.m_every * ev if self.inc else 0,
-                               (t + 1 - wl.m_every * ev) if self.inc else 0))
         self.ck = ck
+        self.set_lag(lag, side)
+
+    def set_lag(self, lag, side):
+        if lag or side is not None:
+            assert self.inc, "a clustering lag applies to the incremental workload only"
+        self.lag, self.side = lag, side
+        self.sched = decode_schedule(self.wl, self.T, lag)
 
     def cluster(self):
         wl = self.wl
@@ -166,8 +201,9 @@ class Case:
                                 idx=self.idx[t], n_sel=self.nsel[t], out=self.O[t],
                                 workspace=self.ws_f)
 
-    def decode(self):
-        for t in range(self.T):
+    def steps(self, a, b):
+        """Decode steps a .. b - 1 (0-based), without increments."""
+        for t in range(a, b):
             if self.inc:
                 self.append(t)
             if self.fused:
@@ -175,8 +211,85 @@ class Case:
             else:
                 self.select(t)
                 self.attn(t)
+
+    def decode(self):
+        import torch
+        main, join_t = torch.cuda.current_stream(), None
+        for t in range(self.T):
+            if t == join_t:
+                main.wait_stream(self.side)
+                join_t = None
+            self.steps(t, t + 1)
             if self.inc and (t + 1) % self.wl.m_every == 0:
-                self.increment((t + 1) // self.wl.m_every - 1)
+                k = (t + 1) // self.wl.m_every - 1
+                if self.side is None:
+                    self.increment(k)
+                else:
+                    self.side.wait_stream(main)
+                    with torch.cuda.stream(self.side):
+                        self.increment(k)
+                    join_t = t + 1 + self.lag
+        if join_t is not None:
+            main.wait_stream(self.side)
+
+    def split_graphs(self):
+        """The decode loop with side-stream increments as linear HIP graphs:
+        the decode steps cut at every fork and join point, one graph per
+        piece, and one graph per increment. Returns a function that replays
+        them on the current stream and forks each increment onto the side
+        stream, joining it through an event before the step that first uses
+        its clusters.
+
+        The fork is paced from the host: the steps after the fork point are
+        submitted first, then the host waits for the decode stream to reach
+        the fork point and only then submits the increment, whose wait is by
+        then satisfied. A side queue holding a wait that is not yet
+        satisfied slows every launch of the decode chain for as long as it
+        waits (measured: about 4.5 us per step), and so does a single graph
+        with the side branch inside."""
+        import torch
+        wl, T, D = self.wl, self.T, self.lag
+        m = wl.m_every
+        fork = {m * (k + 1): k for k in range(self.n_ev)}          # after step index b - 1
+        join = {m * (k + 1) + D: k for k in range(self.n_ev)}      # before step index a
+        cuts = sorted({0, T} | {c for c in list(fork) + list(join) if 0 < c < T})
+        pieces = [(a, b, capture(lambda a=a, b=b: self.steps(a, b)))
+                  for a, b in zip(cuts, cuts[1:])]
+        incs = [capture(lambda k=k: self.increment(k)) for k in range(self.n_ev)]
+        forked = [torch.cuda.Event() for _ in range(self.n_ev)]
+        done = [torch.cuda.Event() for _ in range(self.n_ev)]
+        side = self.side
+
+        def submit(k):
+            forked[k].synchronize()
+            side.wait_event(forked[k])
+            with torch.cuda.stream(side):
+                incs[k].replay()
+            done[k].record(side)
+
+        def replay():
+            main, due, open_ = torch.cuda.current_stream(), None, []
+            for a, b, g in pieces:
+                if a in join:
+                    k = join[a]
+                    if due == k:                    # no step between fork and join
+                        submit(k)
+                        due = None
+                    main.wait_event(done[k])
+                    open_.remove(k)
+                g.replay()
+                if due is not None:                 # the steps after the fork are queued
+                    submit(due)
+                    due = None
+                if b in fork:
+                    due = fork[b]
+                    forked[due].record(main)
+                    open_.append(due)
+            if due is not None:
+                submit(due)
+            for k in open_:
+                main.wait_event(done[k])
+        return replay
 
     def snapshot(self):
         return [x.clone() for x in (self.cent, self.asg, self.off, self.tok, self.idx,
@@ -316,7 +429,10 @@ def main():
     dev = "cuda:0"
     wl = synth.workload(args.workload)
     T = wl.steps if args.decode_steps is None else args.decode_steps
-    case = Case(wl, T, dev, fused=not args.separate)
+    lag, side = 0, None
+    if args.async_cluster is not None:
+        lag, side = args.async_cluster, torch.cuda.Stream(device=dev)
+    case = Case(wl, T, dev, fused=not args.separate, lag=lag, side=side)
 
     # eager reference run
     case.cluster()
@@ -324,12 +440,17 @@ def main():
     torch.cuda.synchronize()
     ref = case.snapshot()
 
-    # graphs: the clustering call and the whole decode loop
+    # graphs: the clustering call and the whole decode loop (with side-stream
+    # increments: linear graphs joined by events)
     g_cluster = capture(case.cluster)
-    g_decode = capture(case.decode)
+    if side is None:
+        g_decode = capture(case.decode)
+        decode_replay = g_decode.replay
+    else:
+        decode_replay = case.split_graphs()
     for rep in range(2):
         g_cluster.replay()
-        g_decode.replay()
+        decode_replay()
         torch.cuda.synchronize()
         for a, b in zip(ref, case.snapshot()):
             assert torch.equal(a, b), "graph replay differs from the eager run"
@@ -338,7 +459,7 @@ def main():
 
     def step():
         g_cluster.replay()
-        g_decode.replay()
+        decode_replay()
 
     for _ in range(args.warmup):
         step()
@@ -352,7 +473,7 @@ def main():
         ev[3 * k].record()
         g_cluster.replay()
         ev[3 * k + 1].record()
-        g_decode.replay()
+        decode_replay()
         ev[3 * k + 2].record()
     stop.record()
     torch.cuda.synchronize()
@@ -437,7 +558,9 @@ def main():
                    "n_sink": wl.n_sink, "C": C, "iters": wl.iters, "B": B,
                    "decode_steps": T, "parallelism": "none (1 GPU)",
                    **({"append_steps": T, "cluster_every": wl.m_every,
-                       "clusters_per_increment": wl.c_plus} if case.inc else {})},
+                       "clusters_per_increment": wl.c_plus, "cluster_lag_steps": lag,
+                       "cluster_stream": "side" if side is not None else "decode"}
+                      if case.inc else {})},
         "cluster_ms_per_layer": round(cl_ms, 4),
         "decode_us_per_step": round(dec_us, 3),
         "decode_path": "ckv_select + ckv_sparse_attn" if args.separate else "ckv_select_attn",
