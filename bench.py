@@ -10,8 +10,10 @@ each captured once as a HIP graph and replayed; every replay's results are
 checked bitwise against an eager run before timing.
 
 Prints one JSON line. `value` is the decode-step latency (select + sparse
-attention, microseconds per step); the clustering time per layer and the
-whole-step time are reported beside it.
+attention, microseconds per step); the clustering time per layer (with its
+p50/p99 over warm replays), the whole-step time and the cold decode step
+(the MALL and L2 flushed by a 512 MiB stream before every step) are reported
+beside it.
 """
 from __future__ import annotations
 
@@ -41,6 +43,8 @@ def parse():
                     help="decode steps per step (default: the workload's)")
     ap.add_argument("--reps", type=int, default=256,
                     help="back-to-back launches per live per-call timing")
+    ap.add_argument("--cluster-reps", type=int, default=20,
+                    help="warm clustering replays timed one by one (mean, p50, p99)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="decode with ckv_select + ckv_sparse_attn instead of ckv_select_attn")
@@ -317,6 +321,12 @@ def time_graph(g, reps=1):
     return a.elapsed_time(b) / reps
 
 
+def pct(xs, p):
+    """p-th percentile of the sorted list xs (nearest rank)."""
+    k = max(0, min(len(xs) - 1, -(-len(xs) * p // 100) - 1))
+    return xs[k]
+
+
 def copy_calibration(mib):
     """Ten copies of `mib` MiB between two device buffers: each reads and
     writes exactly mib * 2^20 bytes, so the byte counters of its kernel give
@@ -371,41 +381,70 @@ def recorded_traffic(kernel, workload):
     return int(float(rec["bytes_per_launch"]))
 
 
-def cpu_baseline(case, sample_steps, cluster_heads):
-    """The oracle as it stands, single-threaded, on a bounded sample of the
-    same workload: `sample_steps` decode steps (all KV heads, selection on the
-    GPU's centroids/CSR) and one K-means iteration on `cluster_heads` heads."""
-    import numpy as np
-    import torch
+def cpu_baseline(case, sample_steps, cluster_heads, threads):
+    """The oracle as it stands on a bounded sample of the same workload:
+    `sample_steps` decode steps (all KV heads, selection on the GPU's
+    centroids/CSR) and one K-means iteration on `cluster_heads` heads, first
+    on one core, then as independent per-head instances on `threads` host
+    threads (the oracle itself stays single-threaded; its C calls release the
+    interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     wl = case.wl
+    G = wl.G
     mu = case.cent.double().cpu().numpy()
     off = case.off.cpu().numpy()
     tok = case.tok.cpu().numpy()
     Kf = case.K.double().cpu().numpy()
     Vf = case.V.double().cpu().numpy()
     Qf = case.Q[:sample_steps].double().cpu().numpy()
-    oracle.select(Qf[0], mu, off, tok, wl.C, wl.n_sink, wl.B, G=wl.G)   # load the library
-    t0 = time.perf_counter()
-    for t in range(sample_steps):
-        idx, ns, _ = oracle.select(Qf[t], mu, off, tok, wl.C, wl.n_sink, wl.B, G=wl.G)
-        oracle.attn(Qf[t], Kf, Vf, idx, ns, G=wl.G)
-    dec_s = (time.perf_counter() - t0) / sample_steps
-    t0 = time.perf_counter()
-    for h in range(cluster_heads):
+    oracle.select(Qf[0], mu, off, tok, wl.C, wl.n_sink, wl.B, G=G)   # load the library
+
+    def decode_head(h):
+        for t in range(sample_steps):
+            q = Qf[t, h * G:(h + 1) * G]
+            idx, ns, _ = oracle.select(q, mu[h:h + 1], off[h:h + 1], tok[h:h + 1], wl.C,
+                                       wl.n_sink, wl.B, G=G)
+            oracle.attn(q, Kf[h:h + 1], Vf[h:h + 1], idx, ns, G=G)
+
+    def iterate_head(h):
         mu0 = oracle.init_centroids(Kf[h], wl.n_sink, wl.C)
         a, _ = oracle.assign(Kf[h], wl.n_sink, mu0, mode=oracle.MIRROR)
         oracle.update(Kf[h], wl.n_sink, a, mu0, mode=oracle.MIRROR)
-    it_s = (time.perf_counter() - t0) / cluster_heads
+
+    def timed(fn, heads, n):
+        t0 = time.perf_counter()
+        if n == 1:
+            for h in heads:
+                fn(h)
+        else:
+            with ThreadPoolExecutor(max_workers=n) as ex:
+                list(ex.map(fn, heads))
+        return time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    for t in range(sample_steps):
+        idx, ns, _ = oracle.select(Qf[t], mu, off, tok, wl.C, wl.n_sink, wl.B, G=G)
+        oracle.attn(Qf[t], Kf, Vf, idx, ns, G=G)
+    dec_s = (time.perf_counter() - t0) / sample_steps
+    it_s = timed(iterate_head, range(cluster_heads), 1) / cluster_heads
+    n = max(1, min(threads, wl.H))
+    dec_n = timed(decode_head, range(wl.H), n) / sample_steps
+    it_n = timed(iterate_head, range(cluster_heads), n) * wl.H / cluster_heads
     return {
         "value": round(dec_s * 1e6, 1), "unit": "us/decode_step", "cores": 1,
         "kind": "oracle",
         "sample": (f"{sample_steps} decode steps (select + sparse attention, all {wl.H} KV "
                    f"heads) and 1 K-means iteration on {cluster_heads} of {wl.H} heads, "
-                   f"single-threaded C oracle (fp64)"),
+                   f"C oracle (fp64), single-threaded"),
         "cluster_ms_per_layer_extrapolated": round(it_s * wl.H * wl.iters * 1e3, 1),
+        "per_head_threads": {
+            "cores": n, "value": round(dec_n * 1e6, 1), "unit": "us/decode_step",
+            "cluster_ms_per_layer_extrapolated": round(it_n * wl.iters * 1e3, 1),
+            "sample": f"the same sample as independent per-head oracle calls on {n} threads"},
         "host_cpu": platform.processor() or platform.machine(),
+        "host_threads": os.cpu_count(),
     }
 
 
@@ -485,6 +524,28 @@ def main():
     log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): cluster {cl_ms:.3f} ms, "
         f"decode {dec_us:.2f} us/step")
 
+    # clustering latency distribution: warm replays, each between HIP events
+    cl_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.cluster_reps)]
+    for a, b in cl_ev:
+        a.record()
+        g_cluster.replay()
+        b.record()
+    torch.cuda.synchronize()
+    cl_reps = sorted(a.elapsed_time(b) for a, b in cl_ev)
+
+    # cold decode steps: a 512 MiB read-modify-write before every step evicts
+    # the MALL and the L2, as the other layers of a model would between two
+    # steps of one layer; cold step = (T(flush + step) - T(flush)) / n
+    flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+    n_cold = min(T, 64)
+    g_fs = capture(lambda: [(flush_buf.add_(1), case.steps(t, t + 1)) for t in range(n_cold)])
+    g_f = capture(lambda: [flush_buf.add_(1) for _ in range(n_cold)])
+    cold_us = (time_graph(g_fs, 3) - time_graph(g_f, 3)) * 1e3 / n_cold
+    del g_fs, g_f, flush_buf
+    log(f"cluster over {len(cl_reps)} warm replays: p50 {pct(cl_reps, 50):.3f} ms, "
+        f"p99 {pct(cl_reps, 99):.3f} ms; cold decode step {cold_us:.2f} us")
+
     # live per-call timings (back-to-back launches of one call, HIP events)
     g_sel = capture(lambda: [case.select(0) for _ in range(args.reps)])
     g_att = capture(lambda: [case.attn(0) for _ in range(args.reps)])
@@ -540,6 +601,11 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = recorded_traffic(dom, wl.name)
+    if dom == "ckv_select_attn" and not case.inc:
+        # the same call with the MALL and L2 flushed before it
+        cold_gbs = fus_bytes / cold_us / 1e3
+        roof["cold"] = {"us_per_call": round(cold_us, 3), "achieved": round(cold_gbs, 1),
+                        "frac": round(cold_gbs / HBM_PEAK_GBS, 4)}
     log(f"per call: select {sel_us:.2f} us, attn {att_us:.2f} us, select_attn {fus_us:.2f} us"
         + (f", decode-time clustering {inc_ms * 1e3:.1f} us per event" if case.inc else "")
         + f"; dominant {dom}")
@@ -547,7 +613,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(case, sample_steps=min(T, 128), cluster_heads=wl.H)
+        cpu = cpu_baseline(case, sample_steps=min(T, 128), cluster_heads=wl.H,
+                           threads=min(16, os.cpu_count() or 1))
 
     out = {
         "metric": METRIC, "value": round(dec_us, 3), "unit": "us/decode_step",
@@ -562,7 +629,11 @@ def main():
                        "cluster_stream": "side" if side is not None else "decode"}
                       if case.inc else {})},
         "cluster_ms_per_layer": round(cl_ms, 4),
+        "cluster_ms_warm_reps": {"n": len(cl_reps), "mean": round(sum(cl_reps) / len(cl_reps), 4),
+                                 "p50": round(pct(cl_reps, 50), 4),
+                                 "p99": round(pct(cl_reps, 99), 4)},
         "decode_us_per_step": round(dec_us, 3),
+        "decode_cold_us_per_step": round(cold_us, 3),
         "decode_path": "ckv_select + ckv_sparse_attn" if args.separate else "ckv_select_attn",
         "roofline": roof,
         "kernels": kernels,
