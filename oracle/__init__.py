@@ -23,6 +23,12 @@ import numpy as np
 EXACT = 0
 MIRROR = 1
 
+# assignment distances (the page keeps the cosine; the other two are its
+# ablation)
+COSINE = 0
+INNER_PRODUCT = 1
+L2 = 2
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ckv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libckv_oracle.so")
@@ -60,11 +66,14 @@ def _load():
         "orc_unit_rows": (None, [_i64, _int, _D, _int, _D]),
         "orc_init_centroids": (None, [_i64, _int, _D, _int, _int, _D]),
         "orc_assign": (None, [_i64, _int, _D, _int, _int, _D, _int, _I32, _D]),
+        "orc_assign_metric": (None, [_i64, _int, _D, _int, _int, _D, _int, _int, _I32, _D]),
         "orc_csr": (None, [_i64, _int, _int, _I32, _i64, _I32, _I32]),
         "orc_update": (None, [_i64, _int, _D, _int, _int, _I32, _D, _int, _D]),
         "orc_objective": (ct.c_double, [_i64, _int, _D, _int, _I32, _D]),
         "orc_cluster": (None, [_int, _int, _i64, _int, _D, _int, _int, _int, _i64,
                                _D, _I32, _I32, _I32, _D, _I64]),
+        "orc_cluster_metric": (None, [_int, _int, _int, _i64, _int, _D, _int, _int, _int,
+                                      _i64, _D, _I32, _I32, _I32, _D, _I64]),
         "orc_select": (_int, [_int, _int, _int, _D, _int, _int, _D, _I32, _I32,
                               _i64, _int, _i64, _i64, _int, _I32, _I32, _D]),
         "orc_attn": (None, [_int, _int, _int, _D, _D, _D, _i64, _I32, _I32, _int,
@@ -118,17 +127,24 @@ def init_centroids(K, n_sink, C):
     return mu
 
 
-def assign(K, n_sink, mu, mode=MIRROR):
-    """Cosine assignment step [ClusterKV, clustering in semantic space].
-    K: [L][d], mu: [C][d]. Returns (assign [L] int32, margin [L])."""
+def assign(K, n_sink, mu, mode=MIRROR, metric=COSINE):
+    """Assignment step [ClusterKV, clustering in semantic space]: cosine by
+    default; INNER_PRODUCT and L2 are the page's ablation. K: [L][d],
+    mu: [C][d]. Returns (assign [L] int32, margin [L]); the margin is the
+    gap between the best and second-best candidate (squared-distance gap
+    for L2)."""
     K, pk = _d(K)
     mu, pm = _d(mu)
     L, d = K.shape
     C = mu.shape[0]
     a = np.empty(L, dtype=np.int32)
     m = np.empty(L)
-    _load().orc_assign(L, d, pk, n_sink, C, pm, mode, a.ctypes.data_as(_I32),
-                       m.ctypes.data_as(_D))
+    if metric == COSINE:
+        _load().orc_assign(L, d, pk, n_sink, C, pm, mode, a.ctypes.data_as(_I32),
+                           m.ctypes.data_as(_D))
+    else:
+        _load().orc_assign_metric(L, d, pk, n_sink, C, pm, metric, mode,
+                                  a.ctypes.data_as(_I32), m.ctypes.data_as(_D))
     return a, m
 
 
@@ -166,8 +182,10 @@ def objective(K, n_sink, assign_, mu):
     return _load().orc_objective(L, d, pk, n_sink, pa, pm)
 
 
-def cluster(K, n_sink, C, iters, mode=MIRROR, token_base=0, trace=False):
+def cluster(K, n_sink, C, iters, mode=MIRROR, token_base=0, trace=False, metric=COSINE):
     """Full K-means for H heads. K: [H][L][d] (or [L][d] for one head).
+    `metric` picks the assignment distance (the trace is the cosine
+    objective, so it needs the cosine).
 
     Returns dict(mu [H][C][d], assign [H][L], offsets [H][C+1],
     tokens [H][L'], trace [H][2*iters] or None, changed [H][iters])."""
@@ -184,11 +202,12 @@ def cluster(K, n_sink, C, iters, mode=MIRROR, token_base=0, trace=False):
     tok = np.empty((H, Lp), dtype=np.int32)
     tr = np.empty((H, 2 * iters)) if trace else None
     ch = np.empty((H, iters), dtype=np.int64)
-    _load().orc_cluster(mode, H, L, d, pk, n_sink, C, iters, token_base,
-                        mu.ctypes.data_as(_D), a.ctypes.data_as(_I32),
-                        off.ctypes.data_as(_I32), tok.ctypes.data_as(_I32),
-                        tr.ctypes.data_as(_D) if trace else _null(_D),
-                        ch.ctypes.data_as(_I64))
+    assert not (trace and metric != COSINE), "the trace is the cosine objective"
+    _load().orc_cluster_metric(metric, mode, H, L, d, pk, n_sink, C, iters, token_base,
+                               mu.ctypes.data_as(_D), a.ctypes.data_as(_I32),
+                               off.ctypes.data_as(_I32), tok.ctypes.data_as(_I32),
+                               tr.ctypes.data_as(_D) if trace else _null(_D),
+                               ch.ctypes.data_as(_I64))
     out = dict(mu=mu, assign=a, offsets=off, tokens=tok, trace=tr, changed=ch)
     if squeeze:
         out = {k: (v[0] if v is not None else None) for k, v in out.items()}

@@ -54,6 +54,14 @@
 #define ORC_EXACT 0
 #define ORC_MIRROR 1
 
+/* Assignment distances. The page argues for the cosine distance over L2 and
+ * inner-product distance (outlier channels of large magnitude make the
+ * latter two swing) and ablates the three [Clustering in semantic space;
+ * recall experiment, Fig. 11b]. */
+#define ORC_COSINE 0
+#define ORC_INNER_PRODUCT 1
+#define ORC_L2 2
+
 /* ------------------------------------------------------------ rounding -- */
 
 /* Round a float to bfloat16 (nearest, ties to even) and return it as float.
@@ -126,28 +134,61 @@ void orc_init_centroids(int64_t L, int d, const double *K, int n_sink, int C,
         memcpy(mu + (int64_t)c * d, K + (n_sink + s * c) * d, sizeof(double) * d);
 }
 
-/* Assignment step: each non-sink key joins the centroid of largest cosine
- * similarity (smallest D) [Clustering in semantic space, Fig. 4]. Ties go to
- * the lower cluster id. Writes assign[0..L) (-1 for sinks) and, if margin is
- * not NULL, margin[i] = best - second-best score (+inf when C == 1, and
- * for sinks). K is one head [L][d]; mu is [C][d]. */
-void orc_assign(int64_t L, int d, const double *K, int n_sink, int C,
-                const double *mu, int mode, int32_t *assign, double *margin)
+/* A key or centroid as the inner-product and L2 comparisons see it:
+ *   EXACT : x itself.
+ *   MIRROR: bf16(fp32(x_j)), the way the GPU stores its operands. */
+static void orc_store(const double *x, int d, int mode, double *out)
+{
+    for (int j = 0; j < d; ++j)
+        out[j] = (mode == ORC_EXACT) ? x[j] : (double)orc_round_bf16((float)x[j]);
+}
+
+/* Squared Euclidean distance sum_j (a_j - b_j)^2, summed in channel order. */
+static double orc_dist2(const double *a, const double *b, int d)
+{
+    double s = 0.0;
+    for (int j = 0; j < d; ++j) s += (a[j] - b[j]) * (a[j] - b[j]);
+    return s;
+}
+
+/* Assignment step under one of the three distances [Clustering in semantic
+ * space, Fig. 4, and its ablation]. Each non-sink key joins
+ *   ORC_COSINE       : the centroid of largest cosine similarity (smallest D);
+ *   ORC_INNER_PRODUCT: the centroid of largest <k, mu>;
+ *   ORC_L2           : the centroid of smallest sum_j (k_j - mu_j)^2.
+ * Ties go to the lower cluster id. Writes assign[0..L) (-1 for sinks) and,
+ * if margin is not NULL, margin[i] = the gap between the best and the
+ * second-best candidate (score gap for cosine and inner product, squared
+ * distance gap for L2; +inf when C == 1, and for sinks). K is one head
+ * [L][d]; mu is [C][d]. */
+void orc_assign_metric(int64_t L, int d, const double *K, int n_sink, int C,
+                       const double *mu, int metric, int mode, int32_t *assign,
+                       double *margin)
 {
     double *mt = malloc(sizeof(double) * (size_t)C * d);
     double *kt = malloc(sizeof(double) * d);
-    for (int c = 0; c < C; ++c) orc_unit(mu + (int64_t)c * d, d, mode, mt + (int64_t)c * d);
+    for (int c = 0; c < C; ++c) {
+        if (metric == ORC_COSINE)
+            orc_unit(mu + (int64_t)c * d, d, mode, mt + (int64_t)c * d);
+        else
+            orc_store(mu + (int64_t)c * d, d, mode, mt + (int64_t)c * d);
+    }
     for (int64_t i = 0; i < L; ++i) {
         if (i < n_sink) {
             assign[i] = -1;
             if (margin) margin[i] = INFINITY;
             continue;
         }
-        orc_unit(K + i * d, d, mode, kt);
+        if (metric == ORC_COSINE)
+            orc_unit(K + i * d, d, mode, kt);
+        else
+            orc_store(K + i * d, d, mode, kt);
         double best = -INFINITY, second = -INFINITY;
         int arg = 0;
         for (int c = 0; c < C; ++c) {
-            double s = orc_dot(kt, mt + (int64_t)c * d, d);
+            /* larger is better: similarity, or the negated distance */
+            double s = (metric == ORC_L2) ? -orc_dist2(kt, mt + (int64_t)c * d, d)
+                                          : orc_dot(kt, mt + (int64_t)c * d, d);
             if (s > best) {
                 second = best;
                 best = s;
@@ -161,6 +202,13 @@ void orc_assign(int64_t L, int d, const double *K, int n_sink, int C,
     }
     free(kt);
     free(mt);
+}
+
+/* The page's assignment: cosine distance. */
+void orc_assign(int64_t L, int d, const double *K, int n_sink, int C,
+                const double *mu, int mode, int32_t *assign, double *margin)
+{
+    orc_assign_metric(L, d, K, n_sink, C, mu, ORC_COSINE, mode, assign, margin);
 }
 
 /* Cluster metadata [Selection and indexing, Fig. 8]: cluster sizes, their
@@ -243,11 +291,29 @@ double orc_objective(int64_t L, int d, const double *K, int n_sink,
  * changed is not NULL it receives per head and iteration the number of
  * tokens whose label differs from the previous iteration (first iteration:
  * all tokens). */
+void orc_cluster_metric(int metric, int mode, int H, int64_t L, int d, const double *K,
+                        int n_sink, int C, int iters, int64_t token_base, double *mu,
+                        int32_t *assign, int32_t *offsets, int32_t *tokens,
+                        double *trace, int64_t *changed);
+
 void orc_cluster(int mode, int H, int64_t L, int d, const double *K, int n_sink,
                  int C, int iters, int64_t token_base, double *mu,
                  int32_t *assign, int32_t *offsets, int32_t *tokens,
                  double *trace, int64_t *changed)
 {
+    orc_cluster_metric(ORC_COSINE, mode, H, L, d, K, n_sink, C, iters, token_base, mu,
+                       assign, offsets, tokens, trace, changed);
+}
+
+/* The same loop with the assignment under `metric` (the update is the mean
+ * of the raw keys for every metric); trace must be NULL unless the metric
+ * is the cosine, whose objective it records. */
+void orc_cluster_metric(int metric, int mode, int H, int64_t L, int d, const double *K,
+                        int n_sink, int C, int iters, int64_t token_base, double *mu,
+                        int32_t *assign, int32_t *offsets, int32_t *tokens,
+                        double *trace, int64_t *changed)
+{
+    if (metric != ORC_COSINE) trace = NULL;
     int64_t Lp = L - n_sink;
     double *mu_next = malloc(sizeof(double) * (size_t)C * d);
     int32_t *prev = malloc(sizeof(int32_t) * (size_t)L);
@@ -258,7 +324,7 @@ void orc_cluster(int mode, int H, int64_t L, int d, const double *K, int n_sink,
         orc_init_centroids(L, d, Kh, n_sink, C, muh);
         for (int64_t i = 0; i < L; ++i) prev[i] = -2;
         for (int t = 0; t < iters; ++t) {
-            orc_assign(L, d, Kh, n_sink, C, muh, mode, ah, NULL);
+            orc_assign_metric(L, d, Kh, n_sink, C, muh, metric, mode, ah, NULL);
             if (trace) trace[(int64_t)h * 2 * iters + 2 * t] =
                 orc_objective(L, d, Kh, n_sink, ah, muh);
             if (changed) {
