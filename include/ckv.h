@@ -53,6 +53,12 @@ typedef enum {
 
 typedef enum { CKV_F32 = 0, CKV_BF16 = 1 } ckv_dtype;
 
+/* Assignment distance of ckv_cluster. The page clusters with the cosine
+ * distance and reports L2 and inner-product distance as worse, because the
+ * outlier channels of keys make them swing [Clustering in semantic space;
+ * recall experiment, Fig. 11b]; the other two exist for that ablation. */
+typedef enum { CKV_COSINE = 0, CKV_INNER_PRODUCT = 1, CKV_L2 = 2 } ckv_metric;
+
 /* Static English text for a status code (never NULL). */
 const char *ckv_status_string(int status);
 
@@ -76,6 +82,16 @@ int ckv_abi_version(void);
  * 1/|x| in fp64, rounded to fp32 then to bf16) with fp32 accumulation for
  * CKV_BF16 keys, and on fp32 unit vectors with fp32 accumulation for
  * CKV_F32 keys. Centroid means are accumulated in fp64 and stored as fp32.
+ *
+ * desc->metric selects the distance of the assignment (the update is the
+ * mean of the raw keys for every metric):
+ *   CKV_COSINE        largest cosine similarity, as above;
+ *   CKV_INNER_PRODUCT largest <k, mu> on the raw key and the centroid
+ *                     rounded to the key's type (bf16 or fp32);
+ *   CKV_L2            smallest |k - mu|^2, evaluated as the largest
+ *                     <k, mu> - |mu|^2 / 2 on the same operands (|mu|^2 an
+ *                     fp64 sum of the rounded centroid's squares, halved
+ *                     and stored as fp32).
  *
  * Outputs (per head h, all caller-owned device buffers):
  *   centroids   fp32 [H][c_cap][d]; slots c_base .. c_base+C-1 written.
@@ -103,6 +119,7 @@ typedef struct {
     int32_t c_cap;          /* centroid slots per head, >= c_base + C */
     int64_t t_base;         /* first token slot written, >= 0 */
     int64_t t_cap;          /* token slots per head, >= t_base + L - n_sink */
+    int32_t metric;         /* ckv_metric of the assignment (0: cosine) */
 } ckv_cluster_desc;
 
 /* Bytes of workspace ckv_cluster needs for `desc` (0 if desc is invalid). */

@@ -30,6 +30,7 @@ __all__ = [
 
 CKV_OK, CKV_ERR_INVALID_ARG, CKV_ERR_UNSUPPORTED, CKV_ERR_WORKSPACE, CKV_ERR_LAUNCH = range(5)
 CKV_F32, CKV_BF16 = 0, 1
+CKV_COSINE, CKV_INNER_PRODUCT, CKV_L2 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libckv.so")
@@ -47,7 +48,7 @@ class ClusterDesc(ct.Structure):
                 ("k_head_stride", ct.c_int64), ("token_base", ct.c_int64),
                 ("n_sink", ct.c_int32), ("C", ct.c_int32), ("iters", ct.c_int32),
                 ("dtype", ct.c_int32), ("c_base", ct.c_int32), ("c_cap", ct.c_int32),
-                ("t_base", ct.c_int64), ("t_cap", ct.c_int64)]
+                ("t_base", ct.c_int64), ("t_cap", ct.c_int64), ("metric", ct.c_int32)]
 
 
 class SelectDesc(ct.Structure):
@@ -174,8 +175,10 @@ def ckv_cluster(K: torch.Tensor, n_sink: int, C: int, iters: int, *, token_base:
                 centroids: Optional[torch.Tensor] = None, assign: Optional[torch.Tensor] = None,
                 csr_offsets: Optional[torch.Tensor] = None,
                 csr_tokens: Optional[torch.Tensor] = None, c_base: int = 0, t_base: int = 0,
-                workspace: Optional[torch.Tensor] = None, stream=None):
-    """Cosine K-means over rows n_sink..L-1 of each head of K [H][L][d].
+                workspace: Optional[torch.Tensor] = None, stream=None,
+                metric: int = CKV_COSINE):
+    """Cosine K-means over rows n_sink..L-1 of each head of K [H][L][d]
+    (metric CKV_INNER_PRODUCT or CKV_L2: the distance ablation).
 
     Returns (centroids [H][c_cap][d] fp32, assign [H][L] int32,
     csr_offsets [H][c_cap+1] int32, csr_tokens [H][t_cap] int32). Passing
@@ -204,7 +207,8 @@ def ckv_cluster(K: torch.Tensor, n_sink: int, C: int, iters: int, *, token_base:
           "bad assign buffer")
     desc = ClusterDesc(H=H, d=d, L=L, k_head_stride=hs, token_base=token_base, n_sink=n_sink,
                        C=C, iters=iters, dtype=_dtype_code(K), c_base=c_base,
-                       c_cap=centroids.shape[1], t_base=t_base, t_cap=csr_tokens.shape[1])
+                       c_cap=centroids.shape[1], t_base=t_base, t_cap=csr_tokens.shape[1],
+                       metric=metric)
     nb = lib.ckv_cluster_workspace(ct.byref(desc))
     if nb == 0:
         # report the reason through the call itself (no launch happens)

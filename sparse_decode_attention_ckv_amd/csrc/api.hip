@@ -56,6 +56,8 @@ int check_cluster(const ckv_cluster_desc *d) {
     if (d->c_base < 0 || (int64_t)d->c_cap < (int64_t)d->c_base + d->C) return CKV_ERR_INVALID_ARG;
     if (d->t_base < 0 || d->t_cap < d->t_base + Lp || d->t_cap > INT32_MAX)
         return CKV_ERR_INVALID_ARG;
+    if (d->metric != CKV_COSINE && d->metric != CKV_INNER_PRODUCT && d->metric != CKV_L2)
+        return CKV_ERR_INVALID_ARG;
     return CKV_OK;
 }
 
@@ -66,6 +68,7 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     p->iters = d->iters;
     p->n_sink = d->n_sink;
     p->dtype = d->dtype;
+    p->metric = d->metric;
     p->c_base = d->c_base;
     p->c_cap = d->c_cap;
     p->L = d->L;
@@ -81,6 +84,8 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     o += align_up((size_t)p->H * p->Lp * kD * es);
     p->mt = ws ? ws + o : nullptr;
     o += align_up((size_t)p->H * p->Cpad * kD * es);
+    p->mb = ws ? (float *)(ws + o) : nullptr;
+    o += align_up((size_t)p->H * p->Cpad * sizeof(float));
     p->tile_hist = ws ? (int32_t *)(ws + o) : nullptr;
     o += align_up((size_t)p->H * p->ntiles * p->C * sizeof(int32_t));
     p->tile_rank = ws ? (int32_t *)(ws + o) : nullptr;
@@ -190,7 +195,7 @@ const char *ckv_status_string(int status) {
     }
 }
 
-int ckv_abi_version(void) { return 2; }
+int ckv_abi_version(void) { return 3; }
 
 size_t ckv_cluster_workspace(const ckv_cluster_desc *desc) {
     if (check_cluster(desc) != CKV_OK) return 0;

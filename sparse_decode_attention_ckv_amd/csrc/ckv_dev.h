@@ -176,14 +176,21 @@ __device__ inline int block_excl_scan(int v, int *wsum, int *total) {
 int device_cu_count();
 
 // ---- launchers (defined in the .hip files) ------------------------------
+// assignment distances (the values of ckv_metric)
+constexpr int kCosine = 0, kInnerProduct = 1, kL2 = 2;
+
 struct ClusterPlan {
     int H, C, Cpad, iters, n_sink, dtype, c_base, c_cap;
+    int metric;               // kCosine, kInnerProduct or kL2
     int64_t L, Lp, k_head_stride, token_base, t_base, t_cap;
     int64_t ntiles;           // CSR tiles per head
     int n_cu;                 // compute units of the device (persistent grids)
     // workspace carve-up (device pointers)
-    void *kt;                 // unit keys [H][Lp][d] (bf16 or f32)
-    void *mt;                 // unit centroids [H][Cpad][d] (bf16 or f32)
+    void *kt;                 // keys as the assignment reads them [H][Lp][d]
+                              // (bf16 or f32; unit rows for the cosine)
+    void *mt;                 // centroids as the assignment reads them [H][Cpad][d]
+                              // (bf16 or f32; unit rows for the cosine)
+    float *mb;                // per-cluster score bias [H][Cpad] (L2: -|mu|^2 / 2)
     int32_t *tile_hist;       // [H][ntiles][C], then tile bases
     int32_t *tile_rank;       // [H][Lp]
     int32_t *counts;          // [H][C] cluster sizes

@@ -7,7 +7,8 @@
 // label-sorted token indices kept as metadata).
 //
 // One call runs, per independent KV head:
-//   normalize_keys            unit keys, once              (HBM-bound)
+//   normalize_keys            unit keys, once (raw copy for the
+//                             inner-product and L2 ablation)  (HBM-bound)
 //   init_centroids            mu_c = k_{n_sink + s*c}
 //   iters x {
 //     assign                  cosine GEMM on bf16 MFMA + fused row argmax
@@ -50,6 +51,30 @@ __device__ void block_unit_row(float x, bool active, int j, void *out_row,
     }
 }
 
+// The row as the inner-product and L2 assignments read it: element j
+// rounded to the key type (bf16 when BF16). For L2 also the score bias
+// -|x^|^2 / 2 of the rounded row x^: one fp64 fma chain over j = 0..127 by
+// thread 0, halved, stored as fp32.
+template <bool BF16, bool L2>
+__device__ void block_store_row(float x, int j, void *out_row, float *sx, float *bias) {
+    float y = x;
+    if (BF16) {
+        const uint32_t b = f32_to_bf16_rne(x);
+        ((uint16_t *)out_row)[j] = (uint16_t)b;
+        y = bf16_to_f32((uint16_t)b);
+    } else {
+        ((float *)out_row)[j] = x;
+    }
+    if (!L2) return;
+    sx[j] = y;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double ss = 0.0;
+        for (int k = 0; k < kD; ++k) ss = __fma_rn((double)sx[k], (double)sx[k], ss);
+        *bias = (float)(-0.5 * ss);
+    }
+}
+
 // --------------------------------------------------------------------------
 // normalize_keys: the fp64 norm is a sequential chain, so one thread owns a
 // row; the rows of a 256-row block are moved through LDS so that global
@@ -58,6 +83,36 @@ __device__ void block_unit_row(float x, bool active, int j, void *out_row,
 constexpr int kNkRows = 256;             // rows per workgroup (one per thread)
 constexpr int kNkStride = 17;            // LDS row stride in 16-byte chunks
 
+// One LDS row (16 chunks of 8 bf16): the chain over it (chunks in order),
+// then the unit row written back in place.
+__device__ __forceinline__ void nk_unit_row(u32x4 *row) {
+    double ss = 0.0;
+#pragma unroll 2
+    for (int i = 0; i < 16; ++i) {
+        float f[8];
+        unpack8(row[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __fma_rn((double)f[e], (double)f[e], ss);
+    }
+    const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+        float f[8];
+        unpack8(row[i], f);
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne((float)((double)f[e] * inv));
+        u32x4 v;
+        v.x = o[0] | (o[1] << 16);
+        v.y = o[2] | (o[3] << 16);
+        v.z = o[4] | (o[5] << 16);
+        v.w = o[6] | (o[7] << 16);
+        row[i] = v;
+    }
+}
+
+// UNIT = false copies the rows unchanged (inner-product and L2 assignment).
+template <bool UNIT>
 __global__ __launch_bounds__(kNkRows) void k_normalize_keys_bf16(
     const uint16_t *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
     uint16_t *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
@@ -85,33 +140,10 @@ __global__ __launch_bounds__(kNkRows) void k_normalize_keys_bf16(
         }
     }
     __syncthreads();
-    // thread tid: the chain over its row (chunks in order), then the unit row
-    // back into LDS
-    u32x4 *row = rows + tid * kNkStride;
-    double ss = 0.0;
-#pragma unroll 2
-    for (int i = 0; i < 16; ++i) {
-        float f[8];
-        unpack8(row[i], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = __fma_rn((double)f[e], (double)f[e], ss);
+    if (UNIT) {
+        nk_unit_row(rows + tid * kNkStride);
+        __syncthreads();
     }
-    const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-        float f[8];
-        unpack8(row[i], f);
-        uint32_t o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne((float)((double)f[e] * inv));
-        u32x4 v;
-        v.x = o[0] | (o[1] << 16);
-        v.y = o[2] | (o[3] << 16);
-        v.z = o[4] | (o[5] << 16);
-        v.w = o[6] | (o[7] << 16);
-        row[i] = v;
-    }
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int e = tid + kNkRows * k;
@@ -119,6 +151,7 @@ __global__ __launch_bounds__(kNkRows) void k_normalize_keys_bf16(
     }
 }
 
+template <bool UNIT>
 __global__ __launch_bounds__(256) void k_normalize_keys_f32(
     const float *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
     float *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
@@ -128,10 +161,14 @@ __global__ __launch_bounds__(256) void k_normalize_keys_f32(
     const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (r >= Lp) return;
     const float *src = K + h * head_stride + (n_sink + r) * kD;
+    float *dst = kt + ((int64_t)h * Lp + r) * kD;
+    if (!UNIT) {
+        for (int j = 0; j < kD; ++j) dst[j] = src[j];
+        return;
+    }
     double ss = 0.0;
     for (int j = 0; j < kD; ++j) ss = __fma_rn((double)src[j], (double)src[j], ss);
     const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
-    float *dst = kt + ((int64_t)h * Lp + r) * kD;
     for (int j = 0; j < kD; ++j) dst[j] = (float)((double)src[j] * inv);
 }
 
@@ -139,24 +176,26 @@ hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *a
                                  hipStream_t s) {
     dim3 grid((unsigned)((p.Lp + 255) / 256), p.H);
     static_assert(kNkRows == 256, "one grid for both element types");
+    const bool unit = p.metric == kCosine;
     if (p.dtype == 1)
-        hipLaunchKernelGGL(k_normalize_keys_bf16, grid, dim3(kNkRows), 0, s,
-                           (const uint16_t *)K, p.k_head_stride, p.n_sink, p.Lp,
-                           (uint16_t *)p.kt, assign, p.L);
+        hipLaunchKernelGGL(unit ? k_normalize_keys_bf16<true> : k_normalize_keys_bf16<false>,
+                           grid, dim3(kNkRows), 0, s, (const uint16_t *)K, p.k_head_stride,
+                           p.n_sink, p.Lp, (uint16_t *)p.kt, assign, p.L);
     else
-        hipLaunchKernelGGL(k_normalize_keys_f32, grid, dim3(256), 0, s,
-                           (const float *)K, p.k_head_stride, p.n_sink, p.Lp,
-                           (float *)p.kt, assign, p.L);
+        hipLaunchKernelGGL(unit ? k_normalize_keys_f32<true> : k_normalize_keys_f32<false>,
+                           grid, dim3(256), 0, s, (const float *)K, p.k_head_stride,
+                           p.n_sink, p.Lp, (float *)p.kt, assign, p.L);
     return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
 // init_centroids: mu_c = raw key at window row n_sink + s*c, s = floor(Lp/C)
 // (the page samples keys as initial centroids; evenly spaced tokens here).
-template <bool BF16>
+template <bool BF16, int M>
 __global__ __launch_bounds__(128) void k_init_centroids(
     const void *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp, int C,
-    float *__restrict__ cent, int c_base, int c_cap, void *__restrict__ mt, int Cpad) {
+    float *__restrict__ cent, int c_base, int c_cap, void *__restrict__ mt,
+    float *__restrict__ mb, int Cpad) {
     __shared__ float sx[kD];
     __shared__ double sinv;
     const int c = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
@@ -166,20 +205,33 @@ __global__ __launch_bounds__(128) void k_init_centroids(
     cent[((int64_t)h * c_cap + c_base + c) * kD + j] = x;
     const int64_t mrow = ((int64_t)h * Cpad + c) * kD;
     void *out = BF16 ? (void *)((uint16_t *)mt + mrow) : (void *)((float *)mt + mrow);
-    block_unit_row<BF16>(x, true, j, out, sx, &sinv);
+    if (M == kCosine)
+        block_unit_row<BF16>(x, true, j, out, sx, &sinv);
+    else
+        block_store_row<BF16, M == kL2>(x, j, out, sx, mb + (int64_t)h * Cpad + c);
+}
+
+template <int M>
+static void launch_init_m(const ClusterPlan &p, const void *K, float *cent, hipStream_t s) {
+    dim3 grid(p.C, p.H);
+    if (p.dtype == 1)
+        hipLaunchKernelGGL((k_init_centroids<true, M>), grid, dim3(128), 0, s, K,
+                           p.k_head_stride, p.n_sink, p.Lp, p.C, cent, p.c_base,
+                           p.c_cap, p.mt, p.mb, p.Cpad);
+    else
+        hipLaunchKernelGGL((k_init_centroids<false, M>), grid, dim3(128), 0, s, K,
+                           p.k_head_stride, p.n_sink, p.Lp, p.C, cent, p.c_base,
+                           p.c_cap, p.mt, p.mb, p.Cpad);
 }
 
 hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cent,
                                  hipStream_t s) {
-    dim3 grid(p.C, p.H);
-    if (p.dtype == 1)
-        hipLaunchKernelGGL(k_init_centroids<true>, grid, dim3(128), 0, s, K,
-                           p.k_head_stride, p.n_sink, p.Lp, p.C, cent, p.c_base,
-                           p.c_cap, p.mt, p.Cpad);
+    if (p.metric == kCosine)
+        launch_init_m<kCosine>(p, K, cent, s);
+    else if (p.metric == kInnerProduct)
+        launch_init_m<kInnerProduct>(p, K, cent, s);
     else
-        hipLaunchKernelGGL(k_init_centroids<false>, grid, dim3(128), 0, s, K,
-                           p.k_head_stride, p.n_sink, p.Lp, p.C, cent, p.c_base,
-                           p.c_cap, p.mt, p.Cpad);
+        launch_init_m<kL2>(p, K, cent, s);
     return hipGetLastError();
 }
 
@@ -225,10 +277,11 @@ __device__ __forceinline__ void as_load_b(const u32x4 *K4, int64_t Lp, int64_t t
 
 // One 16-cluster M tile (LDS rows 16m ..) against the wave's 64 tokens, then
 // the running argmax over the lane's rows c0 .. c0+3 in ascending order
-// (strict >, so the first maximum stays); MASK drops ids >= C.
-template <bool MASK>
-__device__ __forceinline__ void as_mtile(const u32x4 *sA, int m, int col, int kq,
-                                         const bf16x8 (&b)[4][4], int c0, int C,
+// (strict >, so the first maximum stays); MASK drops ids >= C. BIAS adds the
+// clusters' score bias (L2: -|mu|^2 / 2, from LDS) to the scores first.
+template <bool MASK, bool BIAS>
+__device__ __forceinline__ void as_mtile(const u32x4 *sA, const float *sB, int m, int col,
+                                         int kq, const bf16x8 (&b)[4][4], int c0, int C,
                                          float (&best)[4], int (&bid)[4]) {
     bf16x8 afr[4];
     const int r = 16 * m + col;
@@ -243,6 +296,13 @@ __device__ __forceinline__ void as_mtile(const u32x4 *sA, int m, int col, int kq
 #pragma unroll
         for (int t = 0; t < 4; ++t)
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], b[t][s], acc[t], 0, 0, 0);
+    if (BIAS) {
+        const f32x4 bv = *(const f32x4 *)(sB + 16 * m + 4 * kq);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] += bv[i];
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -253,11 +313,13 @@ __device__ __forceinline__ void as_mtile(const u32x4 *sA, int m, int col, int kq
             }
 }
 
+template <bool BIAS>
 __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
-    const uint16_t *__restrict__ kt, const uint16_t *__restrict__ mt, int64_t Lp, int C,
-    int Cpad, int32_t *__restrict__ assign, int64_t L, int n_sink, int tiles_per_head,
-    int n_tiles) {
+    const uint16_t *__restrict__ kt, const uint16_t *__restrict__ mt,
+    const float *__restrict__ mb, int64_t Lp, int C, int Cpad, int32_t *__restrict__ assign,
+    int64_t L, int n_sink, int tiles_per_head, int n_tiles) {
     __shared__ u32x4 sA[kAsRound * 16];
+    __shared__ __align__(16) float sB[BIAS ? kAsRound : 4];
     const uint32_t w = xcd_linear(blockIdx.x, gridDim.x);
     const int t_begin = (int)((int64_t)w * n_tiles / gridDim.x);
     const int t_end = (int)((int64_t)(w + 1) * n_tiles / gridDim.x);
@@ -299,6 +361,7 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
                         if (e < rows * 16) sA[rr * 16 + (q ^ (rr & 15))] = v[k];
                     }
                 }
+                if (BIAS && tid < rows) sB[tid] = mb[(int64_t)h * Cpad + rb + tid];
                 __syncthreads();
                 loaded = h;
             }
@@ -308,8 +371,8 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
             const int nm = rows / 16;
             const int cl = rb + 4 * kq;                   // lane's first row of tile 0
             for (int m = 0; m + 1 < nm; ++m)
-                as_mtile<false>(sA, m, col, kq, b, cl + 16 * m, C, best, bid);
-            as_mtile<true>(sA, nm - 1, col, kq, b, cl + 16 * (nm - 1), C, best, bid);
+                as_mtile<false, BIAS>(sA, sB, m, col, kq, b, cl + 16 * m, C, best, bid);
+            as_mtile<true, BIAS>(sA, sB, nm - 1, col, kq, b, cl + 16 * (nm - 1), C, best, bid);
         }
         // merge the four row groups (lanes l, l^16, l^32, l^48) of each token
         int res[4];
@@ -338,11 +401,12 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
     }
 }
 
-// assign (fp32): one thread per token, fp32 unit vectors, fp32 dot product
-// over j = 0..127, argmax with ties to the lower id. Used for fp32 keys.
+// assign (fp32): one thread per token, fp32 dot product over j = 0..127 of
+// the rows in kt and mt (unit rows for the cosine), plus the cluster's bias
+// when mb is given (L2), argmax with ties to the lower id. Used for fp32 keys.
 __global__ __launch_bounds__(256) void k_assign_f32(
-    const float *__restrict__ kt, const float *__restrict__ mt, int64_t Lp, int C, int Cpad,
-    int32_t *__restrict__ assign, int64_t L, int n_sink) {
+    const float *__restrict__ kt, const float *__restrict__ mt, const float *__restrict__ mb,
+    int64_t Lp, int C, int Cpad, int32_t *__restrict__ assign, int64_t L, int n_sink) {
     const int h = blockIdx.y;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= Lp) return;
@@ -357,6 +421,7 @@ __global__ __launch_bounds__(256) void k_assign_f32(
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < kD; ++j) s = __fmaf_rn(k[j], m[j], s);
+        if (mb) s += mb[(int64_t)h * Cpad + c];
         if (s > best) {
             best = s;
             arg = c;
@@ -370,13 +435,15 @@ hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s) {
         const int tph = (int)((p.Lp + kAsTok - 1) / kAsTok);
         const int n_tiles = tph * p.H;
         const int grid = n_tiles < p.n_cu ? n_tiles : p.n_cu;
-        hipLaunchKernelGGL(k_assign_bf16, dim3((unsigned)grid), dim3(kAsThreads), 0, s,
-                           (const uint16_t *)p.kt, (const uint16_t *)p.mt, p.Lp, p.C,
-                           p.Cpad, assign, p.L, p.n_sink, tph, n_tiles);
+        hipLaunchKernelGGL(p.metric == kL2 ? k_assign_bf16<true> : k_assign_bf16<false>,
+                           dim3((unsigned)grid), dim3(kAsThreads), 0, s,
+                           (const uint16_t *)p.kt, (const uint16_t *)p.mt, (const float *)p.mb,
+                           p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink, tph, n_tiles);
     } else {
         dim3 grid((unsigned)((p.Lp + 255) / 256), p.H);
         hipLaunchKernelGGL(k_assign_f32, grid, dim3(256), 0, s, (const float *)p.kt,
-                           (const float *)p.mt, p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink);
+                           (const float *)p.mt, p.metric == kL2 ? (const float *)p.mb : nullptr,
+                           p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink);
     }
     return hipGetLastError();
 }
@@ -563,11 +630,12 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
 // mean = sum / n in fp64, stored as fp32; an empty cluster keeps its
 // centroid. The unit centroid for the next assignment is written too, by
 // the first wave alone (no barrier after the reduction).
-template <bool BF16>
+template <bool BF16, int M>
 __global__ __launch_bounds__(256) void k_update(
     const void *__restrict__ K, int64_t head_stride, int64_t L, int64_t token_base,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ tokens, int c_base,
-    int c_cap, int64_t t_cap, float *__restrict__ cent, void *__restrict__ mt, int Cpad) {
+    int c_cap, int64_t t_cap, float *__restrict__ cent, void *__restrict__ mt,
+    float *__restrict__ mb, int Cpad) {
     __shared__ double red[4][kD];
     __shared__ __align__(16) float sx[kD];
     const int c = blockIdx.x, h = blockIdx.y;
@@ -654,6 +722,40 @@ __global__ __launch_bounds__(256) void k_update(
         mu[k] = (n > 0) ? (float)(ssum / (double)n) : cp[j];
         cp[j] = mu[k];
     }
+    const int64_t mrow = ((int64_t)h * Cpad + c) * kD;
+    if (M != kCosine) {
+        // inner product and L2 read the mean rounded to the key type; L2 also
+        // the bias -|mu^|^2 / 2 of that rounded row (fp64 chain in channel
+        // order on every lane, written by lane 0)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            float y = mu[k];
+            if (BF16) {
+                const uint32_t b = f32_to_bf16_rne(mu[k]);
+                ((uint16_t *)mt)[mrow + lane + 64 * k] = (uint16_t)b;
+                y = bf16_to_f32((uint16_t)b);
+            } else {
+                ((float *)mt)[mrow + lane + 64 * k] = y;
+            }
+            sx[lane + 64 * k] = y;
+        }
+        if (M == kL2) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            double ss = 0.0;
+#pragma unroll 4
+            for (int j4 = 0; j4 < kD / 4; ++j4) {
+                const f32x4 x = *(const f32x4 *)(sx + 4 * j4);
+                ss = __fma_rn((double)x[0], (double)x[0], ss);
+                ss = __fma_rn((double)x[1], (double)x[1], ss);
+                ss = __fma_rn((double)x[2], (double)x[2], ss);
+                ss = __fma_rn((double)x[3], (double)x[3], ss);
+            }
+            if (lane == 0) mb[(int64_t)h * Cpad + c] = (float)(-0.5 * ss);
+        }
+        return;
+    }
     // the row through LDS (one wave: its LDS accesses stay in order), then
     // every lane runs the chain on broadcast reads
     sx[lane] = mu[0];
@@ -671,7 +773,6 @@ __global__ __launch_bounds__(256) void k_update(
         ss = __fma_rn((double)x[3], (double)x[3], ss);
     }
     const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
-    const int64_t mrow = ((int64_t)h * Cpad + c) * kD;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const float y = (float)((double)mu[k] * inv);
@@ -682,17 +783,28 @@ __global__ __launch_bounds__(256) void k_update(
     }
 }
 
-hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
-                         const int32_t *tokens, float *cent, hipStream_t s) {
+template <int M>
+static void launch_update_m(const ClusterPlan &p, const void *K, const int32_t *offsets,
+                            const int32_t *tokens, float *cent, hipStream_t s) {
     dim3 grid(p.C, p.H);
     if (p.dtype == 1)
-        hipLaunchKernelGGL(k_update<true>, grid, dim3(256), 0, s, K, p.k_head_stride, p.L,
+        hipLaunchKernelGGL((k_update<true, M>), grid, dim3(256), 0, s, K, p.k_head_stride, p.L,
                            p.token_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap, cent,
-                           p.mt, p.Cpad);
+                           p.mt, p.mb, p.Cpad);
     else
-        hipLaunchKernelGGL(k_update<false>, grid, dim3(256), 0, s, K, p.k_head_stride, p.L,
-                           p.token_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap, cent,
-                           p.mt, p.Cpad);
+        hipLaunchKernelGGL((k_update<false, M>), grid, dim3(256), 0, s, K, p.k_head_stride,
+                           p.L, p.token_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap,
+                           cent, p.mt, p.mb, p.Cpad);
+}
+
+hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
+                         const int32_t *tokens, float *cent, hipStream_t s) {
+    if (p.metric == kCosine)
+        launch_update_m<kCosine>(p, K, offsets, tokens, cent, s);
+    else if (p.metric == kInnerProduct)
+        launch_update_m<kInnerProduct>(p, K, offsets, tokens, cent, s);
+    else
+        launch_update_m<kL2>(p, K, offsets, tokens, cent, s);
     return hipGetLastError();
 }
 

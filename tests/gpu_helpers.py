@@ -46,8 +46,28 @@ def gpu_cluster(K, n_sink, C, iters, **kw):
     return out
 
 
+# the library's metric codes for the oracle's
+CK_METRIC = {oracle.COSINE: ck.CKV_COSINE, oracle.INNER_PRODUCT: ck.CKV_INNER_PRODUCT,
+             oracle.L2: ck.CKV_L2}
+
+
+def margin_threshold(metric, Kw, mu, margin, margin_rel):
+    """Per-token margin below which a label is not compared. Cosine scores
+    lie in [-1, 1]: the absolute `margin`. Inner-product and L2 scores grow
+    with |k| |mu|: fp32 accumulation of 128 products errs by at most about
+    128 * 2^-24 |k| |mu|, so the threshold is margin_rel |k| max|mu| (twice
+    that, plus the rounding of the fp32 bias -|mu|^2 / 2, for the L2
+    squared-distance gap)."""
+    if metric == oracle.COSINE:
+        return margin
+    kn = np.linalg.norm(Kw, axis=1)
+    M = np.linalg.norm(mu, axis=1).max()
+    thr = margin_rel * kn * M
+    return thr if metric == oracle.INNER_PRODUCT else 2 * (thr + 2.0 ** -22 * M * M)
+
+
 def lloyd_parity(Kdev, Kf64, n_sink, C, iters, mode, tol_mu=1e-4, margin=1e-4,
-                 token_base=0, sample=None):
+                 token_base=0, sample=None, metric=oracle.COSINE, margin_rel=2e-5):
     """Per-iteration parity of the GPU K-means against the oracle.
 
     For t = 1..iters the GPU runs t iterations from scratch (a prefix of the
@@ -57,7 +77,8 @@ def lloyd_parity(Kdev, Kf64, n_sink, C, iters, mode, tol_mu=1e-4, margin=1e-4,
       * the CSR of the GPU's labels, bit-exact;
       * the centroids of the GPU's labels, max abs error <= tol_mu.
     Kf64: [H][L][d] exact values. `sample`: optional token subset (window
-    rows >= n_sink) for the label check at large sizes.
+    rows >= n_sink) for the label check at large sizes. `metric` is the
+    oracle's assignment distance (the GPU runs the same one).
     Returns per-iteration (excluded fraction) list."""
     H, L, d = Kf64.shape
     Lp = L - n_sink
@@ -65,7 +86,8 @@ def lloyd_parity(Kdev, Kf64, n_sink, C, iters, mode, tol_mu=1e-4, margin=1e-4,
     excluded = []
     for t in range(1, iters + 1):
         say(f"  lloyd iteration {t}/{iters} (H={H}, L={L}, C={C})")
-        cent, asg, off, tok = gpu_cluster(Kdev, n_sink, C, t, token_base=token_base)
+        cent, asg, off, tok = gpu_cluster(Kdev, n_sink, C, t, token_base=token_base,
+                                          metric=CK_METRIC[metric])
         mu_g = host_f64(cent)
         a_g = asg.cpu().numpy()
         off_g = off.cpu().numpy()
@@ -74,13 +96,16 @@ def lloyd_parity(Kdev, Kf64, n_sink, C, iters, mode, tol_mu=1e-4, margin=1e-4,
         ex = 0
         for h in range(H):
             if sample is None:
-                a_o, m_o = oracle.assign(Kf64[h], n_sink, mu_prev[h], mode=mode)
-                keep = m_o[n_sink:] >= margin
+                a_o, m_o = oracle.assign(Kf64[h], n_sink, mu_prev[h], mode=mode, metric=metric)
+                keep = m_o[n_sink:] >= margin_threshold(metric, Kf64[h][n_sink:], mu_prev[h],
+                                                        margin, margin_rel)
                 got = a_g[h, n_sink:]
                 want = a_o[n_sink:]
             else:
-                a_o, m_o = oracle.assign(Kf64[h][sample], 0, mu_prev[h], mode=mode)
-                keep = m_o >= margin
+                a_o, m_o = oracle.assign(Kf64[h][sample], 0, mu_prev[h], mode=mode,
+                                         metric=metric)
+                keep = m_o >= margin_threshold(metric, Kf64[h][sample], mu_prev[h], margin,
+                                               margin_rel)
                 got = a_g[h, sample]
                 want = a_o
             bad = np.nonzero(keep & (got != want))[0]

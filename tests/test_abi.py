@@ -63,7 +63,7 @@ def test_status_strings():
     for s in range(5):
         assert ck.ckv_status_string(s)
     assert ck.ckv_status_string(99) == "unknown status"
-    assert ck.ckv_abi_version() == 2
+    assert ck.ckv_abi_version() == 3
 
 
 def _cl(**kw):
@@ -102,6 +102,8 @@ def _call_cluster(desc, ws_bytes=None, nullK=False):
     (dict(dtype=7), ck.CKV_ERR_INVALID_ARG),
     (dict(H=0), ck.CKV_ERR_INVALID_ARG),
     (dict(token_base=-3), ck.CKV_ERR_INVALID_ARG),
+    (dict(metric=3), ck.CKV_ERR_INVALID_ARG),
+    (dict(metric=-1), ck.CKV_ERR_INVALID_ARG),
 ])
 def test_cluster_rejects_bad_descriptors(kw, status):
     d = _cl(**kw)

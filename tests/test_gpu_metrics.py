@@ -1,0 +1,79 @@
+"""GPU parity of the clustering under the ablation distances.
+
+The page clusters keys by cosine distance and reports L2 and inner-product
+distance as worse ("ClusterKV: Manipulating LLM KV Cache in Semantic Space
+for Recallable Compression", section 语义空间中的聚类 and the recall
+experiment, Fig. 11b). ckv_cluster runs either of them with desc.metric;
+every Lloyd iteration is checked against the oracle's assignment under the
+same distance (labels exact outside a margin scaled by |k| |mu|), the CSR of
+the GPU's labels exactly and the centroids of the GPU's partition within
+1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_decode_attention_ckv_amd as ck
+import synth
+from tests.gpu_helpers import gpu_cluster, lloyd_parity, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+METRICS = {"inner_product": oracle.INNER_PRODUCT, "l2": oracle.L2}
+
+
+def _kv(wl, L, heads=None):
+    K, _, hs = synth.make_kv(wl, L=L, heads=heads)
+    return to_dev(K, wl.dtype), np.stack([h.Kf for h in hs]).astype(np.float64)
+
+
+@pytest.mark.parametrize("name", list(METRICS))
+@pytest.mark.parametrize("H,L,C", [(2, 4112, 51), (1, 1000, 7), (2, 2600, 600)])
+def test_cluster_metric_bf16_per_iteration(name, H, L, C):
+    wl = synth.workload(1)
+    say(f"cluster parity {name} bf16 H={H} L={L} C={C} (MIRROR oracle)")
+    Kd, Kf = _kv(wl, L, heads=range(H))
+    ex = lloyd_parity(Kd, Kf, 16, C, 6, oracle.MIRROR, metric=METRICS[name])
+    say(f"  excluded by the margin rule per iteration: {[round(x, 4) for x in ex]}")
+    assert max(ex) < 0.01
+
+
+@pytest.mark.parametrize("name", list(METRICS))
+def test_cluster_metric_fp32_single_head(name):
+    wl = synth.workload(0)
+    say(f"cluster parity {name}: single-head fp32 2k, 10 iterations (EXACT oracle)")
+    Kd, Kf = _kv(wl, wl.L)
+    ex = lloyd_parity(Kd, Kf, wl.n_sink, wl.C, wl.iters, oracle.EXACT, metric=METRICS[name])
+    assert max(ex) < 0.01
+
+
+@pytest.mark.parametrize("name", list(METRICS))
+def test_cluster_metric_windows_and_determinism(name):
+    wl = synth.workload(1)
+    m = METRICS[name]
+    say(f"cluster {name}: increment-sized and tiny windows, determinism")
+    Kd, Kf = _kv(wl, 400, heads=range(2))
+    lloyd_parity(Kd[:, :320].contiguous(), Kf[:, :320], 0, 4, 10, oracle.MIRROR, metric=m)
+    lloyd_parity(Kd[:, :40].contiguous(), Kf[:, :40], 3, 5, 3, oracle.MIRROR, metric=m)
+    a = gpu_cluster(Kd, 16, 9, 5, metric=m)
+    b = gpu_cluster(Kd, 16, 9, 5, metric=m)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_metrics_differ_on_outlier_keys():
+    """With the workload's outlier channels the three distances partition
+    the keys differently (the ablation measures something), and the cosine
+    result is the default call's."""
+    wl = synth.workload(1)
+    say("cluster: cosine vs inner product vs L2 partitions differ")
+    Kd, _ = _kv(wl, 4112, heads=range(2))
+    base = gpu_cluster(Kd, 16, 51, 6)
+    cos = gpu_cluster(Kd, 16, 51, 6, metric=ck.CKV_COSINE)
+    for x, y in zip(base, cos):
+        assert torch.equal(x, y)
+    ip = gpu_cluster(Kd, 16, 51, 6, metric=ck.CKV_INNER_PRODUCT)
+    l2 = gpu_cluster(Kd, 16, 51, 6, metric=ck.CKV_L2)
+    a_c, a_i, a_l = (x[1].cpu().numpy() for x in (cos, ip, l2))
+    assert (a_c != a_i).mean() > 0.05 and (a_c != a_l).mean() > 0.05
