@@ -6,7 +6,8 @@ package never imports the GPU library: the two share no code.
 
 The arithmetic lives in ``ckv_oracle.c`` (plain single-threaded C, fp64),
 built with gcc into ``libckv_oracle.so`` next to it. This module only
-marshals numpy arrays through ctypes. Each wrapper names the page section its
+marshals numpy arrays through ctypes. The GPU cache of selected rows is pure
+bookkeeping and is stated in numpy in ``cache.py``. Each wrapper names the page section its
 C function follows; the definitions are documented in the C source.
 
 Parity status: every function here is pinned by CPU tests against closed

@@ -43,11 +43,11 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "bf16_bits", "bf16_to_f32",
     "KVHead", "make_head", "make_kv", "make_queries", "make_query_steps", "make_appended",
-    "planted_head",
+    "make_query_stream", "planted_head",
 ]
 
 # Purposes of the per-head random streams.
-_S_DIRS, _S_KEYS, _S_VALS, _S_OUTL, _S_QUERY, _S_APPEND, _S_APPDIRS = range(7)
+_S_DIRS, _S_KEYS, _S_VALS, _S_OUTL, _S_QUERY, _S_APPEND, _S_APPDIRS, _S_QSTREAM = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -249,6 +249,33 @@ def make_query_steps(wl: Workload, steps: int, heads: Optional[Sequence[int]] = 
     float32 values)."""
     st, fv = zip(*(make_queries(wl, t, heads) for t in range(steps)))
     return np.stack(st), np.stack(fv)
+
+
+def make_query_stream(wl: Workload, steps: int, rho: float,
+                      heads: Optional[Sequence[int]] = None):
+    """Queries of a decode stream with step-to-step correlation rho:
+    q_0 = x_0 and q_t = rho q_{t-1} + sqrt(1 - rho^2) x_t, where each x_t is
+    a fresh query drawn like a key of the query head's KV head (outliers
+    included). rho = 0 gives independent queries, rho -> 1 a query that
+    barely moves. Returns ([steps][len(heads) * G][d] storage, float32
+    values)."""
+    hs = list(range(wl.H)) if heads is None else list(heads)
+    rows = []
+    for h in hs:
+        dirs = _head_dirs(wl.seed, h, wl.n_dirs, wl.d)
+        outl = _outliers(wl, h)
+        r = _rng(wl.seed, h, _S_QSTREAM, int(round(rho * 1e6)))
+        x, _ = _draw_keys(r, dirs, steps * wl.G, outl)
+        x = x.reshape(steps, wl.G, wl.d)
+        q = np.empty_like(x)
+        q[0] = x[0]
+        c = np.sqrt(max(0.0, 1.0 - rho * rho))
+        for t in range(1, steps):
+            q[t] = rho * q[t - 1] + c * x[t]
+        rows.append(q)
+    q = np.concatenate(rows, axis=1)
+    st, fv = _to_dtype(q.reshape(-1, wl.d), wl.dtype)
+    return st.reshape(steps, len(hs) * wl.G, wl.d), fv.reshape(steps, len(hs) * wl.G, wl.d)
 
 
 def make_appended(wl: Workload, head: int, n: int):
