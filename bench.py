@@ -52,6 +52,15 @@ def parse():
                     help="incremental workload: run each decode-time clustering on a second "
                          "stream, overlapping the next D decode steps, whose selection keeps "
                          "the window's rows pending until the new clusters are in")
+    ap.add_argument("--kv-host", choices=("direct", "cache"), default=None,
+                    help="K/V in pinned host memory: attention reads the selected rows from "
+                         "there (direct) or through the cluster-granular cache of the rows "
+                         "selected in the last R steps (cache)")
+    ap.add_argument("--cache-steps", type=int, default=1, metavar="R",
+                    help="steps a selected row stays cached (--kv-host cache)")
+    ap.add_argument("--query-rho", type=float, default=None,
+                    help="step-to-step correlation of an AR(1) query stream (default: "
+                         "independent queries; 0.9 with --kv-host)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times and "
                          "exit: the kernel of known traffic that scales the HBM byte counters")
@@ -102,7 +111,8 @@ class Case:
     after the fork. Without `side` the increment runs on the decode stream at
     the fork point, which gives the same results in sequence."""
 
-    def __init__(self, wl, T, dev, fused=True, lag=0, side=None):
+    def __init__(self, wl, T, dev, fused=True, lag=0, side=None, kv_host=None, cache_R=1,
+                 rho=None):
         import numpy as np
         import torch
 
@@ -115,7 +125,10 @@ class Case:
         self.n_ev = T // wl.m_every if self.inc else 0
         Lcap = L + T if self.inc else L
         K, V, _ = synth.make_kv(wl, L=L, L_cap=Lcap)
-        Q, _ = synth.make_query_steps(wl, T)
+        if rho is None:
+            Q, _ = synth.make_query_steps(wl, T)
+        else:
+            Q, _ = synth.make_query_stream(wl, T, rho)
 
         def bf(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
@@ -161,6 +174,24 @@ class Case:
             self.asg_w = torch.empty((H, m), **i32)
         self.ck = ck
         self.set_lag(lag, side)
+        # K/V in pinned host memory: attention reads the selected rows from
+        # there directly, or through the cluster-granular cache
+        self.kv_host = kv_host
+        if kv_host is not None:
+            assert not self.inc, "host-resident K/V is measured on the prompt workloads"
+            self.Kh = torch.empty(self.K.shape, dtype=self.K.dtype, pin_memory=True)
+            self.Vh = torch.empty(self.V.shape, dtype=self.V.dtype, pin_memory=True)
+            self.Kh.copy_(self.K.cpu())
+            self.Vh.copy_(self.V.cpu())
+            self.stats_acc = torch.zeros((H, 5), dtype=torch.int64, device=dev)
+            self.count_stats = False      # summing the statistics is bookkeeping: eager only
+            if kv_host == "cache":
+                self.cdesc = ck.cache_desc(self.Kh, self.asg, self.off, self.tok, C, B, cache_R,
+                                           n_sink=wl.n_sink)
+                self.cst = ck.cache_state(self.cdesc, dev)
+                ad_c = ck.AttnDesc(H=H, G=G, d=d, B=B, kv_head_stride=self.cst["rows"] * d,
+                                   kv_rows=self.cst["rows"], scale=0.0, dtype=ck.CKV_BF16)
+                self.ws_ac = torch.empty(ck.ckv_attn_workspace(ad_c), **u8)
 
     def set_lag(self, lag, side):
         if lag or side is not None:
@@ -205,8 +236,33 @@ class Case:
                                 idx=self.idx[t], n_sel=self.nsel[t], out=self.O[t],
                                 workspace=self.ws_f)
 
+    def host_step(self, t):
+        """Selection, then attention over host-resident K/V: read directly,
+        or through the cache of the rows selected in the last R steps."""
+        self.select(t)
+        if self.kv_host == "direct":
+            self.ck.ckv_sparse_attn(self.Q[t], self.Kh, self.Vh, self.idx[t], self.nsel[t],
+                                    out=self.O[t], workspace=self.ws_a)
+            return
+        st = self.cst
+        cK, cV = self.ck.ckv_cache_step(self.cdesc, t, self.idx[t], self.nsel[t], self.asg,
+                                        self.off, self.tok, self.Kh, self.Vh, st)
+        self.ck.ckv_sparse_attn(self.Q[t], cK, cV, st["idx_cache"], self.nsel[t],
+                                kv_rows=st["rows"], out=self.O[t], workspace=self.ws_ac)
+        if self.count_stats:
+            self.stats_acc.add_(st["stats"])
+
     def steps(self, a, b):
         """Decode steps a .. b - 1 (0-based), without increments."""
+        if self.kv_host is not None:
+            if a == 0:
+                if self.count_stats:
+                    self.stats_acc.zero_()
+                if self.kv_host == "cache":
+                    self.cst["ring"].zero_()
+            for t in range(a, b):
+                self.host_step(t)
+            return
         for t in range(a, b):
             if self.inc:
                 self.append(t)
@@ -296,8 +352,9 @@ class Case:
         return replay
 
     def snapshot(self):
+        extra = [] if self.kv_host is None else [self.stats_acc]
         return [x.clone() for x in (self.cent, self.asg, self.off, self.tok, self.idx,
-                                    self.nsel, self.O)]
+                                    self.nsel, self.O, *extra)]
 
 
 def capture(fn):
@@ -471,13 +528,48 @@ def main():
     lag, side = 0, None
     if args.async_cluster is not None:
         lag, side = args.async_cluster, torch.cuda.Stream(device=dev)
-    case = Case(wl, T, dev, fused=not args.separate, lag=lag, side=side)
+    rho = args.query_rho
+    if args.kv_host is not None and rho is None:
+        rho = 0.9
+    case = Case(wl, T, dev, fused=not args.separate, lag=lag, side=side, kv_host=args.kv_host,
+                cache_R=args.cache_steps, rho=rho)
 
     # eager reference run
     case.cluster()
+    if case.kv_host is not None:
+        case.count_stats = True
     case.decode()
     torch.cuda.synchronize()
     ref = case.snapshot()
+    if case.kv_host is not None:
+        case.count_stats = False
+    kv_host = None
+    if case.kv_host is not None:
+        # the same queries on the device-resident path give the same outputs
+        mode, case.kv_host = case.kv_host, None
+        case.decode()
+        torch.cuda.synchronize()
+        assert torch.equal(case.O, ref[6]) and torch.equal(case.idx, ref[4]), \
+            "host-resident decode differs from the device-resident one"
+        case.kv_host = mode
+        log(f"host-resident ({mode}) decode matches the device-resident decode bitwise")
+        acc = ref[7].cpu()
+        n_sel_rows = int(ref[5].cpu().to(torch.int64).sum())
+        row_bytes = 2 * wl.d * 2                      # one K row and one V row, bf16
+        if mode == "direct":
+            host_rows = n_sel_rows
+        else:
+            host_rows = int(acc[:, 1].sum()) + wl.H * wl.n_sink   # + the sinks, once
+        hit = int(acc[:, 0].sum())
+        kv_host = {"mode": mode, "query_rho": rho,
+                   "host_bytes_per_step": round(host_rows * row_bytes / T),
+                   "selected_rows_per_step": round(n_sel_rows / T, 1)}
+        if mode == "cache":
+            kv_host.update({
+                "R": args.cache_steps,
+                "cluster_rows_from_cache": round(hit / max(1, hit + int(acc[:, 1].sum())), 4),
+                "clusters_whole_in_cache": round(int(acc[:, 2].sum()) /
+                                                 max(1, int(acc[:, 3].sum())), 4)})
 
     # graphs: the clustering call and the whole decode loop (with side-stream
     # increments: linear graphs joined by events)
@@ -521,6 +613,12 @@ def main():
     cl_ms = sum(ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(args.steps)) / args.steps
     dec_ms = sum(ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(args.steps)) / args.steps
     dec_us = dec_ms * 1e3 / T
+    if kv_host is not None:
+        kv_host["host_GB/s_over_step"] = round(kv_host["host_bytes_per_step"] / dec_us / 1e3, 2)
+        log(f"host-resident {kv_host['mode']}: {kv_host['host_bytes_per_step']} host bytes per "
+            f"step ({kv_host['host_GB/s_over_step']} GB/s over the step)"
+            + (f", {kv_host['cluster_rows_from_cache']:.3f} of cluster rows from the cache"
+               if kv_host["mode"] == "cache" else ""))
     log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): cluster {cl_ms:.3f} ms, "
         f"decode {dec_us:.2f} us/step")
 
@@ -634,7 +732,12 @@ def main():
                                  "p99": round(pct(cl_reps, 99), 4)},
         "decode_us_per_step": round(dec_us, 3),
         "decode_cold_us_per_step": round(cold_us, 3),
-        "decode_path": "ckv_select + ckv_sparse_attn" if args.separate else "ckv_select_attn",
+        "decode_path": ("ckv_select + ckv_sparse_attn over host K/V" if args.kv_host == "direct"
+                        else "ckv_select + ckv_cache_step + ckv_sparse_attn over the cache"
+                        if args.kv_host == "cache"
+                        else "ckv_select + ckv_sparse_attn" if args.separate
+                        else "ckv_select_attn"),
+        **({"kv_host": kv_host} if kv_host else {}),
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": cpu,

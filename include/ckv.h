@@ -241,6 +241,86 @@ int ckv_select_attn(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc, co
                     int32_t *n_sel, float *o, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* --------------------------------------------------------------- cache --
+ * Cluster-granular GPU cache of selected KV rows, for KV kept in host memory
+ * [Caching the KV of selected tokens; system overview, Fig. 5]: the GPU keeps
+ * the rows selected in the last R decode steps, and at each step only the
+ * selected rows not in that cache are read from host memory.
+ *
+ * Contents after step s: exactly the rows selected in steps s-R+1 .. s.
+ * Layout of a head's rows (a function of the ring below): slots
+ * 0 .. n_sink-1 hold sink tokens 0 .. n_sink-1; then the clusters in
+ * ascending id, cluster c holding the first N_c tokens of its CSR segment,
+ * N_c = the largest number of c's rows any of those steps selected (a
+ * selection takes a prefix of every admitted cluster).
+ *
+ * State (caller-owned device memory, kept between steps):
+ *   ring      int32 [H][c_cap][R]: rows of every cluster selected in each of
+ *             the last R steps (slot s % R); zero it before step 0.
+ *   cache_K, cache_V  dtype [2][H][rows][d], rows = ckv_cache_rows(desc) =
+ *             n_sink + R * (B - n_sink): step s writes buffer s & 1 from
+ *             buffer (s - 1) & 1 and from K_src / V_src.
+ *   cache_tok int32 [2][H][rows]: token id of every slot of either buffer
+ *             (-1 for unused slots).
+ * Steps must be numbered 0, 1, 2, ... for one sequence (step 0 loads the
+ * sinks); R and the layout inputs stay fixed across its steps.
+ *
+ * Inputs of a step: this step's ckv_select output idx [H][B], n_sel [H];
+ * the labels assign [H][L] of ckv_cluster (token id t is row t - token_base)
+ * and the CSR csr_offsets [H][c_cap+1], csr_tokens [H][t_cap] the selection
+ * used; K_src, V_src: every head's K and V, row t of head h at
+ * (h * kv_head_stride + t * d), either device memory or pinned host memory
+ * (hipHostMalloc; read through its device mapping). Any other pointer is
+ * CKV_ERR_INVALID_ARG.
+ *
+ * Outputs: idx_cache int32 [H][B]: the slot of every selected entry in
+ * buffer step & 1 (-1 past n_sel, and for entries that are neither a sink
+ * nor a clustered row, such as pending decode rows, which the cache does not
+ * hold); stats int32 [H][5]: cluster rows found in the cache, cluster rows
+ * read from K_src/V_src, selected clusters found whole in the cache,
+ * selected clusters, selected entries without a slot. ckv_sparse_attn with
+ * K, V = buffer step & 1 (kv_head_stride rows * d, kv_rows = rows) and idx =
+ * idx_cache then gives the attention of the step, bitwise equal to the one
+ * over K_src/V_src with idx (same rows, same order).
+ *
+ * Workspace: ckv_cache_workspace() bytes. Two launches on `stream`.
+ */
+typedef struct {
+    int32_t H;              /* KV heads, >= 1 */
+    int32_t d;              /* must be 128 */
+    int32_t C;              /* clusters in use, 1 <= C <= min(c_cap, 2048) */
+    int32_t c_cap;          /* cluster slots per head (CSR and ring stride) */
+    int32_t n_sink;         /* sink tokens, 0 <= n_sink <= B */
+    int32_t B;              /* selection budget (idx row stride) */
+    int32_t R;              /* steps a selected row stays cached, 1 .. 8 */
+    int32_t dtype;          /* ckv_dtype of K_src, V_src and the cache */
+    int64_t L;              /* rows of assign per head */
+    int64_t token_base;     /* token id of assign row 0, >= 0 */
+    int64_t t_cap;          /* CSR token slots per head */
+    int64_t kv_head_stride; /* elements between heads of K_src / V_src */
+    int64_t kv_rows;        /* rows per head of K_src / V_src */
+} ckv_cache_desc;
+
+/* Cache rows per head and buffer, n_sink + R * (B - n_sink) (0 if invalid). */
+int64_t ckv_cache_rows(const ckv_cache_desc *desc);
+
+/* Bytes of workspace ckv_cache_step needs (0 if desc is invalid). */
+size_t ckv_cache_workspace(const ckv_cache_desc *desc);
+
+int ckv_cache_step(const ckv_cache_desc *desc, int64_t step, const int32_t *idx,
+                   const int32_t *n_sel, const int32_t *assign, const int32_t *csr_offsets,
+                   const int32_t *csr_tokens, const void *K_src, const void *V_src,
+                   int32_t *ring, void *cache_K, void *cache_V, int32_t *cache_tok,
+                   int32_t *idx_cache, int32_t *stats, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/* The address at which the library's kernels read `ptr`: itself for device
+ * memory, the device mapping for pinned host memory (hipHostMalloc); any
+ * other pointer is CKV_ERR_INVALID_ARG. Lets a caller hand host-resident K/V
+ * to ckv_sparse_attn directly (every selected row read over the host link,
+ * the no-cache baseline of the cache). */
+int ckv_device_view(const void *ptr, const void **device_ptr);
+
 #ifdef __cplusplus
 }
 #endif

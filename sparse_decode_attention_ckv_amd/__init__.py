@@ -26,6 +26,8 @@ __all__ = [
     "AttnDesc", "ckv_cluster", "ckv_select", "ckv_sparse_attn",
     "ckv_cluster_workspace", "ckv_select_workspace", "ckv_attn_workspace",
     "ckv_status_string", "ckv_abi_version", "ckv_select_attn", "ckv_select_attn_workspace",
+    "ckv_cache_rows", "ckv_cache_workspace", "ckv_cache_step", "ckv_device_view",
+    "CacheDesc", "cache_desc", "cache_state",
 ]
 
 CKV_OK, CKV_ERR_INVALID_ARG, CKV_ERR_UNSUPPORTED, CKV_ERR_WORKSPACE, CKV_ERR_LAUNCH = range(5)
@@ -64,6 +66,13 @@ class AttnDesc(ct.Structure):
                 ("scale", ct.c_float), ("dtype", ct.c_int32)]
 
 
+class CacheDesc(ct.Structure):
+    _fields_ = [("H", ct.c_int32), ("d", ct.c_int32), ("C", ct.c_int32), ("c_cap", ct.c_int32),
+                ("n_sink", ct.c_int32), ("B", ct.c_int32), ("R", ct.c_int32),
+                ("dtype", ct.c_int32), ("L", ct.c_int64), ("token_base", ct.c_int64),
+                ("t_cap", ct.c_int64), ("kv_head_stride", ct.c_int64), ("kv_rows", ct.c_int64)]
+
+
 _P = ct.c_void_p
 _SIGS = {
     "ckv_status_string": (ct.c_char_p, [ct.c_int]),
@@ -77,6 +86,11 @@ _SIGS = {
     "ckv_select_attn_workspace": (ct.c_size_t, [ct.POINTER(SelectDesc), ct.POINTER(AttnDesc)]),
     "ckv_select_attn": (ct.c_int, [ct.POINTER(SelectDesc), ct.POINTER(AttnDesc), _P, _P, _P, _P,
                                    _P, _P, _P, _P, _P, _P, ct.c_size_t, _P]),
+    "ckv_cache_rows": (ct.c_int64, [ct.POINTER(CacheDesc)]),
+    "ckv_cache_workspace": (ct.c_size_t, [ct.POINTER(CacheDesc)]),
+    "ckv_cache_step": (ct.c_int, [ct.POINTER(CacheDesc), ct.c_int64, _P, _P, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _P, _P, ct.c_size_t, _P]),
+    "ckv_device_view": (ct.c_int, [_P, ct.POINTER(ct.c_void_p)]),
 }
 
 
@@ -258,13 +272,26 @@ def ckv_select(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch.Tens
     return idx, n_sel
 
 
+def ckv_device_view(t: torch.Tensor) -> int:
+    """Device address of a device tensor or of a pinned host tensor (its
+    device mapping); raises for pageable host memory."""
+    out = ct.c_void_p()
+    _check(load().ckv_device_view(ct.c_void_p(t.data_ptr()), ct.byref(out)), "ckv_device_view")
+    return out.value
+
+
+def _kv_ptr(t: torch.Tensor):
+    return ct.c_void_p(t.data_ptr() if t.is_cuda else ckv_device_view(t))
+
+
 def ckv_sparse_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,
                     n_sel: torch.Tensor, *, kv_rows: Optional[int] = None, scale: float = 0.0,
                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                     stream=None):
     """softmax(q K_S^T * scale) V_S over rows idx[g][:n_sel[g]] of KV head g.
 
-    q [H*G][d]; K, V [H][rows][d] (same strides); idx [H][B]; returns
+    q [H*G][d]; K, V [H][rows][d] (same strides; device tensors, or pinned
+    host tensors read through their device mapping); idx [H][B]; returns
     o [H*G][d] fp32."""
     lib = load()
     hs = _rows(K, "K")
@@ -286,10 +313,74 @@ def ckv_sparse_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torc
                     dtype=_dtype_code(K))
     nb = lib.ckv_attn_workspace(ct.byref(desc))
     ws = _workspace(nb, q.device, workspace)
-    _check(lib.ckv_sparse_attn(ct.byref(desc), _ptr(q), _ptr(K), _ptr(V), _ptr(idx),
+    _check(lib.ckv_sparse_attn(ct.byref(desc), _ptr(q), _kv_ptr(K), _kv_ptr(V), _ptr(idx),
                                _ptr(n_sel), _ptr(out), _ptr(ws), nb, _stream(stream)),
            "ckv_sparse_attn")
     return out
+
+
+# ------------------------------------------------------------------ cache --
+
+def ckv_cache_rows(desc: CacheDesc) -> int:
+    return load().ckv_cache_rows(ct.byref(desc))
+
+
+def ckv_cache_workspace(desc: CacheDesc) -> int:
+    return load().ckv_cache_workspace(ct.byref(desc))
+
+
+def cache_desc(K_src: torch.Tensor, assign: torch.Tensor, csr_offsets: torch.Tensor,
+               csr_tokens: torch.Tensor, C: int, B: int, R: int, *, n_sink: int = 16,
+               token_base: int = 0) -> CacheDesc:
+    """Descriptor of a cache over K_src [H][rows][d] (device or pinned host)
+    for selections of budget B over the CSR and labels of ckv_cluster."""
+    hs = _rows(K_src, "K_src")
+    H, rows, d = K_src.shape
+    return CacheDesc(H=H, d=d, C=C, c_cap=csr_offsets.shape[1] - 1, n_sink=n_sink, B=B, R=R,
+                     dtype=_dtype_code(K_src), L=assign.shape[1], token_base=token_base,
+                     t_cap=csr_tokens.shape[1], kv_head_stride=hs, kv_rows=rows)
+
+
+def cache_state(desc: CacheDesc, device) -> dict:
+    """Zeroed state and output buffers of a cache: ring, the two row buffers
+    of K and V, slot tokens, idx_cache, stats and the workspace."""
+    rows = ckv_cache_rows(desc)
+    _need(rows > 0, "invalid cache descriptor")
+    dt = torch.bfloat16 if desc.dtype == CKV_BF16 else torch.float32
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(
+        rows=rows,
+        ring=torch.zeros((desc.H, desc.c_cap, desc.R), **i32),
+        cache_K=torch.zeros((2, desc.H, rows, desc.d), dtype=dt, device=device),
+        cache_V=torch.zeros((2, desc.H, rows, desc.d), dtype=dt, device=device),
+        cache_tok=torch.full((2, desc.H, rows), -1, **i32),
+        idx_cache=torch.full((desc.H, desc.B), -1, **i32),
+        stats=torch.zeros((desc.H, 5), **i32),
+        workspace=torch.empty(max(ckv_cache_workspace(desc), 1), dtype=torch.uint8,
+                              device=device))
+
+
+def ckv_cache_step(desc: CacheDesc, step: int, idx: torch.Tensor, n_sel: torch.Tensor,
+                   assign: torch.Tensor, csr_offsets: torch.Tensor, csr_tokens: torch.Tensor,
+                   K_src: torch.Tensor, V_src: torch.Tensor, state: dict, stream=None):
+    """One decode step of the cache: buffer step & 1 of state["cache_K"] /
+    ["cache_V"] then holds the rows selected in the last R steps and
+    state["idx_cache"] the slots of this step's selection. Returns the
+    (K, V) views of that buffer."""
+    for t, n in ((idx, "idx"), (n_sel, "n_sel"), (assign, "assign"), (csr_offsets, "csr_offsets"),
+                 (csr_tokens, "csr_tokens")):
+        _need(t.dtype == torch.int32 and t.is_contiguous() and t.is_cuda, f"bad {n}")
+    _need(idx.shape == (desc.H, desc.B) and assign.shape == (desc.H, desc.L), "bad idx or assign")
+    _need(V_src.shape == K_src.shape and V_src.stride() == K_src.stride(), "V_src must match K_src")
+    ws = state["workspace"]
+    _check(load().ckv_cache_step(
+        ct.byref(desc), step, _ptr(idx), _ptr(n_sel), _ptr(assign), _ptr(csr_offsets),
+        _ptr(csr_tokens), ct.c_void_p(K_src.data_ptr()), ct.c_void_p(V_src.data_ptr()),
+        _ptr(state["ring"]), _ptr(state["cache_K"]), _ptr(state["cache_V"]),
+        _ptr(state["cache_tok"]), _ptr(state["idx_cache"]), _ptr(state["stats"]), _ptr(ws),
+        ws.numel(), _stream(stream)), "ckv_cache_step")
+    b = step & 1
+    return state["cache_K"][b], state["cache_V"][b]
 
 
 def ckv_select_attn(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch.Tensor,

@@ -180,6 +180,76 @@ bool stride_ok(int64_t elems, int32_t dtype) {
     return ((elems * (dtype == CKV_BF16 ? 2 : 4)) & 15) == 0;
 }
 
+int check_cache(const ckv_cache_desc *d) {
+    if (!d) return CKV_ERR_INVALID_ARG;
+    if (d->H < 1 || !dtype_ok(d->dtype)) return CKV_ERR_INVALID_ARG;
+    if (d->d != kD) return d->d < 1 ? CKV_ERR_INVALID_ARG : CKV_ERR_UNSUPPORTED;
+    if (d->H > kMaxHeads) return CKV_ERR_UNSUPPORTED;
+    if (d->C < 1 || d->c_cap < d->C) return CKV_ERR_INVALID_ARG;
+    if (d->C > kMaxC) return CKV_ERR_UNSUPPORTED;
+    if (d->n_sink < 0 || d->B < 1 || d->B < d->n_sink) return CKV_ERR_INVALID_ARG;
+    if (d->R < 1) return CKV_ERR_INVALID_ARG;
+    if (d->R > kMaxCacheR) return CKV_ERR_UNSUPPORTED;
+    if (d->L < 1 || d->token_base < 0 || d->t_cap < 1 || d->t_cap > INT32_MAX)
+        return CKV_ERR_INVALID_ARG;
+    if (d->kv_rows < 1 || d->kv_rows > INT32_MAX || d->kv_head_stride < d->kv_rows * kD)
+        return CKV_ERR_INVALID_ARG;
+    const int64_t rows = (int64_t)d->n_sink + (int64_t)d->R * (d->B - d->n_sink);
+    if (rows < 1 || rows > INT32_MAX / 2) return CKV_ERR_UNSUPPORTED;
+    return CKV_OK;
+}
+
+int64_t cache_rows(const ckv_cache_desc *d) {
+    return (int64_t)d->n_sink + (int64_t)d->R * (d->B - d->n_sink);
+}
+
+size_t cache_bytes(const ckv_cache_desc *d) {
+    return align_up((size_t)d->H * cache_rows(d) * sizeof(int32_t)) +
+           align_up((size_t)d->H * sizeof(int32_t));
+}
+
+void plan_cache(const ckv_cache_desc *d, CachePlan *p, void *ws) {
+    p->H = d->H;
+    p->C = d->C;
+    p->c_cap = d->c_cap;
+    p->n_sink = d->n_sink;
+    p->B = d->B;
+    p->R = d->R;
+    p->dtype = d->dtype;
+    p->rows = (int)cache_rows(d);
+    p->L = d->L;
+    p->token_base = d->token_base;
+    p->t_cap = d->t_cap;
+    p->kv_head_stride = d->kv_head_stride;
+    p->kv_rows = d->kv_rows;
+    p->src = (int32_t *)ws;
+    p->tot = (int32_t *)((char *)ws + align_up((size_t)d->H * p->rows * sizeof(int32_t)));
+}
+
+// The address at which a kernel reads `p`: device memory as is, pinned host
+// memory (hipHostMalloc) through its device mapping. Anything else (pageable
+// host memory, unknown pointers) is refused, so no kernel is handed an
+// address it cannot read.
+int device_view(const void *p, const void **out) {
+    if (!p) return CKV_ERR_INVALID_ARG;
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return CKV_ERR_INVALID_ARG;
+    }
+    if (a.type == hipMemoryTypeDevice) {
+        *out = p;
+        return CKV_OK;
+    }
+    if (a.type == hipMemoryTypeHost && a.devicePointer) {
+        const char *hb = (const char *)a.hostPointer;
+        const char *db = (const char *)a.devicePointer;
+        *out = (hb && (const char *)p >= hb) ? db + ((const char *)p - hb) : db;
+        return CKV_OK;
+    }
+    return CKV_ERR_INVALID_ARG;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +365,46 @@ int ckv_select_attn(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc, co
     plan_attn(adesc, &ap, (char *)workspace + sb);
     return launch_status(launch_select_attn(sp, ap, q, centroids, csr_offsets, csr_tokens, K, V,
                                             idx, n_sel, o, (hipStream_t)stream));
+}
+
+int ckv_device_view(const void *ptr, const void **device_ptr) {
+    if (!device_ptr) return CKV_ERR_INVALID_ARG;
+    return device_view(ptr, device_ptr);
+}
+
+int64_t ckv_cache_rows(const ckv_cache_desc *desc) {
+    return check_cache(desc) == CKV_OK ? cache_rows(desc) : 0;
+}
+
+size_t ckv_cache_workspace(const ckv_cache_desc *desc) {
+    return check_cache(desc) == CKV_OK ? cache_bytes(desc) : 0;
+}
+
+int ckv_cache_step(const ckv_cache_desc *desc, int64_t step, const int32_t *idx,
+                   const int32_t *n_sel, const int32_t *assign, const int32_t *csr_offsets,
+                   const int32_t *csr_tokens, const void *K_src, const void *V_src,
+                   int32_t *ring, void *cache_K, void *cache_V, int32_t *cache_tok,
+                   int32_t *idx_cache, int32_t *stats, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    const int st = check_cache(desc);
+    if (st != CKV_OK) return st;
+    if (step < 0) return CKV_ERR_INVALID_ARG;
+    if (!idx || !n_sel || !assign || !csr_offsets || !csr_tokens || !ring || !cache_K ||
+        !cache_V || !cache_tok || !idx_cache || !stats)
+        return CKV_ERR_INVALID_ARG;
+    if (!aligned16(cache_K) || !aligned16(cache_V) ||
+        !stride_ok(desc->kv_head_stride, desc->dtype))
+        return CKV_ERR_INVALID_ARG;
+    const void *Kd = nullptr, *Vd = nullptr;
+    if (device_view(K_src, &Kd) != CKV_OK || device_view(V_src, &Vd) != CKV_OK)
+        return CKV_ERR_INVALID_ARG;
+    if (!aligned16(Kd) || !aligned16(Vd)) return CKV_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < cache_bytes(desc)) return CKV_ERR_WORKSPACE;
+    CachePlan p;
+    plan_cache(desc, &p, workspace);
+    return launch_status(launch_cache_step(p, step, idx, n_sel, assign, csr_offsets, csr_tokens,
+                                           Kd, Vd, ring, cache_K, cache_V, cache_tok, idx_cache,
+                                           stats, (hipStream_t)stream));
 }
 
 }  // extern "C"

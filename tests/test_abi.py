@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 def test_struct_layout_matches_header(tmp_path):
     structs = {"ckv_cluster_desc": ck.ClusterDesc, "ckv_select_desc": ck.SelectDesc,
-               "ckv_attn_desc": ck.AttnDesc}
+               "ckv_attn_desc": ck.AttnDesc, "ckv_cache_desc": ck.CacheDesc}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ckv.h"', "int main(void){"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -217,3 +217,52 @@ def test_select_attn_checks():
     # each descriptor is also checked on its own
     assert lib.ckv_select_attn(ct.byref(_sel(d=64)), ct.byref(_att(d=64)), *args, FAKE, need,
                                None) == ck.CKV_ERR_UNSUPPORTED
+
+
+def _cache(**kw):
+    base = dict(H=2, d=128, C=25, c_cap=30, n_sink=16, B=256, R=2, dtype=1, L=2064,
+                token_base=0, t_cap=2048, kv_head_stride=2064 * 128, kv_rows=2064)
+    base.update(kw)
+    return ck.CacheDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), ck.CKV_ERR_UNSUPPORTED),
+    (dict(C=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(C=31), ck.CKV_ERR_INVALID_ARG),                     # C > c_cap
+    (dict(C=2049, c_cap=2049), ck.CKV_ERR_UNSUPPORTED),
+    (dict(R=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(R=9), ck.CKV_ERR_UNSUPPORTED),
+    (dict(B=8), ck.CKV_ERR_INVALID_ARG),                      # B < n_sink
+    (dict(n_sink=-1), ck.CKV_ERR_INVALID_ARG),
+    (dict(kv_head_stride=2064 * 128 - 1), ck.CKV_ERR_INVALID_ARG),
+    (dict(kv_rows=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(t_cap=0), ck.CKV_ERR_INVALID_ARG),
+    (dict(token_base=-1), ck.CKV_ERR_INVALID_ARG),
+    (dict(dtype=5), ck.CKV_ERR_INVALID_ARG),
+    (dict(H=0), ck.CKV_ERR_INVALID_ARG),
+])
+def test_cache_rejects_bad_descriptors(kw, status):
+    d = _cache(**kw)
+    lib = ck.load()
+    assert lib.ckv_cache_rows(ct.byref(d)) == 0
+    assert lib.ckv_cache_workspace(ct.byref(d)) == 0
+    assert lib.ckv_cache_step(ct.byref(d), 0, *([FAKE] * 13), None, 0, None) == status
+
+
+def test_cache_sizes_and_pointer_checks():
+    d = _cache()
+    lib = ck.load()
+    rows = lib.ckv_cache_rows(ct.byref(d))
+    assert rows == 16 + 2 * (256 - 16)
+    ws = lib.ckv_cache_workspace(ct.byref(d))
+    assert ws >= 2 * rows * 4 + 2 * 4
+    ptrs = [FAKE] * 13
+    for i in range(13):
+        if i in (5, 6):          # K_src / V_src are checked by the device-view step
+            continue
+        bad = list(ptrs)
+        bad[i] = None
+        assert lib.ckv_cache_step(ct.byref(d), 0, *bad, FAKE, ws, None) == ck.CKV_ERR_INVALID_ARG
+    assert lib.ckv_cache_step(ct.byref(d), -1, *ptrs, FAKE, ws, None) == ck.CKV_ERR_INVALID_ARG
+    assert lib.ckv_device_view(FAKE, None) == ck.CKV_ERR_INVALID_ARG
