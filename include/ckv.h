@@ -291,7 +291,7 @@ typedef struct {
     int32_t C;              /* clusters in use, 1 <= C <= min(c_cap, 2048) */
     int32_t c_cap;          /* cluster slots per head (CSR and ring stride) */
     int32_t n_sink;         /* sink tokens, 0 <= n_sink <= B */
-    int32_t B;              /* selection budget (idx row stride) */
+    int32_t B;              /* selection budget (idx row stride), <= 4096 */
     int32_t R;              /* steps a selected row stays cached, 1 .. 8 */
     int32_t dtype;          /* ckv_dtype of K_src, V_src and the cache */
     int64_t L;              /* rows of assign per head */

@@ -189,7 +189,7 @@ int check_cache(const ckv_cache_desc *d) {
     if (d->C > kMaxC) return CKV_ERR_UNSUPPORTED;
     if (d->n_sink < 0 || d->B < 1 || d->B < d->n_sink) return CKV_ERR_INVALID_ARG;
     if (d->R < 1) return CKV_ERR_INVALID_ARG;
-    if (d->R > kMaxCacheR) return CKV_ERR_UNSUPPORTED;
+    if (d->R > kMaxCacheR || d->B > kMaxCacheB) return CKV_ERR_UNSUPPORTED;
     if (d->L < 1 || d->token_base < 0 || d->t_cap < 1 || d->t_cap > INT32_MAX)
         return CKV_ERR_INVALID_ARG;
     if (d->kv_rows < 1 || d->kv_rows > INT32_MAX || d->kv_head_stride < d->kv_rows * kD)

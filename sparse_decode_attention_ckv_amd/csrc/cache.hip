@@ -19,7 +19,7 @@
 // Two launches per step:
 //  * k_cache_plan, one 1024-thread workgroup per head: the step's row count
 //    of every cluster (from the labels of its idx entries), the ring update,
-//    old and new layouts (two block scans), the slot of every selected entry
+//    old and new layouts (one paired block scan), the slot of every selected entry
 //    (idx_cache), where every new slot comes from, its token id, and the
 //    hit/load statistics;
 //  * k_cache_fill: a gather of the new buffer, 16-byte chunks, every row's
@@ -30,6 +30,7 @@
 namespace ckv {
 
 constexpr int kCacheThreads = 1024;
+constexpr int kCacheEPT = kMaxCacheB / kCacheThreads;   // idx entries per thread
 constexpr int kFillRows = 64;            // rows per fill workgroup
 
 // label of selected token `tok` (cluster id, or -1 for a token outside the
@@ -42,16 +43,39 @@ __device__ __forceinline__ int cache_label(int32_t tok, const int32_t *as, int64
     return (lab >= 0 && lab < C) ? lab : -1;
 }
 
-// exclusive scan of a[0 .. C) (C <= 2 * blockDim) into out, plus `base`;
-// returns the total. Every thread calls it.
-__device__ int cache_scan2(const int *a, int *out, int C, int base, int *wsum) {
+// Exclusive scans of a[0 .. C) and b[0 .. C) together (C <= 2 * blockDim),
+// each plus `base`, into oa and ob; one pair of barriers for both. Returns
+// the total of b. wsum: 2 * 16 ints of LDS. Every thread calls it.
+__device__ int cache_scan_pair(const int *a, const int *b, int *oa, int *ob, int C, int base,
+                               int *wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int c0 = 2 * threadIdx.x, c1 = c0 + 1;
-    const int v0 = c0 < C ? a[c0] : 0, v1 = c1 < C ? a[c1] : 0;
-    int total;
-    const int ex = block_excl_scan(v0 + v1, wsum, &total);
-    if (c0 < C) out[c0] = base + ex;
-    if (c1 < C) out[c1] = base + ex + v0;
-    return total;
+    const int a0 = c0 < C ? a[c0] : 0, a1 = c1 < C ? a[c1] : 0;
+    const int b0 = c0 < C ? b[c0] : 0, b1 = c1 < C ? b[c1] : 0;
+    const int xa = wave_incl_scan(a0 + a1), xb = wave_incl_scan(b0 + b1);
+    if (lane == 63) {
+        wsum[wave] = xa;
+        wsum[16 + wave] = xb;
+    }
+    __syncthreads();
+    int pa = 0, pb = 0, tb = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int ta = wsum[w], t2 = wsum[16 + w];
+        pa += w < wave ? ta : 0;
+        pb += w < wave ? t2 : 0;
+        tb += t2;
+    }
+    const int ea = base + pa + xa - (a0 + a1), eb = base + pb + xb - (b0 + b1);
+    if (c0 < C) {
+        oa[c0] = ea;
+        ob[c0] = eb;
+    }
+    if (c1 < C) {
+        oa[c1] = ea + a0;
+        ob[c1] = eb + b0;
+    }
+    __syncthreads();
+    return tb;
 }
 
 __global__ __launch_bounds__(kCacheThreads) void k_cache_plan(
@@ -62,8 +86,10 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_plan(
     int rows, int32_t *__restrict__ cache_tok, int32_t *__restrict__ idx_cache,
     int32_t *__restrict__ stats, int32_t *__restrict__ src, int32_t *__restrict__ tot) {
     __shared__ int sn[kMaxC], sm[kMaxC], sN[kMaxC], sfirst[kMaxC], sold[kMaxC], snew[kMaxC];
-    __shared__ int wsum[17];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    __shared__ int soff[kMaxC];
+    __shared__ int wsum[32];
+    __shared__ int sstat[5];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     constexpr int T = kCacheThreads;
     const int32_t *ix = idx + (int64_t)h * B;
     const int32_t *as = assign + (int64_t)h * L;
@@ -74,19 +100,31 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_plan(
     int ns = n_sel[h];
     ns = ns < 0 ? 0 : (ns > B ? B : ns);
 
+    // this thread's idx entries e = tid + T k: token and label, kept in
+    // registers; the CSR offsets of every cluster into LDS meanwhile
+    int32_t tok[kCacheEPT];
+    int lab[kCacheEPT];
+#pragma unroll
+    for (int k = 0; k < kCacheEPT; ++k) {
+        const int e = tid + T * k;
+        tok[k] = e < ns ? ix[e] : -1;
+    }
     for (int c = tid; c < C; c += T) {
+        soff[c] = off[c];
         sn[c] = 0;
         sfirst[c] = INT32_MAX;
     }
+    if (tid < 5) sstat[tid] = 0;
+#pragma unroll
+    for (int k = 0; k < kCacheEPT; ++k) lab[k] = cache_label(tok[k], as, L, token_base, C);
     __syncthreads();
     // this step's rows per cluster and the first idx entry of each cluster
-    for (int e = tid; e < ns; e += T) {
-        const int lab = cache_label(ix[e], as, L, token_base, C);
-        if (lab >= 0) {
-            atomicAdd(&sn[lab], 1);
-            atomicMin(&sfirst[lab], e);
+#pragma unroll
+    for (int k = 0; k < kCacheEPT; ++k)
+        if (lab[k] >= 0) {
+            atomicAdd(&sn[lab[k]], 1);
+            atomicMin(&sfirst[lab[k]], tid + T * k);
         }
-    }
     __syncthreads();
     // cached rows before (m) and after (N) this step; the ring slot of the
     // step R ago becomes this step's
@@ -109,28 +147,21 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_plan(
         csel += (n > 0);
     }
     __syncthreads();
-    const int old_total = cache_scan2(sm, sold, C, n_sink, wsum);
-    const int new_total = cache_scan2(sN, snew, C, n_sink, wsum);
-    (void)old_total;
-    int t_hit, t_load, t_chit, t_csel;
-    block_excl_scan(hit, wsum, &t_hit);
-    block_excl_scan(load, wsum, &t_load);
-    block_excl_scan(chit, wsum, &t_chit);
-    block_excl_scan(csel, wsum, &t_csel);
-    __syncthreads();   // snew, sold visible to every thread
+    const int new_total = cache_scan_pair(sm, sN, sold, snew, C, n_sink, wsum);
     const int n_slots = n_sink + new_total < rows ? n_sink + new_total : rows;
 
     // the slot of every selected entry (-1: not in the cache)
     int unplaced = 0;
-    for (int e = tid; e < B; e += T) {
+#pragma unroll
+    for (int k = 0; k < kCacheEPT; ++k) {
+        const int e = tid + T * k;
+        if (e >= B) continue;
         int v = -1;
         if (e < ns) {
-            const int32_t t = ix[e];
-            const int lab = cache_label(t, as, L, token_base, C);
-            if (lab >= 0)
-                v = snew[lab] + (e - sfirst[lab]);
-            else if (t >= 0 && t < n_sink)
-                v = t;
+            if (lab[k] >= 0)
+                v = snew[lab[k]] + (e - sfirst[lab[k]]);
+            else if (tok[k] >= 0 && tok[k] < n_sink)
+                v = tok[k];
             if (v >= n_slots) v = -1;
             unplaced += (v < 0);
         }
@@ -139,10 +170,10 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_plan(
     // where every slot of the new buffer comes from: an old slot (>= 0) or a
     // host row (-1 - token id); and the token it holds
     for (int s = tid; s < rows; s += T) {
-        int32_t tok = -1, from = INT32_MIN;
+        int32_t t = -1, from = INT32_MIN;
         if (s < n_slots) {
             if (s < n_sink) {
-                tok = s;
+                t = s;
                 from = first ? -1 - s : s;
             } else {
                 // last cluster whose first new slot is <= s (it is not empty)
@@ -152,26 +183,28 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_plan(
                     if (snew[mid] <= s) lo = mid; else hi = mid - 1;
                 }
                 const int r = s - snew[lo];
-                int64_t p = (int64_t)off[lo] + r;
+                int64_t p = (int64_t)soff[lo] + r;
                 p = p < 0 ? 0 : (p >= t_cap ? t_cap - 1 : p);
-                tok = tk[p];
-                from = r < sm[lo] ? sold[lo] + r : -1 - tok;
+                t = tk[p];
+                from = r < sm[lo] ? sold[lo] + r : -1 - t;
             }
         }
-        ctok[s] = tok;
+        ctok[s] = t;
         srch[s] = from;
     }
-    int t_unplaced;
-    block_excl_scan(unplaced, wsum, &t_unplaced);
-    if (tid == 0) {
-        int32_t *st = stats + (int64_t)h * 5;
-        st[0] = t_hit;
-        st[1] = t_load;
-        st[2] = t_chit;
-        st[3] = t_csel;
-        st[4] = t_unplaced;
-        tot[h] = n_slots;
+    // statistics: wave sums, then one LDS add per wave
+    const int v0 = wave_sum(hit), v1 = wave_sum(load), v2 = wave_sum(chit),
+              v3 = wave_sum(csel), v4 = wave_sum(unplaced);
+    if (lane == 0) {
+        atomicAdd(&sstat[0], v0);
+        atomicAdd(&sstat[1], v1);
+        atomicAdd(&sstat[2], v2);
+        atomicAdd(&sstat[3], v3);
+        atomicAdd(&sstat[4], v4);
     }
+    __syncthreads();
+    if (tid < 5) stats[(int64_t)h * 5 + tid] = sstat[tid];
+    if (tid == 0) tot[h] = n_slots;
 }
 
 // New buffer rows [64 b, 64 b + 64) of head h from the old buffer or the

@@ -240,6 +240,7 @@ hipError_t launch_select_attn(const SelectPlan &sp, const AttnPlan &ap, const vo
 
 // Cluster-granular cache of selected rows (cache.hip).
 constexpr int kMaxCacheR = 8;
+constexpr int kMaxCacheB = 4096;          // largest budget the cache plan holds in registers
 struct CachePlan {
     int H, C, c_cap, n_sink, B, R, dtype, rows;
     int64_t L, token_base, t_cap, kv_head_stride, kv_rows;

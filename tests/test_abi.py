@@ -233,6 +233,7 @@ def _cache(**kw):
     (dict(C=2049, c_cap=2049), ck.CKV_ERR_UNSUPPORTED),
     (dict(R=0), ck.CKV_ERR_INVALID_ARG),
     (dict(R=9), ck.CKV_ERR_UNSUPPORTED),
+    (dict(B=4097), ck.CKV_ERR_UNSUPPORTED),
     (dict(B=8), ck.CKV_ERR_INVALID_ARG),                      # B < n_sink
     (dict(n_sink=-1), ck.CKV_ERR_INVALID_ARG),
     (dict(kv_head_stride=2064 * 128 - 1), ck.CKV_ERR_INVALID_ARG),
