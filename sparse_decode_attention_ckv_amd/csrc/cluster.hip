@@ -275,14 +275,27 @@ __device__ __forceinline__ void as_load_b(const u32x4 *K4, int64_t Lp, int64_t t
     }
 }
 
+// Running argmax as one float max: a score's 11 low mantissa bits are
+// replaced by 2047 - (cluster id), so the larger packed value is the larger
+// score, and scores equal in their upper 13 significant bits go to the lower
+// id (kMaxC = 2048 ids fit in 11 bits). The comparison thus resolves
+// differences above 2^-13 of the score's magnitude, far below the rounding
+// of the bf16 operands themselves.
+__device__ __forceinline__ float as_pack(float score, uint32_t key) {
+    return __uint_as_float((__float_as_uint(score) & 0xFFFFF800u) | key);
+}
+__device__ __forceinline__ int as_unpack(float best) {
+    return 2047 - (int)(__float_as_uint(best) & 0x7FFu);
+}
+
 // One 16-cluster M tile (LDS rows 16m ..) against the wave's 64 tokens, then
-// the running argmax over the lane's rows c0 .. c0+3 in ascending order
-// (strict >, so the first maximum stays); MASK drops ids >= C. BIAS adds the
-// clusters' score bias (L2: -|mu|^2 / 2, from LDS) to the scores first.
+// the running packed max over the lane's rows c0 .. c0+3; MASK drops ids
+// >= C. BIAS adds the clusters' score bias (L2: -|mu|^2 / 2, from LDS) to
+// the scores first.
 template <bool MASK, bool BIAS>
 __device__ __forceinline__ void as_mtile(const u32x4 *sA, const float *sB, int m, int col,
                                          int kq, const bf16x8 (&b)[4][4], int c0, int C,
-                                         float (&best)[4], int (&bid)[4]) {
+                                         float (&best)[4]) {
     bf16x8 afr[4];
     const int r = 16 * m + col;
 #pragma unroll
@@ -303,14 +316,20 @@ __device__ __forceinline__ void as_mtile(const u32x4 *sA, const float *sB, int m
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[t][i] += bv[i];
     }
+    uint32_t key[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 4; ++i) key[i] = (uint32_t)(2047 - (c0 + i));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (acc[t][i] > best[t] && (!MASK || c0 + i < C)) {
-                best[t] = acc[t][i];
-                bid[t] = c0 + i;
-            }
+    for (int t = 0; t < 4; ++t) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = as_pack(acc[t][i], key[i]);
+            if (MASK && c0 + i >= C) p[i] = -INFINITY;
+        }
+        best[t] = fmaxf(fmaxf(best[t], p[0]), p[1]);
+        best[t] = fmaxf(fmaxf(best[t], p[2]), p[3]);
+    }
 }
 
 template <bool BIAS>
@@ -336,12 +355,8 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
         const u32x4 *M4 = (const u32x4 *)(mt + (int64_t)h * Cpad * kD);
         bf16x8 b[4][4];
         float best[4];
-        int bid[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            best[u] = -INFINITY;
-            bid[u] = 0;
-        }
+        for (int u = 0; u < 4; ++u) best[u] = -INFINITY;
         for (int r = 0; r < nr; ++r) {
             const int rb = r * kAsRound;
             const int rows = (crows - rb < kAsRound) ? crows - rb : kAsRound;
@@ -371,25 +386,17 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
             const int nm = rows / 16;
             const int cl = rb + 4 * kq;                   // lane's first row of tile 0
             for (int m = 0; m + 1 < nm; ++m)
-                as_mtile<false, BIAS>(sA, sB, m, col, kq, b, cl + 16 * m, C, best, bid);
-            as_mtile<true, BIAS>(sA, sB, nm - 1, col, kq, b, cl + 16 * (nm - 1), C, best, bid);
+                as_mtile<false, BIAS>(sA, sB, m, col, kq, b, cl + 16 * m, C, best);
+            as_mtile<true, BIAS>(sA, sB, nm - 1, col, kq, b, cl + 16 * (nm - 1), C, best);
         }
         // merge the four row groups (lanes l, l^16, l^32, l^48) of each token
         int res[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             float bb = best[u];
-            int id = bid[u];
-#pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) {
-                const float ob = __shfl_xor(bb, off);
-                const int oid = __shfl_xor(id, off);
-                if (ob > bb || (ob == bb && oid < id)) {
-                    bb = ob;
-                    id = oid;
-                }
-            }
-            res[u] = id;
+            bb = fmaxf(bb, __shfl_xor(bb, 16));
+            bb = fmaxf(bb, __shfl_xor(bb, 32));
+            res[u] = as_unpack(bb);
         }
         const int64_t tok = tok0 + lane;
         const int v = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];

@@ -6,6 +6,7 @@ import torch
 
 import oracle
 import sparse_decode_attention_ckv_amd as ck
+import synth
 
 DEV = "cuda:0"
 
@@ -46,34 +47,52 @@ def gpu_cluster(K, n_sink, C, iters, **kw):
     return out
 
 
+# Label parity margin of the bf16 cosine assignment (scores in [-1, 1]):
+# fp32 accumulation of the MFMA dot products (well under 1e-4) plus the
+# argmax's resolution -- the kernel compares scores whose 11 low mantissa
+# bits carry the cluster id, i.e. to 2^-12 of their magnitude, at most
+# 1.22e-4 for a cosine in [0.5, 1).
+ASSIGN_MARGIN = 2.5e-4
+
 # the library's metric codes for the oracle's
 CK_METRIC = {oracle.COSINE: ck.CKV_COSINE, oracle.INNER_PRODUCT: ck.CKV_INNER_PRODUCT,
              oracle.L2: ck.CKV_L2}
 
 
-def margin_threshold(metric, Kw, mu, margin, margin_rel):
+def margin_threshold(metric, Kw, mu, labels, margin, mode):
     """Per-token margin below which a label is not compared. Cosine scores
-    lie in [-1, 1]: the absolute `margin`. Inner-product and L2 scores grow
-    with |k| |mu|: fp32 accumulation of 128 products errs by at most about
-    128 * 2^-24 |k| |mu|, so the threshold is margin_rel |k| max|mu| (twice
-    that, plus the rounding of the fp32 bias -|mu|^2 / 2, for the L2
-    squared-distance gap)."""
+    lie in [-1, 1]: the absolute `margin`. Inner-product and L2 scores are
+    unbounded, so the threshold follows each token's winning score s (the
+    operands as the kernel reads them: mu rounded to bf16 under MIRROR): the
+    packed comparison resolves 2^-12 |s| on either side, 2^-11 |s| in all,
+    and fp32 accumulation of 128 products errs by at most 128 * 2^-24 |k|
+    max|mu| per score; twice the score gap (plus the bias rounding) for the
+    L2 squared-distance gap; a safety factor of 2 over all."""
     if metric == oracle.COSINE:
         return margin
+    mu_r = mu if mode == oracle.EXACT else synth.bf16_to_f32(synth.bf16_bits(mu)).astype(
+        np.float64)
     kn = np.linalg.norm(Kw, axis=1)
-    M = np.linalg.norm(mu, axis=1).max()
-    thr = margin_rel * kn * M
-    return thr if metric == oracle.INNER_PRODUCT else 2 * (thr + 2.0 ** -22 * M * M)
+    M = np.linalg.norm(mu_r, axis=1).max()
+    m = mu_r[np.clip(labels, 0, len(mu_r) - 1)]
+    s = np.einsum("ij,ij->i", Kw, m)
+    if metric == oracle.L2:
+        s = s - 0.5 * np.einsum("ij,ij->i", m, m)
+    gap = 2.0 ** -11 * np.abs(s) + 2 * 128 * 2.0 ** -24 * kn * M
+    if metric == oracle.L2:
+        gap = 2 * gap + 2.0 ** -22 * M * M
+    return 2 * gap
 
 
-def lloyd_parity(Kdev, Kf64, n_sink, C, iters, mode, tol_mu=1e-4, margin=1e-4,
-                 token_base=0, sample=None, metric=oracle.COSINE, margin_rel=2e-5):
+def lloyd_parity(Kdev, Kf64, n_sink, C, iters, mode, tol_mu=1e-4, margin=ASSIGN_MARGIN,
+                 token_base=0, sample=None, metric=oracle.COSINE):
     """Per-iteration parity of the GPU K-means against the oracle.
 
     For t = 1..iters the GPU runs t iterations from scratch (a prefix of the
     same deterministic sequence). The oracle starts iteration t from the
     GPU's centroids of iteration t-1 and must reproduce:
-      * labels, bit-exact, for tokens whose top-2 margin is >= `margin`;
+      * labels, bit-exact, for tokens whose top-2 margin is >= `margin`
+        (ASSIGN_MARGIN; scaled per token for inner product and L2);
       * the CSR of the GPU's labels, bit-exact;
       * the centroids of the GPU's labels, max abs error <= tol_mu.
     Kf64: [H][L][d] exact values. `sample`: optional token subset (window
@@ -98,14 +117,14 @@ def lloyd_parity(Kdev, Kf64, n_sink, C, iters, mode, tol_mu=1e-4, margin=1e-4,
             if sample is None:
                 a_o, m_o = oracle.assign(Kf64[h], n_sink, mu_prev[h], mode=mode, metric=metric)
                 keep = m_o[n_sink:] >= margin_threshold(metric, Kf64[h][n_sink:], mu_prev[h],
-                                                        margin, margin_rel)
+                                                        a_o[n_sink:], margin, mode)
                 got = a_g[h, n_sink:]
                 want = a_o[n_sink:]
             else:
                 a_o, m_o = oracle.assign(Kf64[h][sample], 0, mu_prev[h], mode=mode,
                                          metric=metric)
-                keep = m_o >= margin_threshold(metric, Kf64[h][sample], mu_prev[h], margin,
-                                               margin_rel)
+                keep = m_o >= margin_threshold(metric, Kf64[h][sample], mu_prev[h], a_o, margin,
+                                               mode)
                 got = a_g[h, sample]
                 want = a_o
             bad = np.nonzero(keep & (got != want))[0]
