@@ -104,6 +104,8 @@ int ckv_abi_version(void);
  *               cluster, ascending inside a cluster.
  * Appending clusters of a later window (c_base > 0, t_base > 0) leaves the
  * earlier slots untouched, so one CSR can index prompt and decode clusters.
+ * A bf16 window of at most 1024 clustered rows and 16 clusters (a decode
+ * increment) runs as one launch with the same arithmetic and results.
  */
 typedef struct {
     int32_t H;              /* independent KV-head problems (batch x KV heads), >= 1 */

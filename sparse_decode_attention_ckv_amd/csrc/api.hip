@@ -290,6 +290,9 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
     p.n_cu = device_cu_count();
     hipStream_t s = (hipStream_t)stream;
 
+    if (p.dtype == CKV_BF16 && p.Lp <= kSmallRows && p.C <= kSmallC)
+        return launch_status(launch_cluster_small(p, K, centroids, assign, csr_offsets,
+                                                  csr_tokens, s));
     hipError_t e = launch_normalize_keys(p, K, assign, s);
     if (e == hipSuccess) e = launch_init_centroids(p, K, centroids, s);
     for (int t = 0; t < p.iters && e == hipSuccess; ++t) {

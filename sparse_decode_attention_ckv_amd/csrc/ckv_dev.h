@@ -207,6 +207,15 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
 hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
                          const int32_t *tokens, float *cent, hipStream_t s);
 
+// Whole K-means of a small bf16 window in one launch (one workgroup per
+// head), bitwise the general path's result.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallRows = kSmallThreads;   // window rows (one per thread)
+constexpr int kSmallC = 16;                 // clusters (one MFMA M tile)
+hipError_t launch_cluster_small(const ClusterPlan &p, const void *K, float *cent,
+                                int32_t *assign, int32_t *offsets, int32_t *tokens,
+                                hipStream_t s);
+
 // Largest idx row (budget B) a selection call accepts: the cut kernel runs
 // one workgroup per 64 slots of every head.
 constexpr int kMaxSelB = 1 << 20;

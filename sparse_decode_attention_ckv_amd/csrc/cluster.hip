@@ -117,6 +117,8 @@ __global__ __launch_bounds__(kNkRows) void k_normalize_keys_bf16(
     const uint16_t *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
     uint16_t *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
     __shared__ u32x4 rows[kNkRows * kNkStride];
+    __shared__ int32_t stok[kSmallRows];
+    __shared__ int32_t soff[kSmallC + 1];
     const int h = blockIdx.y, tid = threadIdx.x;
     if (blockIdx.x == 0)   // sink rows are labelled -1
         for (int i = tid; i < n_sink; i += kNkRows) assign[(int64_t)h * L + i] = -1;
@@ -637,23 +639,20 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
 // mean = sum / n in fp64, stored as fp32; an empty cluster keeps its
 // centroid. The unit centroid for the next assignment is written too, by
 // the first wave alone (no barrier after the reduction).
-template <bool BF16, int M>
-__global__ __launch_bounds__(256) void k_update(
+// First half: the partial sums of cluster c of head h by the 256 threads of
+// a group (ltid = thread in the group) into red; returns the cluster size.
+// off points at the cluster's offset pair and tok at its head's token list
+// (global memory, or LDS copies of both), t_cap bounds the list.
+template <bool BF16>
+__device__ __forceinline__ int64_t upd_partial(
     const void *__restrict__ K, int64_t head_stride, int64_t L, int64_t token_base,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tokens, int c_base,
-    int c_cap, int64_t t_cap, float *__restrict__ cent, void *__restrict__ mt,
-    float *__restrict__ mb, int Cpad) {
-    __shared__ double red[4][kD];
-    __shared__ __align__(16) float sx[kD];
-    const int c = blockIdx.x, h = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = tid >> 4, q = tid & 15;
-    const int32_t *off = offsets + (int64_t)h * (c_cap + 1) + c_base + c;
+    const int32_t *off, const int32_t *tok, int64_t t_cap, int h, int ltid, double (*red)[kD]) {
+    const int lane = ltid & 63, wave = ltid >> 6;
+    const int slot = ltid >> 4, q = ltid & 15;
     int64_t beg = off[0], end = off[1];
     beg = beg < 0 ? 0 : (beg > t_cap ? t_cap : beg);
     end = end < beg ? beg : (end > t_cap ? t_cap : end);
     const int64_t n = end - beg;
-    const int32_t *tok = tokens + (int64_t)h * t_cap;
 
     double acc[8];
 #pragma unroll
@@ -713,37 +712,53 @@ __global__ __launch_bounds__(256) void k_update(
 #pragma unroll
         for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
     }
-    __syncthreads();
-    if (wave != 0) return;
-    // wave 0 finishes: lane l owns channels l and l + 64. mean = sum / n in
-    // fp64, stored as fp32 (an empty cluster keeps its centroid); then the
-    // unit row: |mu|^2 as one fp64 fma chain over j = 0..127 in order,
-    // r = 1/sqrt(|mu|^2), channel j -> fp32(mu_j * r) (then bf16 when BF16);
-    // a zero row stays zero
-    float *cp = cent + ((int64_t)h * c_cap + c_base + c) * kD;
+    return n;
+}
+
+// Second half, by the group's first wave once red is complete: lane l owns
+// channels l and l + 64. mean = sum / n in fp64, stored as fp32 in the
+// centroid row cp (an empty cluster keeps its centroid); then the row the
+// next assignment reads: for the cosine the unit row (|mu|^2 as one fp64 fma
+// chain over j = 0..127 in order, r = 1/sqrt(|mu|^2), channel j ->
+// fp32(mu_j * r), then bf16 when BF16; a zero row stays zero), else the mean
+// rounded to the key type and, for L2, the bias -|mu^|^2 / 2 of that rounded
+// row. That row goes to mrow and the bias to *bias when they are given, and
+// to row c of the swizzled LDS tile sA (and sB[c]) when those are given.
+template <bool BF16, int M>
+__device__ __forceinline__ void upd_final(int c, int lane, int64_t n, const double (*red)[kD],
+                                          float *sx, float *cp, void *mrow, float *bias,
+                                          u32x4 *sA = nullptr, float *sB = nullptr) {
     float mu[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int j = lane + 64 * k;
-        const double ssum = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
-        mu[k] = (n > 0) ? (float)(ssum / (double)n) : cp[j];
+        if (n > 0) {
+            const double ssum = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+            mu[k] = (float)(ssum / (double)n);
+        } else {
+            mu[k] = cp[j];
+        }
         cp[j] = mu[k];
     }
-    const int64_t mrow = ((int64_t)h * Cpad + c) * kD;
+    // channel j of row c in the swizzled tile: chunk j / 8, element j % 8
+    auto put = [&](int j, uint16_t bits, float y) {
+        if (BF16) {
+            if (mrow) ((uint16_t *)mrow)[j] = bits;
+            if (sA) ((uint16_t *)(sA + c * 16 + ((j >> 3) ^ (c & 15))))[j & 7] = bits;
+        } else if (mrow) {
+            ((float *)mrow)[j] = y;
+        }
+    };
     if (M != kCosine) {
-        // inner product and L2 read the mean rounded to the key type; L2 also
-        // the bias -|mu^|^2 / 2 of that rounded row (fp64 chain in channel
-        // order on every lane, written by lane 0)
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             float y = mu[k];
+            uint16_t bits = 0;
             if (BF16) {
-                const uint32_t b = f32_to_bf16_rne(mu[k]);
-                ((uint16_t *)mt)[mrow + lane + 64 * k] = (uint16_t)b;
-                y = bf16_to_f32((uint16_t)b);
-            } else {
-                ((float *)mt)[mrow + lane + 64 * k] = y;
+                bits = (uint16_t)f32_to_bf16_rne(mu[k]);
+                y = bf16_to_f32(bits);
             }
+            put(lane + 64 * k, bits, y);
             sx[lane + 64 * k] = y;
         }
         if (M == kL2) {
@@ -759,7 +774,10 @@ __global__ __launch_bounds__(256) void k_update(
                 ss = __fma_rn((double)x[2], (double)x[2], ss);
                 ss = __fma_rn((double)x[3], (double)x[3], ss);
             }
-            if (lane == 0) mb[(int64_t)h * Cpad + c] = (float)(-0.5 * ss);
+            if (lane == 0) {
+                if (bias) *bias = (float)(-0.5 * ss);
+                if (sB) sB[c] = (float)(-0.5 * ss);
+            }
         }
         return;
     }
@@ -783,10 +801,28 @@ __global__ __launch_bounds__(256) void k_update(
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const float y = (float)((double)mu[k] * inv);
-        if (BF16)
-            ((uint16_t *)mt)[mrow + lane + 64 * k] = (uint16_t)f32_to_bf16_rne(y);
-        else
-            ((float *)mt)[mrow + lane + 64 * k] = y;
+        put(lane + 64 * k, BF16 ? (uint16_t)f32_to_bf16_rne(y) : (uint16_t)0, y);
+    }
+}
+
+template <bool BF16, int M>
+__global__ __launch_bounds__(256) void k_update(
+    const void *__restrict__ K, int64_t head_stride, int64_t L, int64_t token_base,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tokens, int c_base,
+    int c_cap, int64_t t_cap, float *__restrict__ cent, void *__restrict__ mt,
+    float *__restrict__ mb, int Cpad) {
+    __shared__ double red[4][kD];
+    __shared__ __align__(16) float sx[kD];
+    const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int64_t n = upd_partial<BF16>(K, head_stride, L, token_base,
+                                        offsets + (int64_t)h * (c_cap + 1) + c_base + c,
+                                        tokens + (int64_t)h * t_cap, t_cap, h, tid, red);
+    __syncthreads();
+    if ((tid >> 6) == 0) {
+        const int64_t mr = ((int64_t)h * Cpad + c) * kD;
+        upd_final<BF16, M>(c, tid & 63, n, red, sx, cent + ((int64_t)h * c_cap + c_base + c) * kD,
+                           BF16 ? (void *)((uint16_t *)mt + mr) : (void *)((float *)mt + mr),
+                           mb + (int64_t)h * Cpad + c);
     }
 }
 
@@ -812,6 +848,225 @@ hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *off
         launch_update_m<kInnerProduct>(p, K, offsets, tokens, cent, s);
     else
         launch_update_m<kL2>(p, K, offsets, tokens, cent, s);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Small windows (decode-time increments: 320 rows into 4 clusters) in one
+// launch: one 1024-thread workgroup per head runs the whole K-means, with
+// workgroup barriers where the general path has kernel boundaries. Every
+// step is the general path's device code with the same thread-to-data
+// mapping, so the results are bitwise those of the general path:
+//  * unit (or raw) rows: nk_unit_row on rows staged through LDS, 256 at a time;
+//  * initial centroids: the chain of block_unit_row / block_store_row, eight
+//    128-thread groups at a time; centroids stay in LDS and the rows the
+//    assignment reads go straight into its LDS tile;
+//  * assignment: wave w takes tokens 64 w .. 64 w + 63 against the one
+//    16-cluster M tile (as_load_b, as_mtile, the packed lane merge);
+//  * CSR: the stable counting sort (ballot ranks inside a wave, wave counts,
+//    prefix over clusters), tokens in ascending order inside a cluster;
+//  * update: four 256-thread groups run k_update's two halves for clusters
+//    g, g + 4, ..., reading the CSR from LDS copies.
+// Global memory gets only the results (the last iteration's labels and CSR,
+// the final centroids): a barrier after a global store waits for it.
+// Windows up to kSmallRows rows and kSmallC clusters, bf16 keys.
+
+template <int M>
+__global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
+    const uint16_t *__restrict__ K, int64_t head_stride, int64_t L, int n_sink, int64_t Lp,
+    int C, int iters, int64_t token_base, float *__restrict__ cent, int c_base, int c_cap,
+    int32_t *__restrict__ assign, int32_t *__restrict__ offsets, int32_t *__restrict__ tokens,
+    int64_t t_base, int64_t t_cap, uint16_t *__restrict__ kt) {
+    constexpr bool BIAS = M == kL2;
+    __shared__ u32x4 sA[16 * 16];
+    __shared__ __align__(16) float sB[16];
+    __shared__ int wcnt[16][kSmallC];
+    __shared__ double red[4][4][kD];
+    __shared__ __align__(16) float sx[8][kD];
+    __shared__ double sinv[8];
+    __shared__ float scent[kSmallC][kD];
+    __shared__ u32x4 rows[kNkRows * kNkStride];
+    __shared__ int32_t stok[kSmallRows];
+    __shared__ int32_t soff[kSmallC + 1];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int32_t *as = assign + (int64_t)h * L;
+
+    // unit (or raw) rows of the window, 256 rows at a time through LDS as in
+    // k_normalize_keys_bf16 (coalesced 16-byte chunks; thread r < 256 runs
+    // the chain of row r); sinks labelled -1
+    for (int i = tid; i < n_sink; i += kSmallThreads) as[i] = -1;
+    for (int64_t r0 = 0; r0 < Lp; r0 += kNkRows) {
+        const int nrow = (int)(Lp - r0 < kNkRows ? Lp - r0 : kNkRows);
+        const u32x4 *src = (const u32x4 *)(K + h * head_stride + (n_sink + r0) * kD);
+        u32x4 *dst = (u32x4 *)(kt + ((int64_t)h * Lp + r0) * kD);
+        constexpr int PER = kNkRows * 16 / kSmallThreads;        // chunks per thread
+        u32x4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + kSmallThreads * k;
+            v[k] = src[(e >> 4) < nrow ? e : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + kSmallThreads * k;
+            rows[(e >> 4) * kNkStride + (e & 15)] = v[k];
+        }
+        __syncthreads();
+        if (M == kCosine && tid < kNkRows) nk_unit_row(rows + tid * kNkStride);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + kSmallThreads * k;
+            if ((e >> 4) < nrow) dst[e] = rows[(e >> 4) * kNkStride + (e & 15)];
+        }
+        __syncthreads();
+    }
+    // initial centroids mu_c = row n_sink + s c, s = floor(Lp / C), eight at
+    // a time (group g of 128 threads, channel j), as in k_init_centroids: the
+    // centroid into LDS, the row the assignment reads into the LDS tile
+    {
+        const int g = tid >> 7, j = tid & 127;
+        auto put = [&](int c, uint16_t bits) {
+            ((uint16_t *)(sA + c * 16 + ((j >> 3) ^ (c & 15))))[j & 7] = bits;
+        };
+        for (int c0 = 0; c0 < C; c0 += 8) {
+            const int c = c0 + g;
+            const bool act = c < C;
+            float x = 0.f;
+            if (act) {
+                const int64_t row = n_sink + (Lp / C) * (int64_t)c;
+                x = bf16_to_f32(K[h * head_stride + row * kD + j]);
+                scent[c][j] = x;
+                if (M == kCosine) {
+                    sx[g][j] = x;
+                } else {
+                    const uint32_t b = f32_to_bf16_rne(x);
+                    put(c, (uint16_t)b);
+                    sx[g][j] = bf16_to_f32((uint16_t)b);
+                }
+            }
+            __syncthreads();
+            if (act && j == 0 && (M == kCosine || M == kL2)) {
+                double ss = 0.0;
+                for (int k = 0; k < kD; ++k) ss = __fma_rn((double)sx[g][k], (double)sx[g][k], ss);
+                if (M == kCosine)
+                    sinv[g] = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+                else
+                    sB[c] = (float)(-0.5 * ss);
+            }
+            __syncthreads();
+            if (M == kCosine && act)
+                put(c, (uint16_t)f32_to_bf16_rne((float)((double)x * sinv[g])));
+        }
+    }
+    __syncthreads();
+
+    const int col = lane & 15, kq = lane >> 4;
+    const int64_t i = tid;                      // this thread's token
+    const bool valid = i < Lp;
+    int nbits = 1;
+    while ((1 << nbits) < C) ++nbits;
+    for (int it = 0; it < iters; ++it) {
+        const bool last = it == iters - 1;       // only its labels and CSR are kept
+        // assignment: wave w's 64 tokens against the one M tile
+        {
+            bf16x8 b[4][4];
+            as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, (int64_t)wave * 64, col,
+                      kq, b);
+            float best[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) best[u] = -INFINITY;
+            as_mtile<true, BIAS>(sA, sB, 0, col, kq, b, 4 * kq, C, best);
+            int res[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float bb = best[u];
+                bb = fmaxf(bb, __shfl_xor(bb, 16));
+                bb = fmaxf(bb, __shfl_xor(bb, 32));
+                res[u] = as_unpack(bb);
+            }
+            int a = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];
+            if (last && valid) as[n_sink + i] = a;
+            // CSR: rank among equal labels in the wave, then wave counts
+            a = a < 0 ? 0 : (a >= C ? C - 1 : a);
+            for (int e = tid; e < 16 * kSmallC; e += kSmallThreads) (&wcnt[0][0])[e] = 0;
+            __syncthreads();
+            uint64_t eq = __ballot(valid);
+            for (int bt = 0; bt < nbits; ++bt) {
+                const int bit = (a >> bt) & 1;
+                const uint64_t bb = __ballot(bit);
+                eq &= bit ? bb : ~bb;
+            }
+            const int rk = __popcll(eq & __lanemask_lt());
+            if (valid && rk == 0) wcnt[wave][a] = __popcll(eq);
+            __syncthreads();
+            int base = 0, excl = 0;
+            for (int w = 0; w < 16; ++w) base += w < wave ? wcnt[w][a] : 0;
+            for (int c = 0; c < a; ++c)
+                for (int w = 0; w < 16; ++w) excl += wcnt[w][c];
+            // the CSR in LDS for the update (offsets relative to the window's
+            // first token slot); in global memory after the last assignment
+            if (valid) {
+                const int pos = excl + base + rk;
+                if (pos >= 0 && pos < Lp) {
+                    const int32_t t = (int32_t)(token_base + n_sink + i);
+                    stok[pos] = t;
+                    if (last) tokens[(int64_t)h * t_cap + t_base + pos] = t;
+                }
+            }
+            if (tid <= C) {
+                int e = 0;
+                for (int c = 0; c < tid; ++c)
+                    for (int w = 0; w < 16; ++w) e += wcnt[w][c];
+                soff[tid] = e;
+                if (last) offsets[(int64_t)h * (c_cap + 1) + c_base + tid] = (int32_t)(t_base + e);
+            }
+            __syncthreads();
+        }
+        // update: four groups of 256 threads, clusters g, g + 4, ...; the new
+        // centroids stay in LDS, their assignment rows go to the LDS tile
+        {
+            const int g = tid >> 8, ltid = tid & 255;
+            for (int c0 = 0; c0 < C; c0 += 4) {
+                const int c = c0 + g;
+                int64_t n = 0;
+                if (c < C)
+                    n = upd_partial<true>(K, head_stride, L, token_base, soff + c, stok, Lp, h,
+                                          ltid, red[g]);
+                __syncthreads();
+                if (c < C && (ltid >> 6) == 0)
+                    upd_final<true, M>(c, lane, n, red[g], sx[g], scent[c], nullptr, nullptr, sA,
+                                       BIAS ? sB : nullptr);
+                __syncthreads();
+            }
+        }
+    }
+    // the final centroids
+    for (int e = tid; e < C * kD; e += kSmallThreads)
+        cent[((int64_t)h * c_cap + c_base + e / kD) * kD + e % kD] = scent[e / kD][e % kD];
+}
+
+hipError_t launch_cluster_small(const ClusterPlan &p, const void *K, float *cent,
+                                int32_t *assign, int32_t *offsets, int32_t *tokens,
+                                hipStream_t s) {
+    const uint16_t *Kb = (const uint16_t *)K;
+    uint16_t *kt = (uint16_t *)p.kt;
+    if (p.metric == kCosine)
+        hipLaunchKernelGGL(k_cluster_small<kCosine>, dim3(p.H), dim3(kSmallThreads), 0, s, Kb,
+                           p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
+                           cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
+                           kt);
+    else if (p.metric == kInnerProduct)
+        hipLaunchKernelGGL(k_cluster_small<kInnerProduct>, dim3(p.H), dim3(kSmallThreads), 0, s,
+                           Kb, p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
+                           cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
+                           kt);
+    else
+        hipLaunchKernelGGL(k_cluster_small<kL2>, dim3(p.H), dim3(kSmallThreads), 0, s, Kb,
+                           p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
+                           cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
+                           kt);
     return hipGetLastError();
 }
 
