@@ -409,7 +409,7 @@ KERNEL_SOURCES = {
     "ckv_sparse_attn": ["attn.hip", "attn_dev.h", "ckv_dev.h"],
     "ckv_select_attn": ["decode.hip", "select.hip", "sel_dev.h", "attn.hip", "attn_dev.h",
                         "ckv_dev.h"],
-    "ckv_cluster": ["cluster.hip", "ckv_dev.h"],
+    "ckv_cluster": ["cluster.hip", "cluster_dev.h", "ckv_dev.h"],
 }
 
 

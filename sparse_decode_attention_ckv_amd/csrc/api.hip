@@ -9,7 +9,9 @@
 #include <atomic>
 
 #include "ckv.h"
+#include "cache_dev.h"
 #include "ckv_dev.h"
+#include "cluster_dev.h"
 
 using namespace ckv;
 

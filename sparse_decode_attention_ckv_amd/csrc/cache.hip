@@ -25,7 +25,7 @@
 //  * k_cache_fill: a gather of the new buffer, 16-byte chunks, every row's
 //    K and V loads in flight together (the host rows cross the host link, so
 //    many loads must be outstanding).
-#include "ckv_dev.h"
+#include "cache_dev.h"
 
 namespace ckv {
 

@@ -1,4 +1,6 @@
-// ckv_dev.h -- internal declarations of libckv (device helpers + launchers).
+// ckv_dev.h -- internal declarations of libckv: device helpers shared by the
+// kernels, and the plans and launchers of the decode kernels (cluster_dev.h
+// and cache_dev.h hold the others).
 // Not part of the public ABI; include/ckv.h is.
 #pragma once
 
@@ -176,46 +178,6 @@ __device__ inline int block_excl_scan(int v, int *wsum, int *total) {
 int device_cu_count();
 
 // ---- launchers (defined in the .hip files) ------------------------------
-// assignment distances (the values of ckv_metric)
-constexpr int kCosine = 0, kInnerProduct = 1, kL2 = 2;
-
-struct ClusterPlan {
-    int H, C, Cpad, iters, n_sink, dtype, c_base, c_cap;
-    int metric;               // kCosine, kInnerProduct or kL2
-    int64_t L, Lp, k_head_stride, token_base, t_base, t_cap;
-    int64_t ntiles;           // CSR tiles per head
-    int n_cu;                 // compute units of the device (persistent grids)
-    // workspace carve-up (device pointers)
-    void *kt;                 // keys as the assignment reads them [H][Lp][d]
-                              // (bf16 or f32; unit rows for the cosine)
-    void *mt;                 // centroids as the assignment reads them [H][Cpad][d]
-                              // (bf16 or f32; unit rows for the cosine)
-    float *mb;                // per-cluster score bias [H][Cpad] (L2: -|mu|^2 / 2)
-    int32_t *tile_hist;       // [H][ntiles][C], then tile bases
-    int32_t *tile_rank;       // [H][Lp]
-    int32_t *counts;          // [H][C] cluster sizes
-};
-
-constexpr int kCsrTile = 512;          // tokens per CSR tile (one workgroup)
-
-hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *assign,
-                                 hipStream_t s);
-hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cent, hipStream_t s);
-hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s);
-hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offsets,
-                      int32_t *tokens, hipStream_t s);
-hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
-                         const int32_t *tokens, float *cent, hipStream_t s);
-
-// Whole K-means of a small bf16 window in one launch (one workgroup per
-// head), bitwise the general path's result.
-constexpr int kSmallThreads = 1024;
-constexpr int kSmallRows = kSmallThreads;   // window rows (one per thread)
-constexpr int kSmallC = 16;                 // clusters (one MFMA M tile)
-hipError_t launch_cluster_small(const ClusterPlan &p, const void *K, float *cent,
-                                int32_t *assign, int32_t *offsets, int32_t *tokens,
-                                hipStream_t s);
-
 // Largest idx row (budget B) a selection call accepts: the cut kernel runs
 // one workgroup per 64 slots of every head.
 constexpr int kMaxSelB = 1 << 20;
@@ -246,21 +208,5 @@ hipError_t launch_select_attn(const SelectPlan &sp, const AttnPlan &ap, const vo
                               const float *cent, const int32_t *offsets, const int32_t *tokens,
                               const void *K, const void *V, int32_t *idx, int32_t *n_sel,
                               float *o, hipStream_t s);
-
-// Cluster-granular cache of selected rows (cache.hip).
-constexpr int kMaxCacheR = 8;
-constexpr int kMaxCacheB = 4096;          // largest budget the cache plan holds in registers
-struct CachePlan {
-    int H, C, c_cap, n_sink, B, R, dtype, rows;
-    int64_t L, token_base, t_cap, kv_head_stride, kv_rows;
-    int32_t *src;             // workspace [H][rows]: source of every new slot
-    int32_t *tot;             // workspace [H]: slots in use after the step
-};
-hipError_t launch_cache_step(const CachePlan &p, int64_t step, const int32_t *idx,
-                             const int32_t *n_sel, const int32_t *assign,
-                             const int32_t *offsets, const int32_t *tokens, const void *Kh,
-                             const void *Vh, int32_t *ring, void *cache_K, void *cache_V,
-                             int32_t *cache_tok, int32_t *idx_cache, int32_t *stats,
-                             hipStream_t s);
 
 }  // namespace ckv

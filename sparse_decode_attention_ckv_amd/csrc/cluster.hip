@@ -21,7 +21,7 @@
 // threads strided along the sequence, channels split into P partitions) is
 // replaced by the counting sort + segmented reduction: no atomics, so every
 // result is bitwise reproducible.
-#include "ckv_dev.h"
+#include "cluster_dev.h"
 
 namespace ckv {
 
