@@ -13,7 +13,8 @@ Prints one JSON line. `value` is the decode-step latency (select + sparse
 attention, microseconds per step); the clustering time per layer (with its
 p50/p99 over warm replays), the whole-step time and the cold decode step
 (the MALL and L2 flushed by a 512 MiB stream before every step) are reported
-beside it.
+beside it, and the roofline fractions against both the vendor peaks and the
+peaks this GPU achieves on a plain copy and a library GEMM.
 """
 from __future__ import annotations
 
@@ -384,6 +385,40 @@ def pct(xs, p):
     return xs[k]
 
 
+def measured_peaks(dev):
+    """What this GPU achieves on plain work, beside the vendor figures: HBM
+    bandwidth of a 1 GiB device-to-device copy (bytes read + written per
+    second) and bf16 matrix throughput of an 8192^3 GEMM (hipBLASLt through
+    torch.mm, contiguous operands), each the best of 5 timed runs."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    M = 8192
+    a = torch.randn((M, M), device=dev).to(torch.bfloat16)
+    b = torch.randn((M, M), device=dev).to(torch.bfloat16)
+    dst.copy_(src)
+    c = torch.mm(a, b)
+    torch.cuda.synchronize()
+
+    def best(fn):
+        t = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e-3)
+        return min(t)
+    copy_s = best(lambda: dst.copy_(src))
+    gemm_s = best(lambda: torch.mm(a, b, out=c))
+    del src, dst, a, b, c
+    return {"hbm_copy_GB/s": round(2 * n / copy_s / 1e9, 1),
+            "bf16_gemm_TFLOP/s": round(2 * M ** 3 / gemm_s / 1e12, 1),
+            "method": "1 GiB device copy; 8192^3 bf16 torch.mm; best of 5 each"}
+
+
 def copy_calibration(mib):
     """Ten copies of `mib` MiB between two device buffers: each reads and
     writes exactly mib * 2^20 bytes, so the byte counters of its kernel give
@@ -698,12 +733,21 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": k["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    peaks = measured_peaks(dev)
+    roof["measured_peak"] = (peaks["bf16_gemm_TFLOP/s"] if roof["bound"] == "mfma"
+                             else peaks["hbm_copy_GB/s"])
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / roof["measured_peak"], 4)
     roof["traffic"] = recorded_traffic(dom, wl.name)
+    kernels["ckv_cluster"]["assign_frac_of_measured_gemm"] = round(
+        assign_flop / cl_ms / 1e9 / peaks["bf16_gemm_TFLOP/s"], 4)
+    log(f"measured peaks: HBM copy {peaks['hbm_copy_GB/s']} GB/s, bf16 GEMM "
+        f"{peaks['bf16_gemm_TFLOP/s']} TFLOP/s")
     if dom == "ckv_select_attn" and not case.inc:
         # the same call with the MALL and L2 flushed before it
         cold_gbs = fus_bytes / cold_us / 1e3
         roof["cold"] = {"us_per_call": round(cold_us, 3), "achieved": round(cold_gbs, 1),
-                        "frac": round(cold_gbs / HBM_PEAK_GBS, 4)}
+                        "frac": round(cold_gbs / HBM_PEAK_GBS, 4),
+                        "frac_of_measured_peak": round(cold_gbs / peaks["hbm_copy_GB/s"], 4)}
     log(f"per call: select {sel_us:.2f} us, attn {att_us:.2f} us, select_attn {fus_us:.2f} us"
         + (f", decode-time clustering {inc_ms * 1e3:.1f} us per event" if case.inc else "")
         + f"; dominant {dom}")
@@ -739,6 +783,7 @@ def main():
                         else "ckv_select_attn"),
         **({"kv_host": kv_host} if kv_host else {}),
         "roofline": roof,
+        "measured_peaks": peaks,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
