@@ -154,3 +154,33 @@ def test_cache_in_a_graph_replays():
             assert torch.equal(a, b), rep
         torch.ones(256, device=DEV).cumsum(0)         # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_cache_fp32_single_head():
+    """The fp32 path (512-byte rows) on the single-head fp32 workload."""
+    wl = synth.workload(0)
+    say("cache parity: single-head fp32 2k, C=25, B=256, R=2, 10 steps, pinned host K/V")
+    tot = _run_stream(wl, wl.L, [0], wl.C, wl.B, 2, 10, 0.8)
+    assert tot[0] > 0 and tot[1] > 0
+
+
+def test_pageable_host_memory_is_refused():
+    """K/V in ordinary (pageable) host memory has no device mapping: the
+    library refuses it before anything is enqueued."""
+    wl = synth.workload(1)
+    say("cache: pageable host K/V refused")
+    K, V, _ = synth.make_kv(wl, L=200, heads=[0])
+    Kd = to_dev(K, wl.dtype)
+    cent, asg, off, tok = ck.ckv_cluster(Kd, wl.n_sink, 2, 2)
+    Kp, Vp = Kd.cpu(), to_dev(V, wl.dtype).cpu()          # not pinned
+    assert not Kp.is_pinned()
+    desc = ck.cache_desc(Kp, asg, off, tok, 2, 64, 1, n_sink=wl.n_sink)
+    st = ck.cache_state(desc, DEV)
+    idx, ns = ck.ckv_select(to_dev(synth.make_queries(wl, 0, heads=[0])[0], wl.dtype), cent, off,
+                            tok, 2, 64, n_sink=wl.n_sink)
+    with pytest.raises(ck.CKVError) as e:
+        ck.ckv_cache_step(desc, 0, idx, ns, asg, off, tok, Kp, Vp, st)
+    assert e.value.status == ck.CKV_ERR_INVALID_ARG
+    with pytest.raises(ck.CKVError):
+        ck.ckv_device_view(Kp)
+    torch.cuda.synchronize()
