@@ -200,6 +200,7 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ n_sel, int B, double scale,
     float *__restrict__ part, int H, int S) {
     __shared__ float zs[G][kAttnRows];
+    __shared__ uint32_t sv[kAttnRows][kAttnRows];
     int h, s;
     xcd_head_unit(blockIdx.x, S, h, s);
     if (h >= H) return;
@@ -215,8 +216,8 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     n = n < 0 ? 0 : (n > B ? B : n);
     const bool okK = rK < n && tkK >= 0 && (int64_t)tkK < kv_rows;
     const bool okV = rV < n && tkV >= 0 && (int64_t)tkV < kv_rows;
-    attn_rows_bf16<G>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK, okV ? tkV : 0,
-                      (float)scale, part, S, s, zs);
+    attn_rows_bf16<G, false>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK, okV ? tkV : 0,
+                             (float)scale, part, S, s, zs, sv);
 }
 
 // combine: one workgroup per query head, thread j owns channel j; the

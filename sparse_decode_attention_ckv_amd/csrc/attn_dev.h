@@ -20,42 +20,47 @@ constexpr int kAttnPW = kD + 2;             // partial record: m, l, acc[d]
 // part[((hG + g) S + s) * kAttnPW ...].
 //   rowK/okK: the row (and whether it is valid) of split row
 //             16 * wave + (lane & 15), the row this lane scores;
-//   rowV/okV: the row of split row `lane`, whose V channels 2 lane, 2 lane + 1
-//             this lane's wave accumulates (rowV is read from every lane).
+//   rowV/okV: the row of split row `lane` (rowV is read from every lane).
 // Scores: one MFMA tile per wave, v_mfma_f32_16x16x32_bf16 with the query
 // heads on M (rows 0..G-1 of the A tile, the rest zero) and the wave's 16
 // rows on N: lane l supplies, for k step t, channels 32t + 8(l>>4) .. +7 of
 // head (l & 15) (A) and of its score row (B), and receives the scores of
-// heads 4(l>>4) + i for that row. Softmax and V: wave w takes the heads
-// g = w, w+4; lane l owns channels 2l, 2l+1 and row l of the split, so the
-// max and the sum of p are 64-lane wave reductions and the V sum runs over
-// the rows with p_r taken from lane r (readlane): no cross-lane reduction of
-// the accumulators. Every K fragment, q fragment and V word of a thread is
-// requested before the first is used.
-template <int G>
+// heads 4(l>>4) + i for that row. V: wave w loads split rows 16w .. 16w + 15
+// only, 16 bytes per lane (lane l: row 16w + 4i + (l >> 4), channels
+// 8(l & 15) .. + 7), into the LDS tile sv, so each row crosses from L2 once
+// and no V words wait in registers. Softmax and V: wave w takes the heads
+// g = w, w+4; lane l owns channels 2l, 2l+1 (word l of every sv row) and row l
+// of the split, so the max and the sum of p are 64-lane wave reductions and
+// the V sum runs over the rows in order with p_r taken from lane r
+// (readlane): no cross-lane reduction of the accumulators. Every K fragment,
+// q fragment and V chunk of a thread is requested before the first is used.
+// SYNC: sv shares LDS with data the caller read before the call, so a barrier
+// precedes the first write to it.
+template <int G, bool SYNC>
 __device__ __forceinline__ void attn_rows_bf16(const uint16_t *__restrict__ q,
                                                const uint16_t *__restrict__ K,
                                                const uint16_t *__restrict__ V,
                                                int64_t kv_head_stride, int h, int rowK, bool okK,
                                                int rowV, float fscale, float *__restrict__ part,
-                                               int S, int s, float (&zs)[G][kAttnRows]) {
+                                               int S, int s, float (&zs)[G][kAttnRows],
+                                               uint32_t (&sv)[kAttnRows][kAttnRows]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kq = lane >> 4;    // MFMA fragment coordinates
     const uint16_t *Kh = K + (int64_t)h * kv_head_stride;
     const uint16_t *Vh = V + (int64_t)h * kv_head_stride;
     const uint16_t *qrow = q + ((int64_t)h * G + (col < G ? col : 0)) * kD;
-    u32x4 kb[4], qa[4];
+    int vrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vrow[i] = __shfl(rowV, 16 * wave + 4 * i + kq);
+    u32x4 kb[4], qa[4], vb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) kb[t] = *(const u32x4 *)(Kh + (int64_t)rowK * kD + 32 * t + 8 * kq);
 #pragma unroll
     for (int t = 0; t < 4; ++t) qa[t] = *(const u32x4 *)(qrow + 32 * t + 8 * kq);
-    uint32_t vv[kAttnRows];
 #pragma unroll
-    for (int r = 0; r < kAttnRows; ++r) {
-        const int row = __builtin_amdgcn_readlane(rowV, r);
-        vv[r] = *(const uint32_t *)(Vh + (int64_t)row * kD + 2 * lane);
-    }
+    for (int i = 0; i < 4; ++i) vb[i] = *(const u32x4 *)(Vh + (int64_t)vrow[i] * kD + 8 * col);
     __builtin_amdgcn_sched_barrier(0);
+    if (SYNC) __syncthreads();
 
     f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -70,6 +75,8 @@ __device__ __forceinline__ void attn_rows_bf16(const uint16_t *__restrict__ q,
         const int g = 4 * kq + i;
         if (g < G) zs[g][16 * wave + col] = okK ? acc4[i] * fscale : -INFINITY;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4 *)&sv[16 * wave + 4 * i + kq][4 * col] = vb[i];
     __syncthreads();
 
     for (int g = wave; g < G; g += 4) {
@@ -88,8 +95,9 @@ __device__ __forceinline__ void attn_rows_bf16(const uint16_t *__restrict__ q,
 #pragma unroll
         for (int r = 0; r < kAttnRows; ++r) {
             const float pr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p), r));
-            a0 += pr * bf16_lo(vv[r]);
-            a1 += pr * bf16_hi(vv[r]);
+            const uint32_t vw = sv[r][lane];
+            a0 += pr * bf16_lo(vw);
+            a1 += pr * bf16_hi(vw);
         }
         float *dst = part + (((int64_t)h * G + g) * S + s) * kAttnPW;
         if (lane == 0) {

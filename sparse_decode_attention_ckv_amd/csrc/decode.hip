@@ -29,7 +29,12 @@ __global__ __launch_bounds__(kCutThreads) void k_sel_attn_bf16(
     const uint16_t *__restrict__ V, int64_t kv_head_stride, int64_t kv_rows, float fscale,
     float *__restrict__ part, int H, int NS) {
     static_assert(kSelSlice == kAttnRows, "one selection window per attention split");
-    __shared__ SelLds<CMAX> S;
+    // the selection's LDS is dead once the slot is known: the V tile reuses it
+    __shared__ union {
+        SelLds<CMAX> sel;
+        uint32_t sv[kAttnRows][kAttnRows];
+    } U;
+    SelLds<CMAX> &S = U.sel;
     __shared__ float zs[G][kAttnRows];
     int h, s;
     xcd_head_unit(blockIdx.x, NS, h, s);
@@ -50,8 +55,8 @@ __global__ __launch_bounds__(kCutThreads) void k_sel_attn_bf16(
     const int rk = 16 * wave + (lane & 15);
     const int tkK = __shfl(r.val, rk);
     const bool okK = s * kSelSlice + rk < n && tkK >= 0 && (int64_t)tkK < kv_rows;
-    attn_rows_bf16<G>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK, rowV, fscale, part, NS,
-                      s, zs);
+    attn_rows_bf16<G, true>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK, rowV, fscale, part,
+                            NS, s, zs, U.sv);
 }
 
 template <int CMAX, int G>
