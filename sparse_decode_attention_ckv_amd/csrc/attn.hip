@@ -11,8 +11,9 @@
 //  * partial, grid (splits, KV heads): a workgroup takes R = 64 consecutive
 //    entries of idx, the idx and then all K/V/q loads of a thread in flight
 //    at once; scores for the G heads (bf16: one MFMA tile per wave; fp32:
-//    16 lanes per row), split max, exp, weighted V sum (16 lanes per row) ->
-//    (m, l, acc[d]) per query head;
+//    16 lanes per row), split max, exp, weighted V sum (bf16: each wave
+//    stages 16 V rows in an LDS tile and one wave per query head sums all 64
+//    rows in order; fp32: 16 lanes per row) -> (m, l, acc[d]) per query head;
 //  * combine, one workgroup per query head: o = sum_s e^{m_s - M} acc_s /
 //    sum_s e^{m_s - M} l_s, summed in split order.
 // A kernel boundary hands the partials over: on this multi-XCD part a

@@ -35,6 +35,8 @@ def _random_csr(rng, H, C, Lp, n_sink):
     (2, 4, 57, 900, 5000, 16, 0, "bf16"),        # B >= L: every row selected
     (2, 4, 57, 900, 16, 16, 0, "bf16"),          # B = n_sink: sinks only
     (9, 4, 64, 1000, 130, 16, 0, "bf16"),        # H not a multiple of 8
+    (64, 4, 409, 4000, 2048, 16, 0, "bf16"),     # batched grid: 2048 workgroups
+    (3, 4, 1638, 8000, 3000, 16, 40, "bf16"),    # 2048-cluster LDS, pending, ragged split
     (2, 1, 25, 2032, 256, 16, 0, "f32"),         # fp32: the separate kernels
 ])
 def test_fused_equals_separate_and_oracle(H, G, C, Lp, B, n_sink, n_pending, dtype):
