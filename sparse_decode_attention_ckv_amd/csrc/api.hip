@@ -79,7 +79,9 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     p->token_base = d->token_base;
     p->t_base = d->t_base;
     p->t_cap = d->t_cap;
-    p->ntiles = (p->Lp + kCsrTile - 1) / kCsrTile;
+    p->csr_wide = d->C <= kCsrWideMaxC;
+    const int tile = p->csr_wide ? kCsrWideTile : kCsrTile;
+    p->ntiles = (p->Lp + tile - 1) / tile;
     const size_t es = d->dtype == CKV_BF16 ? 2 : 4;
     size_t o = 0;
     p->kt = ws ? ws + o : nullptr;

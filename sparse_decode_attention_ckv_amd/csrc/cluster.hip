@@ -610,11 +610,152 @@ __global__ __launch_bounds__(kCsrTile) void k_csr_scatter(
         tokens[(int64_t)h * t_cap + t_base + pos] = (int32_t)(token_base + n_sink + i);
 }
 
+// Two-launch CSR for C <= 512: the same stable counting sort over tiles of
+// 2048 tokens, with the scan folded into the scatter.
+//  count_wide: wave w of the tile's 512 threads takes its tokens
+//              [256 w, 256 w + 256) in 4 rounds of 64; a token's rank among
+//              equal labels of its wave is its ballot rank in the round plus
+//              the wave's running count of that label (LDS, updated by the
+//              round's first lane of each label); after a barrier the counts
+//              of the waves before it make that a rank in the tile, and the
+//              waves' sums are the tile's histogram.
+//  scatter_wide: thread c sums cluster c's histogram over all tiles of the
+//              head (its size) and over the tiles before this one (its base
+//              here); an exclusive scan over the sizes gives the offsets, and
+//              token i of label a goes to offsets[a] + base[a] + rank_i.
+// Ranks grow with the token position, so each cluster lists its tokens in
+// ascending order, as in the three-pass version.
+constexpr int kCsrThreads = 512;
+constexpr int kCsrRounds = kCsrWideTile / kCsrThreads;   // rounds of 64 per wave
+
+__global__ __launch_bounds__(kCsrThreads) void k_csr_count_wide(
+    const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C, int nbits,
+    int64_t ntiles, int32_t *__restrict__ tile_hist, int32_t *__restrict__ tile_rank) {
+    static_assert(kCsrRounds * kCsrThreads == kCsrWideTile, "tile = waves x rounds x 64");
+    __shared__ int32_t wcnt[kCsrThreads / 64][kCsrWideMaxC];
+    const int h = blockIdx.y;
+    const int64_t tile = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t first = tile * kCsrWideTile + (int64_t)wave * (64 * kCsrRounds) + lane;
+    int a[kCsrRounds];
+    bool valid[kCsrRounds];
+#pragma unroll
+    for (int r = 0; r < kCsrRounds; ++r) {
+        const int64_t i = first + 64 * r;
+        valid[r] = i < Lp;
+        const int v = valid[r] ? assign[(int64_t)h * L + n_sink + i] : 0;
+        a[r] = v < 0 ? 0 : (v >= C ? C - 1 : v);
+    }
+    for (int e = tid; e < (kCsrThreads / 64) * kCsrWideMaxC; e += kCsrThreads)
+        (&wcnt[0][0])[e] = 0;
+    __syncthreads();
+    int rk[kCsrRounds];
+#pragma unroll
+    for (int r = 0; r < kCsrRounds; ++r) {
+        uint64_t eq = __ballot(valid[r]);
+        for (int b = 0; b < nbits; ++b) {
+            const int bit = (a[r] >> b) & 1;
+            const uint64_t bb = __ballot(bit);
+            eq &= bit ? bb : ~bb;
+        }
+        const int before = __popcll(eq & __lanemask_lt());
+        // every lane reads the running count before the label's first lane
+        // (one per label) writes it back: one wave, program order
+        const int run = wcnt[wave][a[r]];
+        rk[r] = run + before;
+        if (valid[r] && before == 0) wcnt[wave][a[r]] = run + __popcll(eq);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kCsrRounds; ++r) {
+        if (!valid[r]) continue;
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += wcnt[w][a[r]];
+        tile_rank[(int64_t)h * Lp + first + 64 * r] = rk[r] + base;
+    }
+    int32_t *hist = tile_hist + ((int64_t)h * ntiles + tile) * C;
+    for (int c = tid; c < C; c += kCsrThreads) {
+        int sacc = 0;
+#pragma unroll
+        for (int w = 0; w < kCsrThreads / 64; ++w) sacc += wcnt[w][c];
+        hist[c] = sacc;
+    }
+}
+
+__global__ __launch_bounds__(kCsrThreads) void k_csr_scatter_wide(
+    const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C,
+    int64_t ntiles, const int32_t *__restrict__ tile_hist, const int32_t *__restrict__ tile_rank,
+    int32_t *__restrict__ offsets, int c_base, int c_cap, int64_t t_base, int64_t t_cap,
+    int64_t token_base, int32_t *__restrict__ tokens) {
+    static_assert(kCsrWideMaxC <= kCsrThreads, "one cluster per thread");
+    constexpr int NB = 16;                      // histogram loads in flight per batch
+    __shared__ int start[kCsrWideMaxC];         // offsets[c] + base of this tile
+    __shared__ int wsum[17];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    // this thread's tokens: label and rank (loads in flight with the counts)
+    int a[kCsrRounds], rk[kCsrRounds];
+#pragma unroll
+    for (int r = 0; r < kCsrRounds; ++r) {
+        const int64_t i = tile * kCsrWideTile + (int64_t)kCsrThreads * r + tid;
+        const int64_t ii = i < Lp ? i : Lp - 1;
+        const int v = assign[(int64_t)h * L + n_sink + ii];
+        a[r] = v < 0 ? 0 : (v >= C ? C - 1 : v);
+        rk[r] = tile_rank[(int64_t)h * Lp + ii];
+    }
+    // cluster tid: its size over all tiles and its count in the tiles before this one
+    int cnt = 0, base = 0;
+    if (tid < C) {
+        const int32_t *col = tile_hist + (int64_t)h * ntiles * C + tid;
+        for (int64_t t0 = 0; t0 < ntiles; t0 += NB) {
+            int v[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int64_t t = t0 + k;
+                v[k] = col[(t < ntiles ? t : ntiles - 1) * C];
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int64_t t = t0 + k;
+                cnt += t < ntiles ? v[k] : 0;
+                base += t < tile ? v[k] : 0;
+            }
+        }
+    }
+    int total;
+    const int run = block_excl_scan(tid < C ? cnt : 0, wsum, &total);
+    if (tid < C) start[tid] = run + base;
+    if (tile == 0) {
+        int32_t *off = offsets + (int64_t)h * (c_cap + 1) + c_base;
+        if (tid < C) off[tid] = (int32_t)(t_base + run);
+        if (tid == 0) off[C] = (int32_t)(t_base + total);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kCsrRounds; ++r) {
+        const int64_t i = tile * kCsrWideTile + (int64_t)kCsrThreads * r + tid;
+        const int64_t pos = (int64_t)start[a[r]] + rk[r];
+        if (i < Lp && pos >= 0 && pos < Lp)
+            tokens[(int64_t)h * t_cap + t_base + pos] = (int32_t)(token_base + n_sink + i);
+    }
+}
+
 hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offsets,
                       int32_t *tokens, hipStream_t s) {
     int nbits = 1;
     while ((1 << nbits) < p.C) ++nbits;
     dim3 grid((unsigned)p.ntiles, p.H);
+    if (p.csr_wide) {
+        hipLaunchKernelGGL(k_csr_count_wide, grid, dim3(kCsrThreads), 0, s, assign, p.L,
+                           p.n_sink, p.Lp, p.C, nbits, p.ntiles, p.tile_hist, p.tile_rank);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_csr_scatter_wide, grid, dim3(kCsrThreads), 0, s, assign, p.L,
+                           p.n_sink, p.Lp, p.C, p.ntiles, (const int32_t *)p.tile_hist,
+                           (const int32_t *)p.tile_rank, offsets, p.c_base, p.c_cap, p.t_base,
+                           p.t_cap, p.token_base, tokens);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_csr_count, grid, dim3(kCsrTile), (size_t)8 * p.C * sizeof(int32_t), s,
                        assign, p.L, p.n_sink, p.Lp, p.C, nbits, p.ntiles, p.tile_hist,
                        p.tile_rank);

@@ -12,6 +12,7 @@ struct ClusterPlan {
     int metric;               // kCosine, kInnerProduct or kL2
     int64_t L, Lp, k_head_stride, token_base, t_base, t_cap;
     int64_t ntiles;           // CSR tiles per head
+    bool csr_wide;            // C <= kCsrWideMaxC: the two-launch CSR over wide tiles
     int n_cu;                 // compute units of the device (persistent grids)
     // workspace carve-up (device pointers)
     void *kt;                 // keys as the assignment reads them [H][Lp][d]
@@ -25,6 +26,8 @@ struct ClusterPlan {
 };
 
 constexpr int kCsrTile = 512;          // tokens per CSR tile (one workgroup)
+constexpr int kCsrWideTile = 2048;     // tokens per tile of the two-launch CSR
+constexpr int kCsrWideMaxC = 512;      // clusters it handles (one per scatter thread)
 
 hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *assign,
                                  hipStream_t s);
