@@ -184,3 +184,22 @@ def test_pageable_host_memory_is_refused():
     with pytest.raises(ck.CKVError):
         ck.ckv_device_view(Kp)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_cache_random_shapes(seed):
+    """Seeded random heads, window, cluster count, budget, R and query
+    correlation; every step checked against the oracle as above."""
+    r = np.random.default_rng(7500 + seed)
+    wl = synth.workload(1)
+    H = int(r.integers(1, 6))
+    C = int(r.integers(2, 300))
+    L = wl.n_sink + int(r.integers(C, 5000))
+    B = int(r.integers(wl.n_sink + 1, min(4096, L + 200)))
+    R = int(r.integers(1, 9))
+    steps = int(r.integers(R + 1, 14))
+    rho = float(r.choice([0.0, 0.6, 0.95]))
+    host = bool(seed % 4 != 3)
+    say(f"cache random seed {seed}: H={H} L={L} C={C} B={B} R={R} steps={steps} rho={rho} "
+        f"host={host}")
+    _run_stream(wl, L, list(range(H)), C, B, R, steps, rho, host=host)
