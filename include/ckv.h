@@ -200,6 +200,10 @@ int ckv_select(const ckv_select_desc *desc, const void *q, const float *centroid
  * Inputs: q [H*G][d] (dtype), K and V (dtype; row r of head g at
  * (g * kv_head_stride + r) * d), idx int32 [H][B], n_sel int32 [H].
  * Output: o fp32 [H*G][d].
+ * K and V may be device memory or the device mapping of pinned host memory
+ * (ckv_device_view). The call reads the pointer's memory type: for host
+ * memory the bf16 gather keeps more row requests in flight over the host
+ * link. The result is the same either way.
  */
 typedef struct {
     int32_t H;              /* KV heads, >= 1 */

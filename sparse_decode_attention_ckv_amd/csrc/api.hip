@@ -165,6 +165,18 @@ void plan_attn(const ckv_attn_desc *d, AttnPlan *p, void *partials) {
     p->kv_rows = d->kv_rows;
     p->scale = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)kD);
     p->partials = partials;
+    p->host_kv = false;
+}
+
+// Whether p points into host memory mapped for the device (pinned host
+// memory, read over the host link).
+bool host_memory(const void *p) {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return a.type == hipMemoryTypeHost;
 }
 
 // the two descriptors of one decode step describe the same problem
@@ -344,6 +356,7 @@ int ckv_sparse_attn(const ckv_attn_desc *desc, const void *q, const void *K, con
     if (!workspace || workspace_bytes < attn_bytes(desc)) return CKV_ERR_WORKSPACE;
     AttnPlan p;
     plan_attn(desc, &p, workspace);
+    p.host_kv = host_memory(K);
     return launch_status(launch_attn(p, q, K, V, idx, n_sel, o, (hipStream_t)stream));
 }
 

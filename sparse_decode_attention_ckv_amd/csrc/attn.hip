@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void k_attn_partial(
 // partial, bf16: the rows of split s come from idx (the V row of lane l is
 // split row l, the score row of lane l of wave w is split row 16w + (l & 15));
 // everything else is attn_rows_bf16.
-template <int G>
+template <int G, bool VTILE>
 __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t kv_head_stride, int64_t kv_rows,
@@ -217,8 +217,8 @@ __global__ __launch_bounds__(256) void k_attn_partial_bf16(
     n = n < 0 ? 0 : (n > B ? B : n);
     const bool okK = rK < n && tkK >= 0 && (int64_t)tkK < kv_rows;
     const bool okV = rV < n && tkV >= 0 && (int64_t)tkV < kv_rows;
-    attn_rows_bf16<G, false>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK, okV ? tkV : 0,
-                             (float)scale, part, S, s, zs, sv);
+    attn_rows_bf16<G, false, VTILE>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK,
+                                    okV ? tkV : 0, (float)scale, part, S, s, zs, sv);
 }
 
 // combine: one workgroup per query head, thread j owns channel j; the
@@ -273,10 +273,11 @@ static void launch_g(const AttnPlan &p, const void *q, const void *K, const void
                      const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s) {
     typedef typename Acc<T>::type A;
     if (sizeof(T) == 2)
-        hipLaunchKernelGGL((k_attn_partial_bf16<G>), dim3(xcd_head_grid(p.H, p.S)), dim3(256),
-                           0, s, (const uint16_t *)q, (const uint16_t *)K, (const uint16_t *)V,
-                           p.kv_head_stride, p.kv_rows, idx, n_sel, p.B, p.scale,
-                           (float *)p.partials, p.H, p.S);
+        hipLaunchKernelGGL((p.host_kv ? &k_attn_partial_bf16<G, false>
+                                      : &k_attn_partial_bf16<G, true>),
+                           dim3(xcd_head_grid(p.H, p.S)), dim3(256), 0, s, (const uint16_t *)q,
+                           (const uint16_t *)K, (const uint16_t *)V, p.kv_head_stride, p.kv_rows,
+                           idx, n_sel, p.B, p.scale, (float *)p.partials, p.H, p.S);
     else
         hipLaunchKernelGGL((k_attn_partial<T, G>), dim3(xcd_head_grid(p.H, p.S)), dim3(256), 0,
                            s, (const T *)q, (const T *)K, (const T *)V, p.kv_head_stride,

@@ -35,8 +35,12 @@ constexpr int kAttnPW = kD + 2;             // partial record: m, l, acc[d]
 // (readlane): no cross-lane reduction of the accumulators. Every K fragment,
 // q fragment and V chunk of a thread is requested before the first is used.
 // SYNC: sv shares LDS with data the caller read before the call, so a barrier
-// precedes the first write to it.
-template <int G, bool SYNC>
+// precedes the first write to it. VTILE false (K/V in host memory read over
+// the host link): every wave instead requests all 64 V rows itself, 4 bytes
+// per lane into 64 VGPRs, which keeps four times as many requests in flight on
+// the link's long round trip; the V sum is the same arithmetic in the same
+// order, so the result is the same.
+template <int G, bool SYNC, bool VTILE = true>
 __device__ __forceinline__ void attn_rows_bf16(const uint16_t *__restrict__ q,
                                                const uint16_t *__restrict__ K,
                                                const uint16_t *__restrict__ V,
@@ -50,15 +54,27 @@ __device__ __forceinline__ void attn_rows_bf16(const uint16_t *__restrict__ q,
     const uint16_t *Vh = V + (int64_t)h * kv_head_stride;
     const uint16_t *qrow = q + ((int64_t)h * G + (col < G ? col : 0)) * kD;
     int vrow[4];
+    if constexpr (VTILE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vrow[i] = __shfl(rowV, 16 * wave + 4 * i + kq);
+        for (int i = 0; i < 4; ++i) vrow[i] = __shfl(rowV, 16 * wave + 4 * i + kq);
+    }
     u32x4 kb[4], qa[4], vb[4];
+    uint32_t vv[VTILE ? 1 : kAttnRows];
 #pragma unroll
     for (int t = 0; t < 4; ++t) kb[t] = *(const u32x4 *)(Kh + (int64_t)rowK * kD + 32 * t + 8 * kq);
 #pragma unroll
     for (int t = 0; t < 4; ++t) qa[t] = *(const u32x4 *)(qrow + 32 * t + 8 * kq);
+    if constexpr (VTILE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vb[i] = *(const u32x4 *)(Vh + (int64_t)vrow[i] * kD + 8 * col);
+        for (int i = 0; i < 4; ++i)
+            vb[i] = *(const u32x4 *)(Vh + (int64_t)vrow[i] * kD + 8 * col);
+    } else {
+#pragma unroll
+        for (int r = 0; r < kAttnRows; ++r) {
+            const int row = __builtin_amdgcn_readlane(rowV, r);
+            vv[r] = *(const uint32_t *)(Vh + (int64_t)row * kD + 2 * lane);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (SYNC) __syncthreads();
 
@@ -75,8 +91,10 @@ __device__ __forceinline__ void attn_rows_bf16(const uint16_t *__restrict__ q,
         const int g = 4 * kq + i;
         if (g < G) zs[g][16 * wave + col] = okK ? acc4[i] * fscale : -INFINITY;
     }
+    if constexpr (VTILE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4 *)&sv[16 * wave + 4 * i + kq][4 * col] = vb[i];
+        for (int i = 0; i < 4; ++i) *(u32x4 *)&sv[16 * wave + 4 * i + kq][4 * col] = vb[i];
+    }
     __syncthreads();
 
     for (int g = wave; g < G; g += 4) {
@@ -95,7 +113,7 @@ __device__ __forceinline__ void attn_rows_bf16(const uint16_t *__restrict__ q,
 #pragma unroll
         for (int r = 0; r < kAttnRows; ++r) {
             const float pr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p), r));
-            const uint32_t vw = sv[r][lane];
+            const uint32_t vw = VTILE ? sv[r][lane] : vv[VTILE ? 0 : r];
             a0 += pr * bf16_lo(vw);
             a1 += pr * bf16_hi(vw);
         }

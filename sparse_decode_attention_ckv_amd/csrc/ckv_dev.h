@@ -197,6 +197,7 @@ struct AttnPlan {
     int64_t kv_head_stride, kv_rows;
     double scale;
     void *partials;           // [H*G][S][2 + d] (float for bf16, double for f32)
+    bool host_kv;             // K and V in pinned host memory (bf16: V gathered for the link)
 };
 hipError_t launch_attn(const AttnPlan &p, const void *q, const void *K, const void *V,
                        const int32_t *idx, const int32_t *n_sel, float *o, hipStream_t s);

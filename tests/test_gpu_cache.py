@@ -57,7 +57,10 @@ def _run_stream(wl, L, heads, C, B, R, steps, rho, host=True):
         cK, cV = ck.ckv_cache_step(desc, t, idx, ns, asg, off, tok, Ks, Vs, st)
         o_c = ck.ckv_sparse_attn(Q[t], cK, cV, st["idx_cache"], ns, kv_rows=rows)
         o_d = ck.ckv_sparse_attn(Q[t], Kd, Vd, idx, ns)
+        # the same rows read directly from pinned host memory (no cache)
+        o_h = ck.ckv_sparse_attn(Q[t], Ks, Vs, idx, ns) if host else o_d
         torch.cuda.synchronize()
+        assert torch.equal(o_h, o_d), t
         idx_n, ns_n = idx.cpu().numpy(), ns.cpu().numpy()
         want = oc.step(hist, idx_n, ns_n, asg_n, off_n, tok_n, wl.n_sink, R)
         hist = want["history"]
