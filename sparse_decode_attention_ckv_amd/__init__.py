@@ -428,7 +428,7 @@ def ckv_select_attn(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch
     nb = lib.ckv_select_attn_workspace(ct.byref(sd), ct.byref(ad))
     ws = _workspace(nb, dev, workspace)
     _check(lib.ckv_select_attn(ct.byref(sd), ct.byref(ad), _ptr(q), _ptr(centroids),
-                               _ptr(csr_offsets), _ptr(csr_tokens), _ptr(K), _ptr(V), _ptr(idx),
+                               _ptr(csr_offsets), _ptr(csr_tokens), _kv_ptr(K), _kv_ptr(V), _ptr(idx),
                                _ptr(n_sel), _ptr(out), _ptr(ws), nb, _stream(stream)),
            "ckv_select_attn")
     return idx, n_sel, out

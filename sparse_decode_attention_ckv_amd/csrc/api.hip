@@ -168,16 +168,6 @@ void plan_attn(const ckv_attn_desc *d, AttnPlan *p, void *partials) {
     p->host_kv = false;
 }
 
-// Whether p points into host memory mapped for the device (pinned host
-// memory, read over the host link).
-bool host_memory(const void *p) {
-    hipPointerAttribute_t a;
-    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    return a.type == hipMemoryTypeHost;
-}
 
 // the two descriptors of one decode step describe the same problem
 int check_select_attn(const ckv_select_desc *s, const ckv_attn_desc *a) {
@@ -245,9 +235,10 @@ void plan_cache(const ckv_cache_desc *d, CachePlan *p, void *ws) {
 // The address at which a kernel reads `p`: device memory as is, pinned host
 // memory (hipHostMalloc) through its device mapping. Anything else (pageable
 // host memory, unknown pointers) is refused, so no kernel is handed an
-// address it cannot read.
-int device_view(const void *p, const void **out) {
+// address it cannot read. *host (if given) tells which of the two it is.
+int device_view(const void *p, const void **out, bool *host = nullptr) {
     if (!p) return CKV_ERR_INVALID_ARG;
+    if (host) *host = false;
     hipPointerAttribute_t a;
     if (hipPointerGetAttributes(&a, p) != hipSuccess) {
         (void)hipGetLastError();
@@ -258,6 +249,7 @@ int device_view(const void *p, const void **out) {
         return CKV_OK;
     }
     if (a.type == hipMemoryTypeHost && a.devicePointer) {
+        if (host) *host = true;
         const char *hb = (const char *)a.hostPointer;
         const char *db = (const char *)a.devicePointer;
         *out = (hb && (const char *)p >= hb) ? db + ((const char *)p - hb) : db;
@@ -354,10 +346,17 @@ int ckv_sparse_attn(const ckv_attn_desc *desc, const void *q, const void *K, con
         !stride_ok(desc->kv_head_stride, desc->dtype))
         return CKV_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < attn_bytes(desc)) return CKV_ERR_WORKSPACE;
+    // K and V as the kernels read them (pinned host memory through its device
+    // mapping; pageable host memory and unknown pointers are refused)
+    const void *Kd, *Vd;
+    bool hk, hv;
+    if (device_view(K, &Kd, &hk) != CKV_OK || device_view(V, &Vd, &hv) != CKV_OK)
+        return CKV_ERR_INVALID_ARG;
+    if (!aligned16(Kd) || !aligned16(Vd)) return CKV_ERR_INVALID_ARG;
     AttnPlan p;
     plan_attn(desc, &p, workspace);
-    p.host_kv = host_memory(K);
-    return launch_status(launch_attn(p, q, K, V, idx, n_sel, o, (hipStream_t)stream));
+    p.host_kv = hk || hv;
+    return launch_status(launch_attn(p, q, Kd, Vd, idx, n_sel, o, (hipStream_t)stream));
 }
 
 size_t ckv_select_attn_workspace(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc) {
@@ -379,12 +378,18 @@ int ckv_select_attn(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc, co
         return CKV_ERR_INVALID_ARG;
     const size_t sb = select_bytes(sdesc);
     if (!workspace || workspace_bytes < sb + attn_bytes(adesc)) return CKV_ERR_WORKSPACE;
+    const void *Kd, *Vd;
+    bool hk, hv;
+    if (device_view(K, &Kd, &hk) != CKV_OK || device_view(V, &Vd, &hv) != CKV_OK)
+        return CKV_ERR_INVALID_ARG;
+    if (!aligned16(Kd) || !aligned16(Vd)) return CKV_ERR_INVALID_ARG;
     SelectPlan sp;
     plan_select(sdesc, &sp, workspace);
     AttnPlan ap;
     plan_attn(adesc, &ap, (char *)workspace + sb);
-    return launch_status(launch_select_attn(sp, ap, q, centroids, csr_offsets, csr_tokens, K, V,
-                                            idx, n_sel, o, (hipStream_t)stream));
+    ap.host_kv = hk || hv;
+    return launch_status(launch_select_attn(sp, ap, q, centroids, csr_offsets, csr_tokens, Kd,
+                                            Vd, idx, n_sel, o, (hipStream_t)stream));
 }
 
 int ckv_device_view(const void *ptr, const void **device_ptr) {

@@ -20,7 +20,7 @@
 
 namespace ckv {
 
-template <int CMAX, int G>
+template <int CMAX, int G, bool VTILE>
 __global__ __launch_bounds__(kCutThreads) void k_sel_attn_bf16(
     const double *__restrict__ scores, int C, const int32_t *__restrict__ offsets, int c_cap,
     const int32_t *__restrict__ tokens, int64_t t_cap, int n_sink, int64_t pending_begin,
@@ -55,15 +55,18 @@ __global__ __launch_bounds__(kCutThreads) void k_sel_attn_bf16(
     const int rk = 16 * wave + (lane & 15);
     const int tkK = __shfl(r.val, rk);
     const bool okK = s * kSelSlice + rk < n && tkK >= 0 && (int64_t)tkK < kv_rows;
-    attn_rows_bf16<G, true>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK, rowV, fscale, part,
-                            NS, s, zs, U.sv);
+    attn_rows_bf16<G, true, VTILE>(q, K, V, kv_head_stride, h, okK ? tkK : 0, okK, rowV, fscale,
+                                   part, NS, s, zs, U.sv);
 }
 
 template <int CMAX, int G>
 static void launch_fused_g(const SelectPlan &sp, const AttnPlan &ap, const void *q,
                            const int32_t *offsets, const int32_t *tokens, const void *K,
                            const void *V, int32_t *idx, int32_t *n_sel, hipStream_t s) {
-    hipLaunchKernelGGL((k_sel_attn_bf16<CMAX, G>), dim3(xcd_head_grid(sp.H, ap.S)),
+    // pinned host K/V: the V gather that keeps more requests in flight on the link
+    hipLaunchKernelGGL((ap.host_kv ? &k_sel_attn_bf16<CMAX, G, false>
+                                   : &k_sel_attn_bf16<CMAX, G, true>),
+                       dim3(xcd_head_grid(sp.H, ap.S)),
                        dim3(kCutThreads), 0, s, sp.scores, sp.C, offsets, sp.c_cap, tokens,
                        sp.t_cap, sp.n_sink, sp.pending_begin, sp.n_pending, sp.B, idx, n_sel,
                        (const uint16_t *)q, (const uint16_t *)K, (const uint16_t *)V,

@@ -2,6 +2,8 @@
 must be bitwise what ckv_select followed by ckv_sparse_attn produce on the
 same inputs, and match the oracle (selection bit-exact, attention within
 2e-3 for bf16 and 1e-5 for fp32 of the exact fp64 attention)."""
+import ctypes as ct
+
 import numpy as np
 import pytest
 import torch
@@ -119,3 +121,55 @@ def test_fused_on_gpu_clusters_full_size_and_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(fidx, idx) and torch.equal(fns, ns) and torch.equal(fo, o), rep
+
+
+def test_host_kv_and_pageable_refusal():
+    """K/V in pinned host memory: the fused step and the separate attention
+    read them through their device mapping (the gather pattern for the host
+    link) and give the device results bitwise. Pageable host memory is
+    refused before anything is launched, by the binding and by the C entry
+    points themselves."""
+    say("fused and separate attention over pinned host K/V; pageable K/V refused")
+    rng = np.random.default_rng(11)
+    H, G, C, Lp, B, n_sink = 3, 4, 57, 3000, 700, 16
+    mu = (rng.standard_normal((H, C, D)) * 2).astype(np.float32)
+    off, tok = _random_csr(rng, H, C, Lp, n_sink)
+    L = n_sink + Lp
+    Kd = to_dev(synth.bf16_bits(rng.standard_normal((H, L, D)) * 2), "bf16")
+    Vd = to_dev(synth.bf16_bits(rng.standard_normal((H, L, D))), "bf16")
+    qd = to_dev(synth.bf16_bits(rng.standard_normal((H * G, D)) * 3), "bf16")
+    mud, offd, tokd = (torch.from_numpy(x).to(DEV) for x in (mu, off, tok))
+    Kh = torch.empty(Kd.shape, dtype=Kd.dtype, pin_memory=True)
+    Vh = torch.empty(Vd.shape, dtype=Vd.dtype, pin_memory=True)
+    Kh.copy_(Kd.cpu())
+    Vh.copy_(Vd.cpu())
+    idx, ns, o = ck.ckv_select_attn(qd, mud, offd, tokd, C, B, Kd, Vd)
+    hidx, hns, ho = ck.ckv_select_attn(qd, mud, offd, tokd, C, B, Kh, Vh)
+    so = ck.ckv_sparse_attn(qd, Kh, Vh, idx, ns)
+    torch.cuda.synchronize()
+    assert torch.equal(hidx, idx) and torch.equal(hns, ns)
+    assert torch.equal(ho, o) and torch.equal(so, o)
+
+    Kp, Vp = Kd.cpu(), Vd.cpu()                       # pageable
+    assert not Kp.is_pinned()
+    with pytest.raises(ck.CKVError):
+        ck.ckv_select_attn(qd, mud, offd, tokd, C, B, Kp, Vp)
+    with pytest.raises(ck.CKVError):
+        ck.ckv_sparse_attn(qd, Kp, Vp, idx, ns)
+    lib = ck.load()
+    sd = ck.SelectDesc(H=H, G=G, d=D, C=C, c_cap=C, n_sink=n_sink, t_cap=tokd.shape[1],
+                       pending_begin=0, n_pending=0, B=B, dtype=ck.CKV_BF16)
+    ad = ck.AttnDesc(H=H, G=G, d=D, B=B, kv_head_stride=Kd.stride(0), kv_rows=L, scale=0.0,
+                     dtype=ck.CKV_BF16)
+    ws = torch.empty(ck.ckv_select_attn_workspace(sd, ad), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(o)
+    p = lambda t: ct.c_void_p(t.data_ptr())
+    st = lib.ckv_select_attn(ct.byref(sd), ct.byref(ad), p(qd), p(mud), p(offd), p(tokd), p(Kp),
+                             p(Vp), p(idx), p(ns), p(out), p(ws), ws.numel(),
+                             ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == ck.CKV_ERR_INVALID_ARG
+    wa = torch.empty(ck.ckv_attn_workspace(ad), dtype=torch.uint8, device=DEV)
+    st = lib.ckv_sparse_attn(ct.byref(ad), p(qd), p(Kp), p(Vp), p(idx), p(ns), p(out), p(wa),
+                             wa.numel(), ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == ck.CKV_ERR_INVALID_ARG
+    torch.cuda.synchronize()
