@@ -145,6 +145,15 @@ def _need(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+def _on_gpu(**tensors):
+    """Every tensor a kernel reads or writes as device memory must live on the
+    GPU: a host address handed to a kernel would fault. (K and V of the
+    attention may also be pinned host tensors; they go through
+    ckv_device_view instead.)"""
+    for name, t in tensors.items():
+        _need(t is None or t.is_cuda, f"{name} must be a GPU tensor")
+
+
 def _rows(t: torch.Tensor, name: str):
     """[H][rows][d] tensor with contiguous rows; returns head stride (elements)."""
     _need(t.dim() == 3 and t.stride(2) == 1 and t.stride(1) == t.shape[2],
@@ -198,6 +207,8 @@ def ckv_cluster(K: torch.Tensor, n_sink: int, C: int, iters: int, *, token_base:
     csr_offsets [H][c_cap+1] int32, csr_tokens [H][t_cap] int32). Passing
     existing buffers with c_base / t_base appends a window's clusters to them.
     """
+    _on_gpu(K=K, centroids=centroids, assign=assign, csr_offsets=csr_offsets,
+            csr_tokens=csr_tokens, workspace=workspace)
     lib = load()
     hs = _rows(K, "K")
     H, L, d = K.shape
@@ -245,6 +256,8 @@ def ckv_select(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch.Tens
 
     q [H*G][d]; centroids [H][c_cap][d] fp32; csr_offsets [H][c_cap+1];
     csr_tokens [H][t_cap]. Returns (idx [H][B] int32, n_sel [H] int32)."""
+    _on_gpu(q=q, centroids=centroids, csr_offsets=csr_offsets, csr_tokens=csr_tokens, idx=idx,
+            n_sel=n_sel, workspace=workspace)
     lib = load()
     H, c_cap, d = centroids.shape
     _need(q.dim() == 2 and q.is_contiguous() and q.shape[1] == d and q.shape[0] % H == 0,
@@ -293,6 +306,7 @@ def ckv_sparse_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torc
     q [H*G][d]; K, V [H][rows][d] (same strides; device tensors, or pinned
     host tensors read through their device mapping); idx [H][B]; returns
     o [H*G][d] fp32."""
+    _on_gpu(q=q, idx=idx, n_sel=n_sel, out=out, workspace=workspace)
     lib = load()
     hs = _rows(K, "K")
     _need(V.shape == K.shape and V.stride() == K.stride() and V.dtype == K.dtype,
@@ -367,6 +381,7 @@ def ckv_cache_step(desc: CacheDesc, step: int, idx: torch.Tensor, n_sel: torch.T
     ["cache_V"] then holds the rows selected in the last R steps and
     state["idx_cache"] the slots of this step's selection. Returns the
     (K, V) views of that buffer."""
+    _on_gpu(**{k: v for k, v in state.items() if isinstance(v, torch.Tensor)})
     for t, n in ((idx, "idx"), (n_sel, "n_sel"), (assign, "assign"), (csr_offsets, "csr_offsets"),
                  (csr_tokens, "csr_tokens")):
         _need(t.dtype == torch.int32 and t.is_contiguous() and t.is_cuda, f"bad {n}")
@@ -394,6 +409,8 @@ def ckv_select_attn(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch
 
     Arguments as in those two calls. Returns (idx [H][B] int32, n_sel [H]
     int32, o [H*G][d] fp32), bitwise what the separate calls return."""
+    _on_gpu(q=q, centroids=centroids, csr_offsets=csr_offsets, csr_tokens=csr_tokens, idx=idx,
+            n_sel=n_sel, out=out, workspace=workspace)
     lib = load()
     H, c_cap, d = centroids.shape
     hs = _rows(K, "K")

@@ -12,6 +12,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import sparse_decode_attention_ckv_amd as ck
 
@@ -267,3 +268,24 @@ def test_cache_sizes_and_pointer_checks():
         assert lib.ckv_cache_step(ct.byref(d), 0, *bad, FAKE, ws, None) == ck.CKV_ERR_INVALID_ARG
     assert lib.ckv_cache_step(ct.byref(d), -1, *ptrs, FAKE, ws, None) == ck.CKV_ERR_INVALID_ARG
     assert lib.ckv_device_view(FAKE, None) == ck.CKV_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """A CPU tensor where a kernel reads or writes device memory is refused by
+    the binding (ValueError) before the library or the GPU is touched."""
+    d = 128
+    q = torch.zeros(4, d, dtype=torch.bfloat16)
+    K = torch.zeros(1, 64, d, dtype=torch.bfloat16)
+    cent = torch.zeros(1, 3, d)
+    off = torch.zeros(1, 4, dtype=torch.int32)
+    tok = torch.zeros(1, 48, dtype=torch.int32)
+    idx = torch.zeros(1, 32, dtype=torch.int32)
+    ns = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ck.ckv_cluster(K, 16, 3, 1)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ck.ckv_select(q, cent, off, tok, 3, 32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ck.ckv_sparse_attn(q, K, K, idx, ns)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ck.ckv_select_attn(q, cent, off, tok, 3, 32, K, K)
