@@ -128,7 +128,8 @@ typedef struct {
 size_t ckv_cluster_workspace(const ckv_cluster_desc *desc);
 
 /* K: window row 0 of head 0, element type desc->dtype, row r of head h at
- * K + (h * k_head_stride + r) * d. */
+ * K + (h * k_head_stride + r) * d. Device memory, or pinned host memory (read
+ * through its device mapping); any other pointer is CKV_ERR_INVALID_ARG. */
 int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
                 int32_t *assign, int32_t *csr_offsets, int32_t *csr_tokens,
                 void *workspace, size_t workspace_bytes, void *stream);

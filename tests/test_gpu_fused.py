@@ -173,3 +173,34 @@ def test_host_kv_and_pageable_refusal():
                              wa.numel(), ct.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == ck.CKV_ERR_INVALID_ARG
     torch.cuda.synchronize()
+
+
+def test_cluster_reads_pinned_host_keys_and_refuses_pageable():
+    """ckv_cluster over pinned host keys (read through their device mapping)
+    equals the clustering of the same keys in device memory; a pageable host
+    pointer is refused by the C entry point before anything is launched."""
+    say("ckv_cluster over pinned host keys; pageable keys refused")
+    wl = synth.workload(1)
+    K, _, _ = synth.make_kv(wl, L=2064, heads=range(2))
+    Kd = to_dev(K, "bf16")
+    ref = gpu_cluster(Kd, 16, 25, 3)
+    Kh = torch.empty(Kd.shape, dtype=Kd.dtype, pin_memory=True)
+    Kh.copy_(Kd.cpu())
+    outs = [torch.empty_like(x) for x in ref]
+    desc = ck.ClusterDesc(H=2, d=D, L=Kd.shape[1], k_head_stride=Kd.stride(0), token_base=0,
+                          n_sink=16, C=25, iters=3, dtype=ck.CKV_BF16, c_base=0, c_cap=25,
+                          t_base=0, t_cap=Kd.shape[1] - 16, metric=ck.CKV_COSINE)
+    lib = ck.load()
+    ws = torch.empty(max(ck.ckv_cluster_workspace(desc), 1), dtype=torch.uint8, device=DEV)
+    p = lambda t: ct.c_void_p(t.data_ptr())
+    stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st = lib.ckv_cluster(ct.byref(desc), p(Kh), *(p(x) for x in outs), p(ws), ws.numel(), stream)
+    torch.cuda.synchronize()
+    assert st == ck.CKV_OK
+    for a, b in zip(outs, ref):
+        assert torch.equal(a, b)
+    Kp = Kd.cpu()
+    assert not Kp.is_pinned()
+    st = lib.ckv_cluster(ct.byref(desc), p(Kp), *(p(x) for x in outs), p(ws), ws.numel(), stream)
+    assert st == ck.CKV_ERR_INVALID_ARG
+    torch.cuda.synchronize()
