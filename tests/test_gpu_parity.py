@@ -284,6 +284,50 @@ def test_cluster_append_increment():
             f"{np.mean(a_g == r['assign']):.4f}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_cluster_append_random(seed):
+    """Seeded appends: prompt and window lengths, cluster counts (even seeds
+    through the one-launch small-window kernel, odd ones through the general
+    path), window sinks, iterations, and a strided window view into the cache.
+    The appended segment must be bitwise the window clustered alone, shifted
+    by c_base, t_base and token_base, and nothing before it may change."""
+    r = np.random.default_rng(7700 + seed)
+    wl = synth.workload(3)
+    H = int(r.integers(1, 4))
+    L0 = int(r.integers(600, 4000))
+    C0 = int(r.integers(2, 300))
+    small = seed % 2 == 0
+    ws = int(r.choice([0, 0, 5]))
+    Lw = ws + (int(r.integers(40, 1025)) if small else int(r.integers(1100, 3000)))
+    Cw = int(r.integers(1, 17)) if small else int(r.integers(17, 300))
+    iters = int(r.integers(1, 6))
+    say(f"cluster append seed {seed}: H={H} prompt {L0} rows C={C0}, window {Lw} rows "
+        f"(sinks {ws}) C={Cw}, {iters} iterations")
+    Kd, _, _, _ = _kv(wl, L0 + Lw, heads=range(H))
+    c_cap, t_cap = C0 + Cw, (L0 - 16) + (Lw - ws)
+    cent = torch.zeros((H, c_cap, D), dtype=torch.float32, device=DEV)
+    off = torch.zeros((H, c_cap + 1), dtype=torch.int32, device=DEV)
+    tok = torch.zeros((H, t_cap), dtype=torch.int32, device=DEV)
+    asg0 = torch.empty((H, L0), dtype=torch.int32, device=DEV)
+    ck.ckv_cluster(Kd[:, :L0], 16, C0, 3, centroids=cent, assign=asg0, csr_offsets=off,
+                   csr_tokens=tok)
+    torch.cuda.synchronize()
+    before = (cent.clone(), off.clone(), tok.clone())
+    win = Kd[:, L0:L0 + Lw]                       # strided view into the cache
+    asg1 = torch.empty((H, Lw), dtype=torch.int32, device=DEV)
+    ck.ckv_cluster(win, ws, Cw, iters, token_base=L0, centroids=cent, assign=asg1,
+                   csr_offsets=off, csr_tokens=tok, c_base=C0, t_base=L0 - 16)
+    rc, ra, ro, rt = gpu_cluster(win.contiguous(), ws, Cw, iters, token_base=L0)
+    torch.cuda.synchronize()
+    assert torch.equal(cent[:, :C0], before[0][:, :C0])
+    assert torch.equal(off[:, :C0 + 1], before[1][:, :C0 + 1])
+    assert torch.equal(tok[:, :L0 - 16], before[2][:, :L0 - 16])
+    assert torch.equal(cent[:, C0:], rc)
+    assert torch.equal(asg1, ra)
+    assert torch.equal(off[:, C0:], ro + (L0 - 16))
+    assert torch.equal(tok[:, L0 - 16:], rt)
+
+
 def test_cluster_full_size_sampled_and_deterministic():
     """Llama-8B-shaped layer at 32k (8 KV heads, C=409, 10 iterations) in the
     launch configuration the benchmark times; labels checked on a token
