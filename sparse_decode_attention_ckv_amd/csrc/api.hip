@@ -291,15 +291,15 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
     if (!K || !centroids || !assign || !csr_offsets || !csr_tokens) return CKV_ERR_INVALID_ARG;
     if (!aligned16(K) || !aligned16(centroids) || !stride_ok(desc->k_head_stride, desc->dtype))
         return CKV_ERR_INVALID_ARG;
+    ClusterPlan p;
+    size_t need;
+    plan_cluster(desc, &p, &need, (char *)workspace);
+    if (!workspace || workspace_bytes < need) return CKV_ERR_WORKSPACE;
     // K as the kernels read it: device memory, or pinned host memory through
     // its device mapping; pageable host memory and unknown pointers are refused
     const void *Kv;
     if (device_view(K, &Kv) != CKV_OK || !aligned16(Kv)) return CKV_ERR_INVALID_ARG;
     K = Kv;
-    ClusterPlan p;
-    size_t need;
-    plan_cluster(desc, &p, &need, (char *)workspace);
-    if (!workspace || workspace_bytes < need) return CKV_ERR_WORKSPACE;
     p.n_cu = device_cu_count();
     hipStream_t s = (hipStream_t)stream;
 
