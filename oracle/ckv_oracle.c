@@ -89,9 +89,10 @@ static double orc_sumsq(const double *x, int d)
 
 /* Unit vector of x, for the cosine distance D(i,j) = 1 - <k_i,k_j>/(|k_i||k_j|)
  * [Clustering in semantic space]. A zero vector maps to zero (its cosine
- * with anything is taken as 0).
- *   EXACT : x_j / sqrt(|x|^2) in fp64.
- *   MIRROR: bf16(fp32(x_j * r)), r = 1 / sqrt(|x|^2) in fp64. */
+ * with anything is taken as 0). |x| = sqrt of the fp64 chain above, and
+ * the quotient x_j / |x| is one fp64 division.
+ *   EXACT : the fp64 quotient.
+ *   MIRROR: bf16(fp32(quotient)), nearest-even both times. */
 static void orc_unit(const double *x, int d, int mode, double *out)
 {
     double ss = orc_sumsq(x, d);
@@ -99,12 +100,10 @@ static void orc_unit(const double *x, int d, int mode, double *out)
         for (int j = 0; j < d; ++j) out[j] = 0.0;
         return;
     }
-    if (mode == ORC_EXACT) {
-        double n = sqrt(ss);
-        for (int j = 0; j < d; ++j) out[j] = x[j] / n;
-    } else {
-        double r = 1.0 / sqrt(ss);
-        for (int j = 0; j < d; ++j) out[j] = (double)orc_round_bf16((float)(x[j] * r));
+    double n = sqrt(ss);
+    for (int j = 0; j < d; ++j) {
+        double u = x[j] / n;
+        out[j] = (mode == ORC_EXACT) ? u : (double)orc_round_bf16((float)u);
     }
 }
 

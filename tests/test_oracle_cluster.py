@@ -141,16 +141,115 @@ def test_fixed_point_repeats_exactly():
     assert np.array_equal(r3["tokens"], r9["tokens"])
 
 
+def _bf16_of_fp32_of_quotient(X):
+    """Independent path for the MIRROR operands: numpy's sequential fp64
+    sum of the exact squares (x_j^2 is exact in fp64 for fp32/bf16 inputs,
+    so this is the definition's fp64 chain), numpy's sqrt and division,
+    numpy's fp64 -> fp32 cast and torch's fp32 -> bf16 cast (both round to
+    nearest-even)."""
+    X = np.asarray(X, dtype=np.float64)
+    n = np.sqrt(np.cumsum(X * X, axis=1)[:, -1:])
+    u32 = (X / n).astype(np.float32)
+    return torch.from_numpy(u32).to(torch.bfloat16).double().numpy(), X / n
+
+
 def test_mirror_operands_are_bf16_of_fp32_of_unit_vector():
+    """Every MIRROR operand bit equals bf16(fl32(k_j / |k|)) computed by the
+    independent path, on keys drawn like the workload's (bf16 storage, fp32
+    storage and wide dynamic range). The sample must hold double-rounding
+    cases -- where rounding the fp64 quotient straight to bf16 gives another
+    value -- so that an oracle skipping the fp32 step would fail."""
     r = np.random.default_rng(6)
-    X = r.standard_normal((50, D)) * 20
+    wl = synth.workload(1)
+    hd = synth.make_head(wl, 0, L=4096)
+    X = np.concatenate([
+        hd.Kf,                                                         # bf16 keys
+        (r.standard_normal((2048, D)) * 20).astype(np.float32),       # fp32 keys
+        (r.standard_normal((2048, D)) * 10.0 ** r.uniform(-3, 3, (2048, 1))
+         ).astype(np.float32)]).astype(np.float64)
     u = oracle.unit_rows(X, mode=oracle.MIRROR)
-    ex = X / np.linalg.norm(X, axis=1, keepdims=True)
-    want = torch.from_numpy(ex.astype(np.float32)).to(torch.bfloat16).double().numpy()
-    # the oracle's fp64 norm differs from numpy's only in the last bits; the
-    # rounded operands agree except at a rounding boundary
-    assert np.mean(u == want) > 0.999
-    np.testing.assert_allclose(u, ex, atol=2 ** -8)
+    want, q = _bf16_of_fp32_of_quotient(X)
+    assert np.array_equal(u, want)
+    # fp64 -> bf16 in one rounding (nearest-even on the 8-bit significand)
+    m, e = np.frexp(q)
+    direct = np.ldexp(np.rint(m * 256.0) / 256.0, e)
+    assert np.count_nonzero(direct != want) > 0
+    # the EXACT operand is the fp64 quotient itself
+    assert np.array_equal(oracle.unit_rows(X, mode=oracle.EXACT), q)
+
+
+def test_mirror_operands_of_centroids_in_assignment():
+    """The assignment's margin is the fp64 dot product of the MIRROR operands:
+    with one key and two centroids it equals the difference of the two dot
+    products of the independently rounded unit rows."""
+    r = np.random.default_rng(11)
+    for _ in range(20):
+        k = r.standard_normal((1, D)) * 5
+        mu = r.standard_normal((2, D)) * 3
+        a, m = oracle.assign(k, 0, mu, mode=oracle.MIRROR)
+        ku, _ = _bf16_of_fp32_of_quotient(k)
+        mt, _ = _bf16_of_fp32_of_quotient(mu)
+        s = np.array([np.dot(ku[0], mt[c]) for c in range(2)])
+        assert a[0] == int(np.argmax(s))
+        assert abs(m[0] - abs(s[0] - s[1])) <= 1e-15
+
+
+def test_objective_closed_forms():
+    """J_w = sum_i (|k_i| - <k_i, mu_a>/|mu_a|), pinned by values that hold
+    whatever the data: a hand-worked 2-D case; C = L' with every token its
+    own centroid gives 0; C = 1 with the mean as centroid gives
+    sum |k_i| - |sum k_i|; a zero centroid contributes |k_i|; scaling the
+    keys by a scales J by a, scaling a centroid leaves J unchanged."""
+    # hand-worked: k = (3, 4), mu = (1, 0): |k| = 5, <k, mu>/|mu| = 3 -> 2;
+    # k = (0, 2), mu = (0, -7): 2 - (-2) = 4; sinks never count
+    K = np.array([[9.0, 9.0], [3.0, 4.0], [0.0, 2.0]])
+    mu = np.array([[1.0, 0.0], [0.0, -7.0]])
+    assert oracle.objective(K, 1, np.array([-1, 0, 1]), mu) == 6.0
+
+    r = np.random.default_rng(12)
+    n_sink, Lp = 4, 200
+    Kr = r.standard_normal((n_sink + Lp, D)) * 3
+    own = np.concatenate([-np.ones(n_sink, np.int32), np.arange(Lp, dtype=np.int32)])
+    J_own = oracle.objective(Kr, n_sink, own, Kr[n_sink:])
+    assert abs(J_own) <= 1e-12 * np.linalg.norm(Kr[n_sink:], axis=1).sum()
+
+    one = np.concatenate([-np.ones(n_sink, np.int32), np.zeros(Lp, np.int32)])
+    mean = Kr[n_sink:].mean(axis=0, keepdims=True)
+    want = np.linalg.norm(Kr[n_sink:], axis=1).sum() - np.linalg.norm(Kr[n_sink:].sum(axis=0))
+    got = oracle.objective(Kr, n_sink, one, mean)
+    assert abs(got - want) <= 1e-10 * abs(want), (got, want)
+
+    zero = np.zeros((1, D))
+    assert abs(oracle.objective(Kr, n_sink, one, zero)
+               - np.linalg.norm(Kr[n_sink:], axis=1).sum()) <= 1e-10 * Lp
+
+    lab = np.concatenate([-np.ones(n_sink, np.int32), r.integers(0, 5, Lp).astype(np.int32)])
+    mu5 = r.standard_normal((5, D))
+    J = oracle.objective(Kr, n_sink, lab, mu5)
+    assert abs(oracle.objective(2.5 * Kr, n_sink, lab, mu5) - 2.5 * J) <= 1e-10 * abs(J)
+    assert abs(oracle.objective(Kr, n_sink, lab, mu5 * np.arange(1, 6)[:, None]) - J) \
+        <= 1e-10 * abs(J)
+    # the value matches the definition's terms summed independently
+    km = mu5[lab[n_sink:]]
+    terms = np.linalg.norm(Kr[n_sink:], axis=1) - np.einsum(
+        "ij,ij->i", Kr[n_sink:], km) / np.linalg.norm(km, axis=1)
+    assert abs(J - terms.sum()) <= 1e-10 * np.abs(terms).sum()
+
+
+def test_objective_trace_is_the_objective_of_each_state():
+    """The trace's entries are J_w of the partition after each assignment
+    (against the centroids it was assigned with) and after each update
+    (against the new means): recompute both from oracle.assign/update."""
+    wl = synth.workload(0)
+    hd = synth.make_head(wl, 0, L=600)
+    C, iters, n_sink = 7, 4, 16
+    r = oracle.cluster(hd.Kf, n_sink, C, iters, mode=oracle.EXACT, trace=True)
+    mu = oracle.init_centroids(hd.Kf, n_sink, C)
+    for t in range(iters):
+        a, _ = oracle.assign(hd.Kf, n_sink, mu, mode=oracle.EXACT)
+        assert r["trace"][2 * t] == oracle.objective(hd.Kf, n_sink, a, mu)
+        mu = oracle.update(hd.Kf, n_sink, a, mu, mode=oracle.EXACT)
+        assert r["trace"][2 * t + 1] == oracle.objective(hd.Kf, n_sink, a, mu)
 
 
 def test_incremental_window_labels_and_absolute_ids():
