@@ -287,8 +287,11 @@ int ckv_select_attn(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc, co
  * read from K_src/V_src, selected clusters found whole in the cache,
  * selected clusters, selected entries without a slot. ckv_sparse_attn with
  * K, V = buffer step & 1 (kv_head_stride rows * d, kv_rows = rows) and idx =
- * idx_cache then gives the attention of the step, bitwise equal to the one
- * over K_src/V_src with idx (same rows, same order).
+ * idx_cache leaves out every entry without a slot (-1). When a head has none
+ * (stats[h][4] == 0, always the case for a selection without pending rows,
+ * n_pending == 0), that attention is bitwise equal to the one over
+ * K_src/V_src with idx (same rows, same order); with pending rows it is not,
+ * and the caller must attend those rows from where they live.
  *
  * Workspace: ckv_cache_workspace() bytes. Two launches on `stream`.
  */

@@ -14,6 +14,7 @@ budget B) and sparse decode attention softmax(q K_S^T / sqrt(d)) V_S.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as ct
 import os
 from typing import Optional
@@ -166,14 +167,24 @@ def _check(status: int, where: str):
         raise CKVError(status, where)
 
 
-def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
-    """Caller workspace, a fresh one, or None when the call needs none."""
+def _alloc_on(stream):
+    """Allocations a call makes for itself (workspace, default outputs) are
+    made on the stream its kernels run on, so that torch's caching allocator
+    never hands their memory to another stream while those kernels may still
+    use it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], stream=None):
+    """Caller workspace, a fresh one (on the call's stream), or None when the
+    call needs none."""
     if ws is not None:
         _need(ws.is_cuda and ws.numel() * ws.element_size() >= nbytes, "workspace too small")
         return ws
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with _alloc_on(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ calls --
@@ -214,14 +225,15 @@ def ckv_cluster(K: torch.Tensor, n_sink: int, C: int, iters: int, *, token_base:
     H, L, d = K.shape
     dev = K.device
     Lp = L - n_sink
-    if centroids is None:
-        centroids = torch.empty((H, c_base + C, d), dtype=torch.float32, device=dev)
-    if csr_offsets is None:
-        csr_offsets = torch.empty((H, centroids.shape[1] + 1), dtype=torch.int32, device=dev)
-    if csr_tokens is None:
-        csr_tokens = torch.empty((H, t_base + Lp), dtype=torch.int32, device=dev)
-    if assign is None:
-        assign = torch.empty((H, L), dtype=torch.int32, device=dev)
+    with _alloc_on(stream):
+        if centroids is None:
+            centroids = torch.empty((H, c_base + C, d), dtype=torch.float32, device=dev)
+        if csr_offsets is None:
+            csr_offsets = torch.empty((H, centroids.shape[1] + 1), dtype=torch.int32, device=dev)
+        if csr_tokens is None:
+            csr_tokens = torch.empty((H, t_base + Lp), dtype=torch.int32, device=dev)
+        if assign is None:
+            assign = torch.empty((H, L), dtype=torch.int32, device=dev)
     _need(centroids.dtype == torch.float32 and centroids.is_contiguous()
           and centroids.shape[0] == H and centroids.shape[2] == d, "bad centroids buffer")
     _need(csr_offsets.dtype == torch.int32 and csr_offsets.is_contiguous()
@@ -240,7 +252,7 @@ def ckv_cluster(K: torch.Tensor, n_sink: int, C: int, iters: int, *, token_base:
         _check(lib.ckv_cluster(ct.byref(desc), _ptr(K), _ptr(centroids), _ptr(assign),
                                _ptr(csr_offsets), _ptr(csr_tokens), None, 0, _stream(stream)),
                "ckv_cluster")
-    ws = _workspace(nb, dev, workspace)
+    ws = _workspace(nb, dev, workspace, stream)
     _check(lib.ckv_cluster(ct.byref(desc), _ptr(K), _ptr(centroids), _ptr(assign),
                            _ptr(csr_offsets), _ptr(csr_tokens), _ptr(ws), nb, _stream(stream)),
            "ckv_cluster")
@@ -268,17 +280,18 @@ def ckv_select(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch.Tens
     _need(csr_tokens.dtype == torch.int32 and csr_tokens.is_contiguous()
           and csr_tokens.shape[0] == H, "bad csr_tokens")
     dev = q.device
-    if idx is None:
-        idx = torch.empty((H, B), dtype=torch.int32, device=dev)
-    if n_sel is None:
-        n_sel = torch.empty((H,), dtype=torch.int32, device=dev)
+    with _alloc_on(stream):
+        if idx is None:
+            idx = torch.empty((H, B), dtype=torch.int32, device=dev)
+        if n_sel is None:
+            n_sel = torch.empty((H,), dtype=torch.int32, device=dev)
     _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.shape == (H, B), "bad idx")
     _need(n_sel.dtype == torch.int32 and n_sel.numel() == H, "bad n_sel")
     desc = SelectDesc(H=H, G=q.shape[0] // H, d=d, C=C, c_cap=c_cap, n_sink=n_sink,
                       t_cap=csr_tokens.shape[1], pending_begin=pending_begin,
                       n_pending=n_pending, B=B, dtype=_dtype_code(q))
     nb = lib.ckv_select_workspace(ct.byref(desc))
-    ws = _workspace(nb, dev, workspace)
+    ws = _workspace(nb, dev, workspace, stream)
     _check(lib.ckv_select(ct.byref(desc), _ptr(q), _ptr(centroids), _ptr(csr_offsets),
                           _ptr(csr_tokens), _ptr(idx), _ptr(n_sel), _ptr(ws), nb,
                           _stream(stream)), "ckv_select")
@@ -319,14 +332,15 @@ def ckv_sparse_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torc
     _need(n_sel.dtype == torch.int32 and n_sel.numel() == H, "bad n_sel")
     G = q.shape[0] // H
     if out is None:
-        out = torch.empty((H * G, d), dtype=torch.float32, device=q.device)
+        with _alloc_on(stream):
+            out = torch.empty((H * G, d), dtype=torch.float32, device=q.device)
     _need(out.dtype == torch.float32 and out.is_contiguous() and out.shape == (H * G, d),
           "bad out")
     desc = AttnDesc(H=H, G=G, d=d, B=idx.shape[1], kv_head_stride=hs,
                     kv_rows=rows if kv_rows is None else kv_rows, scale=scale,
                     dtype=_dtype_code(K))
     nb = lib.ckv_attn_workspace(ct.byref(desc))
-    ws = _workspace(nb, q.device, workspace)
+    ws = _workspace(nb, q.device, workspace, stream)
     _check(lib.ckv_sparse_attn(ct.byref(desc), _ptr(q), _kv_ptr(K), _kv_ptr(V), _ptr(idx),
                                _ptr(n_sel), _ptr(out), _ptr(ws), nb, _stream(stream)),
            "ckv_sparse_attn")
@@ -426,12 +440,13 @@ def ckv_select_attn(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch
           and csr_tokens.shape[0] == H, "bad csr_tokens")
     G = q.shape[0] // H
     dev = q.device
-    if idx is None:
-        idx = torch.empty((H, B), dtype=torch.int32, device=dev)
-    if n_sel is None:
-        n_sel = torch.empty((H,), dtype=torch.int32, device=dev)
-    if out is None:
-        out = torch.empty((H * G, d), dtype=torch.float32, device=dev)
+    with _alloc_on(stream):
+        if idx is None:
+            idx = torch.empty((H, B), dtype=torch.int32, device=dev)
+        if n_sel is None:
+            n_sel = torch.empty((H,), dtype=torch.int32, device=dev)
+        if out is None:
+            out = torch.empty((H * G, d), dtype=torch.float32, device=dev)
     _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.shape == (H, B), "bad idx")
     _need(n_sel.dtype == torch.int32 and n_sel.numel() == H, "bad n_sel")
     _need(out.dtype == torch.float32 and out.is_contiguous() and out.shape == (H * G, d),
@@ -443,7 +458,7 @@ def ckv_select_attn(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch
                   kv_rows=K.shape[1] if kv_rows is None else kv_rows, scale=scale,
                   dtype=_dtype_code(K))
     nb = lib.ckv_select_attn_workspace(ct.byref(sd), ct.byref(ad))
-    ws = _workspace(nb, dev, workspace)
+    ws = _workspace(nb, dev, workspace, stream)
     _check(lib.ckv_select_attn(ct.byref(sd), ct.byref(ad), _ptr(q), _ptr(centroids),
                                _ptr(csr_offsets), _ptr(csr_tokens), _kv_ptr(K), _kv_ptr(V), _ptr(idx),
                                _ptr(n_sel), _ptr(out), _ptr(ws), nb, _stream(stream)),

@@ -21,6 +21,8 @@
 // threads strided along the sequence, channels split into P partitions) is
 // replaced by the counting sort + segmented reduction: no atomics, so every
 // result is bitwise reproducible.
+#include <type_traits>
+
 #include "cluster_dev.h"
 
 namespace ckv {
@@ -29,21 +31,23 @@ namespace ckv {
 // Unit vector of a 128-element row held one element per thread (128 threads
 // of the block participate; others pass active=false). |x|^2 is one fp64
 // fused-multiply-add chain over j = 0..127 (evaluated by thread 0 in that
-// order), r = 1/sqrt(|x|^2) in fp64, and element j becomes fp32(x_j * r),
-// rounded once more to bf16 when BF16. A zero row stays zero.
+// order), |x| its fp64 square root, and element j becomes fp32(x_j / |x|)
+// (one fp64 division), rounded once more to bf16 when BF16. A zero row
+// stays zero.
 template <bool BF16>
 __device__ void block_unit_row(float x, bool active, int j, void *out_row,
-                               float *sx, double *sinv) {
+                               float *sx, double *snrm) {
     if (active) sx[j] = x;
     __syncthreads();
     if (threadIdx.x == 0) {
         double ss = 0.0;
         for (int k = 0; k < kD; ++k) ss = __fma_rn((double)sx[k], (double)sx[k], ss);
-        *sinv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+        *snrm = sqrt(ss);
     }
     __syncthreads();
     if (active) {
-        float y = (float)((double)x * *sinv);
+        const double n = *snrm;
+        float y = (n > 0.0) ? (float)((double)x / n) : 0.f;
         if (BF16)
             ((uint16_t *)out_row)[j] = (uint16_t)f32_to_bf16_rne(y);
         else
@@ -84,7 +88,8 @@ constexpr int kNkRows = 256;             // rows per workgroup (one per thread)
 constexpr int kNkStride = 17;            // LDS row stride in 16-byte chunks
 
 // One LDS row (16 chunks of 8 bf16): the chain over it (chunks in order),
-// then the unit row written back in place.
+// |x| its fp64 square root, then the unit row bf16(fp32(x_j / |x|)) written
+// back in place.
 __device__ __forceinline__ void nk_unit_row(u32x4 *row) {
     double ss = 0.0;
 #pragma unroll 2
@@ -94,14 +99,16 @@ __device__ __forceinline__ void nk_unit_row(u32x4 *row) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = __fma_rn((double)f[e], (double)f[e], ss);
     }
-    const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+    const double n = sqrt(ss);
+    const bool nz = ss > 0.0;
 #pragma unroll 4
     for (int i = 0; i < 16; ++i) {
         float f[8];
         unpack8(row[i], f);
         uint32_t o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne((float)((double)f[e] * inv));
+        for (int e = 0; e < 8; ++e)
+            o[e] = nz ? f32_to_bf16_rne((float)((double)f[e] / n)) : 0u;
         u32x4 v;
         v.x = o[0] | (o[1] << 16);
         v.y = o[2] | (o[3] << 16);
@@ -170,8 +177,8 @@ __global__ __launch_bounds__(256) void k_normalize_keys_f32(
     }
     double ss = 0.0;
     for (int j = 0; j < kD; ++j) ss = __fma_rn((double)src[j], (double)src[j], ss);
-    const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
-    for (int j = 0; j < kD; ++j) dst[j] = (float)((double)src[j] * inv);
+    const double n = sqrt(ss);
+    for (int j = 0; j < kD; ++j) dst[j] = (ss > 0.0) ? (float)((double)src[j] / n) : 0.f;
 }
 
 hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *assign,
@@ -199,7 +206,7 @@ __global__ __launch_bounds__(128) void k_init_centroids(
     float *__restrict__ cent, int c_base, int c_cap, void *__restrict__ mt,
     float *__restrict__ mb, int Cpad) {
     __shared__ float sx[kD];
-    __shared__ double sinv;
+    __shared__ double snrm;
     const int c = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
     const int64_t row = n_sink + (Lp / C) * (int64_t)c;
     const int64_t e = h * head_stride + row * kD + j;
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(128) void k_init_centroids(
     const int64_t mrow = ((int64_t)h * Cpad + c) * kD;
     void *out = BF16 ? (void *)((uint16_t *)mt + mrow) : (void *)((float *)mt + mrow);
     if (M == kCosine)
-        block_unit_row<BF16>(x, true, j, out, sx, &sinv);
+        block_unit_row<BF16>(x, true, j, out, sx, &snrm);
     else
         block_store_row<BF16, M == kL2>(x, j, out, sx, mb + (int64_t)h * Cpad + c);
 }
@@ -241,28 +248,47 @@ hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cen
 // assign (bf16): scores = Kt . Mt^T on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation, fused with a per-token argmax (ties -> lower cluster id).
 //
-// Persistent workgroups of 16 waves (four per SIMD, so one wave's argmax
-// VALU work and LDS reads overlap the others' MFMAs), one workgroup per CU,
-// each walking a contiguous range of 1024-token tiles (head-major, so
-// consecutive tiles share a head). Tokens sit on the MFMA N dimension,
-// clusters on M. Each wave owns 64 tokens of a tile: four 16-token N tiles
-// whose B fragments stay in registers while the wave sweeps every cluster.
-// The head's unit centroids sit in LDS, up to 512 clusters at a time (a
-// round), XOR-swizzled so the 16 lanes reading one 16-byte column of 16 rows
-// hit distinct banks; with a single round they are loaded once per head and
-// the waves then run without barriers. A tile's B fragments are requested
-// only after the centroids are in LDS: each wave then starts its MFMAs as
-// soon as its own rows arrive, instead of all waves waiting at the LDS
-// barrier for every wave's rows.
+// Persistent workgroups of 8 waves (two per SIMD, 256 registers each), one
+// per CU, each walking a contiguous range of 512-token tiles (head-major, so
+// consecutive tiles share a head and the workgroups of one XCD share a head's
+// centroids in L2). Tokens sit on the MFMA N dimension, clusters on M. Each
+// wave owns 64 tokens of a tile: four 16-token N tiles whose B fragments stay
+// in registers while the wave sweeps every cluster; the next tile's fragments
+// are requested into a second register set as soon as the current tile
+// starts, so the token rows arrive while the MFMAs run. The head's unit
+// centroids sit in LDS, up to 512 clusters at a time (a round), XOR-swizzled
+// so the 16 lanes reading one 16-byte column of 16 rows hit distinct banks;
+// with a single round they are loaded once per head.
+//
+// Inside a wave the M tiles are software-pipelined: the 16 MFMAs of tile m
+// are issued between the argmax instructions of tile m - 1, and the A
+// fragments of tile m + 1 are read from LDS meanwhile, so the matrix pipe,
+// the vector ALU and LDS work at once.
 //
 // MFMA 16x16x32 fragment layout (wave64): lane l supplies row/column
 // (l & 15) and the 8 consecutive k values 8*(l >> 4) .. +7 of a 32-wide k
 // step, for A and B alike; the 16x16 fp32 result gives lane l column
 // (l & 15) and rows 4*(l >> 4) + i, i = 0..3.
-constexpr int kAsWaves = 16;
+//
+// The argmax is exact up to the fp32 accumulation of the scores:
+//  * cosine: the accumulation starts from 2.0, so every score 2 + s lies in
+//    [0.99, 3.01] and orders like its bit pattern. Within a group of
+//    kAsGroup consecutive M tiles a lane's candidates carry a 5-bit key in
+//    their low bits (larger for the lower id) and are reduced with float max;
+//    the group's winner then replaces the running best only if its score with
+//    the key bits cleared is strictly larger, and lanes merge on (truncated
+//    score, id). Every decision therefore compares 2 + s truncated to 2^-17
+//    of its magnitude (7.6e-6 absolute at most) and resolves equal truncated
+//    scores -- exact ties included -- to the lower id.
+//  * inner product and L2: a plain compare-and-select per score (strict >
+//    in ascending id order), then the same lane merge on (score, id).
+constexpr int kAsWaves = 8;
 constexpr int kAsThreads = 64 * kAsWaves;
 constexpr int kAsTok = 64 * kAsWaves;   // tokens per tile
 constexpr int kAsRound = 512;           // clusters resident in LDS at a time
+constexpr int kAsGroup = 8;             // M tiles per packed-argmax group
+constexpr uint32_t kAsKey = 4 * kAsGroup - 1;   // key bits of a group (5)
+static_assert(kAsRound % (16 * kAsGroup) == 0, "groups never straddle a round");
 
 // B fragments of the wave's 64 tokens from row tok0 (rows past the window
 // read the last row; their results are not stored).
@@ -277,68 +303,136 @@ __device__ __forceinline__ void as_load_b(const u32x4 *K4, int64_t Lp, int64_t t
     }
 }
 
-// Running argmax as one float max: a score's 11 low mantissa bits are
-// replaced by 2047 - (cluster id), so the larger packed value is the larger
-// score, and scores equal in their upper 13 significant bits go to the lower
-// id (kMaxC = 2048 ids fit in 11 bits). The comparison thus resolves
-// differences above 2^-13 of the score's magnitude, far below the rounding
-// of the bf16 operands themselves.
-__device__ __forceinline__ float as_pack(float score, uint32_t key) {
-    return __uint_as_float((__float_as_uint(score) & 0xFFFFF800u) | key);
-}
-__device__ __forceinline__ int as_unpack(float best) {
-    return 2047 - (int)(__float_as_uint(best) & 0x7FFu);
-}
-
-// One 16-cluster M tile (LDS rows 16m ..) against the wave's 64 tokens, then
-// the running packed max over the lane's rows c0 .. c0+3; MASK drops ids
-// >= C. BIAS adds the clusters' score bias (L2: -|mu|^2 / 2, from LDS) to
-// the scores first.
-template <bool MASK, bool BIAS>
-__device__ __forceinline__ void as_mtile(const u32x4 *sA, const float *sB, int m, int col,
-                                         int kq, const bf16x8 (&b)[4][4], int c0, int C,
-                                         float (&best)[4]) {
-    bf16x8 afr[4];
+// A fragments of M tile m (LDS rows 16m .. 16m + 15 of the round).
+__device__ __forceinline__ void as_lds_a(const u32x4 *sA, int m, int col, int kq,
+                                         bf16x8 (&a)[4]) {
     const int r = 16 * m + col;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        afr[s] = __builtin_bit_cast(bf16x8, sA[r * 16 + ((4 * s + kq) ^ col)]);
-    f32x4 acc[4];
+    for (int s = 0; s < 4; ++s) a[s] = __builtin_bit_cast(bf16x8, sA[r * 16 + ((4 * s + kq) ^ col)]);
+}
+
+// The 16 MFMAs of one M tile against the wave's four N tiles, k steps in
+// order for every N tile; the cosine's accumulation starts from 2.0.
+template <bool COS>
+__device__ __forceinline__ void as_mfma(const bf16x8 (&a)[4], const bf16x8 (&b)[4][4],
+                                        f32x4 (&acc)[4]) {
+    const float c0 = COS ? 2.f : 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[t][0], (f32x4){c0, c0, c0, c0},
+                                                         0, 0, 0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 1; s < 4; ++s)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], b[t][s], acc[t], 0, 0, 0);
-    if (BIAS) {
-        const f32x4 bv = *(const f32x4 *)(sB + 16 * m + 4 * kq);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] += bv[i];
-    }
-    uint32_t key[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = (uint32_t)(2047 - (c0 + i));
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[t][s], acc[t], 0, 0, 0);
+}
+
+// Cosine, one M tile at position mm of its group: the lane's rows c0 .. c0+3
+// get keys kAsKey - (4 mm + i) in their low bits and join the group maxima
+// gb[t]; MASK drops ids >= C (0 never wins against 2 + s).
+// vmask is ~kAsKey held in a vector register: with the key (uniform, a
+// scalar register) the insert is one v_and_or_b32, which may read only one
+// scalar operand.
+template <bool MASK>
+__device__ __forceinline__ void as_cos_tile(const f32x4 (&acc)[4], int mm, int c0, int C,
+                                            uint32_t vmask, float (&gb)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = as_pack(acc[t][i], key[i]);
-            if (MASK && c0 + i >= C) p[i] = -INFINITY;
+            const uint32_t key = kAsKey - (uint32_t)(4 * mm + i);
+            p[i] = __uint_as_float((__float_as_uint(acc[t][i]) & vmask) | key);
+            if (MASK && c0 + i >= C) p[i] = 0.f;
         }
-        best[t] = fmaxf(fmaxf(best[t], p[0]), p[1]);
-        best[t] = fmaxf(fmaxf(best[t], p[2]), p[3]);
+        gb[t] = fmaxf(fmaxf(gb[t], p[0]), p[1]);
+        gb[t] = fmaxf(fmaxf(gb[t], p[2]), p[3]);
     }
 }
 
-template <bool BIAS>
+// ~kAsKey in a vector register (opaque to the compiler, so it stays there).
+__device__ __forceinline__ uint32_t as_vmask() {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(~kAsKey));
+    return v;
+}
+
+// Cosine, end of group g: its winner replaces the running best (bv: the
+// truncated score, bk: g << 5 | key) only if strictly larger; gb restarts.
+__device__ __forceinline__ void as_cos_close(float (&gb)[4], int g, float (&bv)[4],
+                                             uint32_t (&bk)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t u = __float_as_uint(gb[t]);
+        const float v = __uint_as_float(u & ~kAsKey);
+        if (v > bv[t]) {
+            bv[t] = v;
+            bk[t] = ((uint32_t)g << 5) | (u & kAsKey);
+        }
+        gb[t] = 0.f;
+    }
+}
+
+// The cluster id a lane's running best stands for.
+__device__ __forceinline__ int as_cos_id(uint32_t bk, int kq) {
+    const int j = (int)(kAsKey - (bk & kAsKey));       // 4 mm + i
+    return 16 * (kAsGroup * (int)(bk >> 5) + (j >> 2)) + 4 * kq + (j & 3);
+}
+
+// Inner product and L2, one M tile: scores (plus the clusters' bias for L2,
+// from LDS row 16m of the round) compared one by one in ascending id.
+template <bool MASK, bool BIAS>
+__device__ __forceinline__ void as_exact_tile(const f32x4 (&acc)[4], const float *sB, int m,
+                                              int kq, int c0, int C, float (&bv)[4],
+                                              int (&bc)[4]) {
+    f32x4 bias = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (BIAS) bias = *(const f32x4 *)(sB + 16 * m + 4 * kq);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sc = BIAS ? acc[t][i] + bias[i] : acc[t][i];
+            if ((!MASK || c0 + i < C) && sc > bv[t]) {
+                bv[t] = sc;
+                bc[t] = c0 + i;
+            }
+        }
+}
+
+// Merge the four row groups of a token (lanes l, l^16, l^32, l^48): larger
+// score, then lower id.
+__device__ __forceinline__ int as_merge(float v, int c) {
+#pragma unroll
+    for (int off = 16; off <= 32; off *= 2) {
+        const float ov = __shfl_xor(v, off);
+        const int oc = __shfl_xor(c, off);
+        if (ov > v || (ov == v && oc < c)) {
+            v = ov;
+            c = oc;
+        }
+    }
+    return c;
+}
+
+// Scheduling hints for one pipelined M tile: its 4 LDS reads early, each
+// MFMA followed by one or two argmax instructions.
+template <int K = 0>
+__device__ __forceinline__ void as_sched_tile() {
+    if constexpr (K < 16) {
+        if constexpr (K < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, K < 8 ? 2 : 1, 0);            // VALU
+        as_sched_tile<K + 1>();
+    }
+}
+
+template <int M>
 __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
     const uint16_t *__restrict__ kt, const uint16_t *__restrict__ mt,
     const float *__restrict__ mb, int64_t Lp, int C, int Cpad, int32_t *__restrict__ assign,
     int64_t L, int n_sink, int tiles_per_head, int n_tiles) {
+    constexpr bool COS = M == kCosine, BIAS = M == kL2;
     __shared__ u32x4 sA[kAsRound * 16];
     __shared__ __align__(16) float sB[BIAS ? kAsRound : 4];
     const uint32_t w = xcd_linear(blockIdx.x, gridDim.x);
@@ -347,18 +441,33 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
     const int col = lane & 15, kq = lane >> 4;
-    const int crows = (C + 15) / 16 * 16;                 // rows that hold real clusters
+    const int crows = (C + 31) / 32 * 32;                 // even number of M tiles, <= Cpad
     const int nr = (crows + kAsRound - 1) / kAsRound;     // rounds per tile
     int loaded = -1;                                      // head of the resident round
     int h = t_begin / tiles_per_head;
     int tile = t_begin - h * tiles_per_head;
+    const uint32_t vmask = as_vmask();
+    bf16x8 b[4][4], bn[4][4];
     for (int t = t_begin; t < t_end; ++t) {
         const int64_t tok0 = (int64_t)tile * kAsTok + wave * 64;
         const u32x4 *M4 = (const u32x4 *)(mt + (int64_t)h * Cpad * kD);
-        bf16x8 b[4][4];
-        float best[4];
+        // the next tile (fragments prefetched when one round holds every cluster)
+        int hn = h, tilen = tile + 1;
+        if (tilen == tiles_per_head) {
+            tilen = 0;
+            ++hn;
+        }
+        float bv[4];
+        uint32_t bk[4];
+        int bc[4];
+        float gb[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) best[u] = -INFINITY;
+        for (int u = 0; u < 4; ++u) {
+            bv[u] = COS ? 0.f : -INFINITY;
+            bk[u] = kAsKey;
+            bc[u] = 0x7fffffff;
+            gb[u] = 0.f;
+        }
         for (int r = 0; r < nr; ++r) {
             const int rb = r * kAsRound;
             const int rows = (crows - rb < kAsRound) ? crows - rb : kAsRound;
@@ -378,35 +487,72 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
                         if (e < rows * 16) sA[rr * 16 + (q ^ (rr & 15))] = v[k];
                     }
                 }
-                if (BIAS && tid < rows) sB[tid] = mb[(int64_t)h * Cpad + rb + tid];
+                if (BIAS)
+                    for (int e = tid; e < rows; e += kAsThreads) sB[e] = mb[(int64_t)h * Cpad + rb + e];
                 __syncthreads();
                 loaded = h;
             }
-            // the tile's B fragments after the first fill: each wave then
-            // starts on its MFMAs as soon as its own rows arrive
-            if (r == 0) as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, tok0, col, kq, b);
-            const int nm = rows / 16;
-            const int cl = rb + 4 * kq;                   // lane's first row of tile 0
-            for (int m = 0; m + 1 < nm; ++m)
-                as_mtile<false, BIAS>(sA, sB, m, col, kq, b, cl + 16 * m, C, best);
-            as_mtile<true, BIAS>(sA, sB, nm - 1, col, kq, b, cl + 16 * (nm - 1), C, best);
+            if (r == 0) {
+                // this tile's fragments (after the fill, so each wave starts as
+                // soon as its own rows arrive), then the next tile's
+                if (t == t_begin || nr > 1) {
+                    as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, tok0, col, kq, b);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) b[u][s2] = bn[u][s2];
+                }
+                if (nr == 1 && t + 1 < t_end)
+                    as_load_b((const u32x4 *)(kt + (int64_t)hn * Lp * kD), Lp,
+                              (int64_t)tilen * kAsTok + wave * 64, col, kq, bn);
+            }
+            const int nm = rows / 16;                     // even
+            const int mg0 = rb / 16;                      // global index of the round's tile 0
+            bf16x8 aE[4], aO[4];
+            f32x4 cE[4], cO[4];
+            // argmax of tile m (global mg0 + m) held in acc
+            auto amax = [&](const f32x4 (&acc)[4], int m, auto mask) {
+                constexpr bool MK = decltype(mask)::value;
+                const int mg = mg0 + m;
+                if (COS)
+                    as_cos_tile<MK>(acc, mg % kAsGroup, 16 * mg + 4 * kq, C, vmask, gb);
+                else
+                    as_exact_tile<MK, BIAS>(acc, sB, m, kq, 16 * mg + 4 * kq, C, bv, bc);
+            };
+            using NoMask = std::integral_constant<bool, false>;
+            using Mask = std::integral_constant<bool, true>;
+            as_lds_a(sA, 0, col, kq, aE);
+            as_lds_a(sA, 1, col, kq, aO);
+            as_mfma<COS>(aE, b, cE);                      // tile 0
+            int m = 1;
+            for (; m + 1 < nm; m += 2) {
+                as_lds_a(sA, m + 1, col, kq, aE);
+                as_mfma<COS>(aO, b, cO);                  // tile m
+                amax(cE, m - 1, NoMask{});
+                as_sched_tile();
+                __builtin_amdgcn_sched_barrier(0);
+                as_lds_a(sA, m + 2, col, kq, aO);
+                as_mfma<COS>(aE, b, cE);                  // tile m + 1
+                amax(cO, m, NoMask{});
+                as_sched_tile();
+                __builtin_amdgcn_sched_barrier(0);
+                if (COS && (mg0 + m) % kAsGroup == kAsGroup - 1)
+                    as_cos_close(gb, (mg0 + m) / kAsGroup, bv, bk);
+            }
+            as_mfma<COS>(aO, b, cO);                      // tile nm - 1
+            amax(cE, nm - 2, Mask{});
+            amax(cO, nm - 1, Mask{});
+            if (COS) as_cos_close(gb, (mg0 + nm - 1) / kAsGroup, bv, bk);
         }
-        // merge the four row groups (lanes l, l^16, l^32, l^48) of each token
         int res[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            float bb = best[u];
-            bb = fmaxf(bb, __shfl_xor(bb, 16));
-            bb = fmaxf(bb, __shfl_xor(bb, 32));
-            res[u] = as_unpack(bb);
-        }
+        for (int u = 0; u < 4; ++u) res[u] = as_merge(bv[u], COS ? as_cos_id(bk[u], kq) : bc[u]);
         const int64_t tok = tok0 + lane;
         const int v = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];
         if (tok < Lp) assign[(int64_t)h * L + n_sink + tok] = v;
-        if (++tile == tiles_per_head) {
-            tile = 0;
-            ++h;
-        }
+        h = hn;
+        tile = tilen;
     }
 }
 
@@ -444,8 +590,10 @@ hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s) {
         const int tph = (int)((p.Lp + kAsTok - 1) / kAsTok);
         const int n_tiles = tph * p.H;
         const int grid = n_tiles < p.n_cu ? n_tiles : p.n_cu;
-        hipLaunchKernelGGL(p.metric == kL2 ? k_assign_bf16<true> : k_assign_bf16<false>,
-                           dim3((unsigned)grid), dim3(kAsThreads), 0, s,
+        auto kern = p.metric == kCosine ? k_assign_bf16<kCosine>
+                  : p.metric == kL2     ? k_assign_bf16<kL2>
+                                        : k_assign_bf16<kInnerProduct>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kAsThreads), 0, s,
                            (const uint16_t *)p.kt, (const uint16_t *)p.mt, (const float *)p.mb,
                            p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink, tph, n_tiles);
     } else {
@@ -860,8 +1008,8 @@ __device__ __forceinline__ int64_t upd_partial(
 // channels l and l + 64. mean = sum / n in fp64, stored as fp32 in the
 // centroid row cp (an empty cluster keeps its centroid); then the row the
 // next assignment reads: for the cosine the unit row (|mu|^2 as one fp64 fma
-// chain over j = 0..127 in order, r = 1/sqrt(|mu|^2), channel j ->
-// fp32(mu_j * r), then bf16 when BF16; a zero row stays zero), else the mean
+// chain over j = 0..127 in order, |mu| its fp64 square root, channel j ->
+// fp32(mu_j / |mu|), then bf16 when BF16; a zero row stays zero), else the mean
 // rounded to the key type and, for L2, the bias -|mu^|^2 / 2 of that rounded
 // row. That row goes to mrow and the bias to *bias when they are given, and
 // to row c of the swizzled LDS tile sA (and sB[c]) when those are given.
@@ -938,10 +1086,10 @@ __device__ __forceinline__ void upd_final(int c, int lane, int64_t n, const doub
         ss = __fma_rn((double)x[2], (double)x[2], ss);
         ss = __fma_rn((double)x[3], (double)x[3], ss);
     }
-    const double inv = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+    const double nrm = sqrt(ss);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const float y = (float)((double)mu[k] * inv);
+        const float y = (ss > 0.0) ? (float)((double)mu[k] / nrm) : 0.f;
         put(lane + 64 * k, BF16 ? (uint16_t)f32_to_bf16_rne(y) : (uint16_t)0, y);
     }
 }
@@ -1003,7 +1151,8 @@ hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *off
 //    128-thread groups at a time; centroids stay in LDS and the rows the
 //    assignment reads go straight into its LDS tile;
 //  * assignment: wave w takes tokens 64 w .. 64 w + 63 against the one
-//    16-cluster M tile (as_load_b, as_mtile, the packed lane merge);
+//    16-cluster M tile (as_load_b, as_mfma and the general kernel's argmax:
+//    the same comparisons in the same order);
 //  * CSR: the stable counting sort (ballot ranks inside a wave, wave counts,
 //    prefix over clusters), tokens in ascending order inside a cluster;
 //  * update: four 256-thread groups run k_update's two halves for clusters
@@ -1024,7 +1173,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
     __shared__ int wcnt[16][kSmallC];
     __shared__ double red[4][4][kD];
     __shared__ __align__(16) float sx[8][kD];
-    __shared__ double sinv[8];
+    __shared__ double snrm[8];
     __shared__ float scent[kSmallC][kD];
     __shared__ u32x4 rows[kNkRows * kNkStride];
     __shared__ int32_t stok[kSmallRows];
@@ -1092,13 +1241,14 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
                 double ss = 0.0;
                 for (int k = 0; k < kD; ++k) ss = __fma_rn((double)sx[g][k], (double)sx[g][k], ss);
                 if (M == kCosine)
-                    sinv[g] = (ss > 0.0) ? 1.0 / sqrt(ss) : 0.0;
+                    snrm[g] = sqrt(ss);
                 else
                     sB[c] = (float)(-0.5 * ss);
             }
             __syncthreads();
             if (M == kCosine && act)
-                put(c, (uint16_t)f32_to_bf16_rne((float)((double)x * sinv[g])));
+                put(c, snrm[g] > 0.0 ? (uint16_t)f32_to_bf16_rne((float)((double)x / snrm[g]))
+                                     : (uint16_t)0);
         }
     }
     __syncthreads();
@@ -1112,20 +1262,26 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
         const bool last = it == iters - 1;       // only its labels and CSR are kept
         // assignment: wave w's 64 tokens against the one M tile
         {
-            bf16x8 b[4][4];
+            bf16x8 b[4][4], afr[4];
             as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, (int64_t)wave * 64, col,
                       kq, b);
-            float best[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) best[u] = -INFINITY;
-            as_mtile<true, BIAS>(sA, sB, 0, col, kq, b, 4 * kq, C, best);
+            as_lds_a(sA, 0, col, kq, afr);
+            f32x4 acc[4];
+            as_mfma<M == kCosine>(afr, b, acc);
             int res[4];
+            if (M == kCosine) {
+                float gb[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
+                uint32_t bk[4] = {kAsKey, kAsKey, kAsKey, kAsKey};
+                as_cos_tile<true>(acc, 0, 4 * kq, C, as_vmask(), gb);
+                as_cos_close(gb, 0, bv, bk);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float bb = best[u];
-                bb = fmaxf(bb, __shfl_xor(bb, 16));
-                bb = fmaxf(bb, __shfl_xor(bb, 32));
-                res[u] = as_unpack(bb);
+                for (int u = 0; u < 4; ++u) res[u] = as_merge(bv[u], as_cos_id(bk[u], kq));
+            } else {
+                float bv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                int bc[4] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff};
+                as_exact_tile<true, BIAS>(acc, sB, 0, kq, 4 * kq, C, bv, bc);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) res[u] = as_merge(bv[u], bc[u]);
             }
             int a = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];
             if (last && valid) as[n_sink + i] = a;

@@ -417,3 +417,39 @@ def test_attention_largest_budget_and_strided_cache():
     err = rel_err(host_f64(o), oracle.attn(qf, Kf, Vf, idx, n_sel, G=G))
     say(f"  rel err {err:.2e}")
     assert err <= 2e-3
+
+
+def test_single_head_fp32_end_to_end():
+    """The single-head fp32 2k workload end to end on the GPU: its own
+    10-iteration clustering, then selection with B = 256 on those clusters
+    (bit-exact against the oracle given the GPU's centroids and CSR), then
+    the sparse attention over the selected rows and the fused one-call step,
+    both within 1e-5 of the fp64 oracle; with B >= L the selection takes
+    every row and the output is dense decode attention, within 1e-5."""
+    wl = synth.workload(0)
+    say("single-head fp32 2k end to end: cluster -> select -> attention")
+    Kd, Vd, Kf, Vf = _kv(wl, wl.L)
+    cent, asg, off, tok = gpu_cluster(Kd, wl.n_sink, wl.C, wl.iters)
+    mu, off_h, tok_h = host_f64(cent), off.cpu().numpy(), tok.cpu().numpy()
+    # the CSR is the one of the GPU's labels
+    o_off, o_tok = oracle.csr(asg.cpu().numpy()[0], wl.n_sink, wl.C)
+    assert np.array_equal(off_h[0], o_off) and np.array_equal(tok_h[0], o_tok)
+    for step in range(3):
+        qd, qf = _q(wl, step)
+        for B in (wl.B, wl.L, wl.L + 64):
+            idx, ns = ck.ckv_select(qd, cent, off, tok, wl.C, B, n_sink=wl.n_sink)
+            o = ck.ckv_sparse_attn(qd, Kd, Vd, idx, ns)
+            idx2, ns2, o2 = ck.ckv_select_attn(qd, cent, off, tok, wl.C, B, Kd, Vd,
+                                               n_sink=wl.n_sink)
+            torch.cuda.synchronize()
+            o_idx, o_ns, _ = oracle.select(qf, mu, off_h, tok_h, wl.C, wl.n_sink, B, G=wl.G)
+            assert np.array_equal(idx.cpu().numpy(), o_idx), (step, B)
+            assert np.array_equal(ns.cpu().numpy(), o_ns), (step, B)
+            assert torch.equal(idx, idx2) and torch.equal(o, o2), (step, B)
+            ref = oracle.attn(qf, Kf, Vf, o_idx, o_ns, G=wl.G)
+            err = rel_err(host_f64(o), ref)
+            assert err <= 1e-5, (step, B, err)
+            if B >= wl.L:
+                assert o_ns[0] == wl.L
+                dense = oracle.dense_attn(qf, Kf, Vf, G=wl.G)
+                assert rel_err(host_f64(o), dense) <= 1e-5, (step, B)
