@@ -101,14 +101,35 @@ __device__ __forceinline__ void nk_unit_row(u32x4 *row) {
     }
     const double n = sqrt(ss);
     const bool nz = ss > 0.0;
+    const double r = nz ? 1.0 / n : 0.0;
 #pragma unroll 4
     for (int i = 0; i < 16; ++i) {
         float f[8];
         unpack8(row[i], f);
+        // x * (1/|x|) is within two fp64 ulps of the quotient x / |x|, so it
+        // rounds to the same fp32 value unless it lies within a few ulps of
+        // a point halfway between two fp32 values (its 29 bits below fp32
+        // precision near 2^28) or in fp32's subnormal range; only then is
+        // the division carried out.
+        double qv[8];
+        bool amb = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qv[e] = (double)f[e] * r;
+            const uint64_t u = (uint64_t)__double_as_longlong(qv[e]);
+            const uint32_t lo = (uint32_t)u & 0x1FFFFFFFu;
+            const uint32_t ex = (uint32_t)(u >> 52) & 0x7FFu;   // biased exponent
+            // bitwise, not short-circuit: no branch per element (a zero
+            // also takes the division, which gives it exactly)
+            amb = amb | ((lo - (0x10000000u - 4u)) <= 8u) | (ex < 1023u - 125u);
+        }
+        if (amb) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = (double)f[e] / n;
+        }
         uint32_t o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            o[e] = nz ? f32_to_bf16_rne((float)((double)f[e] / n)) : 0u;
+        for (int e = 0; e < 8; ++e) o[e] = nz ? f32_to_bf16_rne((float)qv[e]) : 0u;
         u32x4 v;
         v.x = o[0] | (o[1] << 16);
         v.y = o[2] | (o[3] << 16);
@@ -417,6 +438,18 @@ __device__ __forceinline__ int as_merge(float v, int c) {
 
 // Scheduling hints for one pipelined M tile: its 4 LDS reads early, each
 // MFMA followed by one or two argmax instructions.
+#ifndef CKV_AS_SCHED
+#define CKV_AS_SCHED 1
+#endif
+#if CKV_AS_SCHED
+#define AS_SCHED()                          \
+    do {                                    \
+        as_sched_tile();                    \
+        __builtin_amdgcn_sched_barrier(0);  \
+    } while (0)
+#else
+#define AS_SCHED() do {} while (0)
+#endif
 template <int K = 0>
 __device__ __forceinline__ void as_sched_tile() {
     if constexpr (K < 16) {
@@ -425,6 +458,32 @@ __device__ __forceinline__ void as_sched_tile() {
         __builtin_amdgcn_sched_group_barrier(0x002, K < 8 ? 2 : 1, 0);            // VALU
         as_sched_tile<K + 1>();
     }
+}
+
+// LDS fill of one round: centroid rows rb .. rb + rows - 1 of the head at M4
+// (and their score bias when BIAS), behind barriers on both sides. DEPTH
+// 16-byte loads per thread are in flight at once (16 cover a whole round).
+template <bool BIAS, int DEPTH>
+__device__ __forceinline__ void as_fill(u32x4 *sA, float *sB, const u32x4 *M4,
+                                        const float *mbh, int rb, int rows, int tid) {
+    __syncthreads();                                      // the previous round is done
+    for (int e0 = 0; e0 < rows * 16; e0 += kAsThreads * DEPTH) {
+        u32x4 v[DEPTH];
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+            const int e = e0 + tid + kAsThreads * k;
+            v[k] = M4[(int64_t)rb * 16 + (e < rows * 16 ? e : 0)];
+        }
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+            const int e = e0 + tid + kAsThreads * k;
+            const int rr = e >> 4, q = e & 15;
+            if (e < rows * 16) sA[rr * 16 + (q ^ (rr & 15))] = v[k];
+        }
+    }
+    if (BIAS)
+        for (int e = tid; e < rows; e += kAsThreads) sB[e] = mbh[rb + e];
+    __syncthreads();
 }
 
 template <int M>
@@ -443,20 +502,34 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
     const int col = lane & 15, kq = lane >> 4;
     const int crows = (C + 31) / 32 * 32;                 // even number of M tiles, <= Cpad
     const int nr = (crows + kAsRound - 1) / kAsRound;     // rounds per tile
-    int loaded = -1;                                      // head of the resident round
+    const uint32_t vmask = as_vmask();
     int h = t_begin / tiles_per_head;
     int tile = t_begin - h * tiles_per_head;
-    const uint32_t vmask = as_vmask();
+    // A single round stays resident while the head does not change: fill it
+    // first, then request the first tile's rows (each wave starts as soon as
+    // its own rows arrive). Fragments of tile t + 1 are requested while tile
+    // t computes; no load is issued under a branch, so the compiler's waits
+    // for b never include them.
+    int loaded = -1;
+    if (nr == 1) {
+        as_fill<BIAS, kAsRound * 16 / kAsThreads>(sA, sB, (const u32x4 *)(mt + (int64_t)h * Cpad * kD),
+                                                  mb + (int64_t)h * Cpad, 0, crows, tid);
+        loaded = h;
+    }
     bf16x8 b[4][4], bn[4][4];
+    as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, (int64_t)tile * kAsTok + wave * 64,
+              col, kq, b);
     for (int t = t_begin; t < t_end; ++t) {
         const int64_t tok0 = (int64_t)tile * kAsTok + wave * 64;
         const u32x4 *M4 = (const u32x4 *)(mt + (int64_t)h * Cpad * kD);
-        // the next tile (fragments prefetched when one round holds every cluster)
+        // the next tile (the last one requests its own rows again: harmless)
         int hn = h, tilen = tile + 1;
         if (tilen == tiles_per_head) {
             tilen = 0;
             ++hn;
         }
+        const bool more = t + 1 < t_end;
+        const int hp = more ? hn : h, tp = more ? tilen : tile;
         float bv[4];
         uint32_t bk[4];
         int bc[4];
@@ -468,45 +541,18 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
             bc[u] = 0x7fffffff;
             gb[u] = 0.f;
         }
-        for (int r = 0; r < nr; ++r) {
+        // one round: its LDS fill when needed, then its M tiles
+        auto fill = [&](int r) {
             const int rb = r * kAsRound;
             const int rows = (crows - rb < kAsRound) ? crows - rb : kAsRound;
             if (nr > 1 || loaded != h) {
-                __syncthreads();                          // the previous round is done
-                for (int e0 = 0; e0 < rows * 16; e0 += kAsThreads * 4) {
-                    u32x4 v[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int e = e0 + tid + kAsThreads * k;
-                        v[k] = M4[(int64_t)rb * 16 + (e < rows * 16 ? e : 0)];
-                    }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int e = e0 + tid + kAsThreads * k;
-                        const int rr = e >> 4, q = e & 15;
-                        if (e < rows * 16) sA[rr * 16 + (q ^ (rr & 15))] = v[k];
-                    }
-                }
-                if (BIAS)
-                    for (int e = tid; e < rows; e += kAsThreads) sB[e] = mb[(int64_t)h * Cpad + rb + e];
-                __syncthreads();
+                as_fill<BIAS, 4>(sA, sB, M4, mb + (int64_t)h * Cpad, rb, rows, tid);
                 loaded = h;
             }
-            if (r == 0) {
-                // this tile's fragments (after the fill, so each wave starts as
-                // soon as its own rows arrive), then the next tile's
-                if (t == t_begin || nr > 1) {
-                    as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, tok0, col, kq, b);
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) b[u][s2] = bn[u][s2];
-                }
-                if (nr == 1 && t + 1 < t_end)
-                    as_load_b((const u32x4 *)(kt + (int64_t)hn * Lp * kD), Lp,
-                              (int64_t)tilen * kAsTok + wave * 64, col, kq, bn);
-            }
+        };
+        auto run = [&](int r) {
+            const int rb = r * kAsRound;
+            const int rows = (crows - rb < kAsRound) ? crows - rb : kAsRound;
             const int nm = rows / 16;                     // even
             const int mg0 = rb / 16;                      // global index of the round's tile 0
             bf16x8 aE[4], aO[4];
@@ -530,13 +576,11 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
                 as_lds_a(sA, m + 1, col, kq, aE);
                 as_mfma<COS>(aO, b, cO);                  // tile m
                 amax(cE, m - 1, NoMask{});
-                as_sched_tile();
-                __builtin_amdgcn_sched_barrier(0);
+                AS_SCHED();
                 as_lds_a(sA, m + 2, col, kq, aO);
                 as_mfma<COS>(aE, b, cE);                  // tile m + 1
                 amax(cO, m, NoMask{});
-                as_sched_tile();
-                __builtin_amdgcn_sched_barrier(0);
+                AS_SCHED();
                 if (COS && (mg0 + m) % kAsGroup == kAsGroup - 1)
                     as_cos_close(gb, (mg0 + m) / kAsGroup, bv, bk);
             }
@@ -544,10 +588,24 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
             amax(cE, nm - 2, Mask{});
             amax(cO, nm - 1, Mask{});
             if (COS) as_cos_close(gb, (mg0 + nm - 1) / kAsGroup, bv, bk);
+        };
+        fill(0);
+        as_load_b((const u32x4 *)(kt + (int64_t)hp * Lp * kD), Lp,
+                  (int64_t)tp * kAsTok + wave * 64, col, kq, bn);
+        run(0);
+        for (int r = 1; r < nr; ++r) {
+            fill(r);
+            run(r);
         }
         int res[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) res[u] = as_merge(bv[u], COS ? as_cos_id(bk[u], kq) : bc[u]);
+        // the next tile's fragments become current (this waits for them),
+        // then the labels are stored
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) b[u][s2] = bn[u][s2];
         const int64_t tok = tok0 + lane;
         const int v = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];
         if (tok < Lp) assign[(int64_t)h * L + n_sink + tok] = v;
