@@ -282,9 +282,9 @@ hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cen
 // with a single round they are loaded once per head.
 //
 // Inside a wave the M tiles are software-pipelined: the 16 MFMAs of tile m
-// are issued between the argmax instructions of tile m - 1, and the A
-// fragments of tile m + 1 are read from LDS meanwhile, so the matrix pipe,
-// the vector ALU and LDS work at once.
+// are issued next to the argmax instructions of tile m - 1 (two sets of
+// accumulators), and the A fragments of tile m + 1 are read from LDS
+// meanwhile, so the matrix pipe, the vector ALU and LDS work at once.
 //
 // MFMA 16x16x32 fragment layout (wave64): lane l supplies row/column
 // (l & 15) and the 8 consecutive k values 8*(l >> 4) .. +7 of a 32-wide k
@@ -436,30 +436,6 @@ __device__ __forceinline__ int as_merge(float v, int c) {
     return c;
 }
 
-// Scheduling hints for one pipelined M tile: its 4 LDS reads early, each
-// MFMA followed by one or two argmax instructions.
-#ifndef CKV_AS_SCHED
-#define CKV_AS_SCHED 1
-#endif
-#if CKV_AS_SCHED
-#define AS_SCHED()                          \
-    do {                                    \
-        as_sched_tile();                    \
-        __builtin_amdgcn_sched_barrier(0);  \
-    } while (0)
-#else
-#define AS_SCHED() do {} while (0)
-#endif
-template <int K = 0>
-__device__ __forceinline__ void as_sched_tile() {
-    if constexpr (K < 16) {
-        if constexpr (K < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, K < 8 ? 2 : 1, 0);            // VALU
-        as_sched_tile<K + 1>();
-    }
-}
-
 // LDS fill of one round: centroid rows rb .. rb + rows - 1 of the head at M4
 // (and their score bias when BIAS), behind barriers on both sides. DEPTH
 // 16-byte loads per thread are in flight at once (16 cover a whole round).
@@ -550,11 +526,20 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
                 loaded = h;
             }
         };
+        // the next tile's fragments: requested halfway through round 0's M
+        // tiles (earlier, the waves whose rows came first would delay the
+        // others' first rows with their prefetch), or after them when round
+        // 0 is too short to reach that point
+        auto prefetch = [&]() {
+            as_load_b((const u32x4 *)(kt + (int64_t)hp * Lp * kD), Lp,
+                      (int64_t)tp * kAsTok + wave * 64, col, kq, bn);
+        };
         auto run = [&](int r) {
             const int rb = r * kAsRound;
             const int rows = (crows - rb < kAsRound) ? crows - rb : kAsRound;
             const int nm = rows / 16;                     // even
             const int mg0 = rb / 16;                      // global index of the round's tile 0
+            const int m_pf = (nm / 2) | 1;                // odd, like the loop's m
             bf16x8 aE[4], aO[4];
             f32x4 cE[4], cO[4];
             // argmax of tile m (global mg0 + m) held in acc
@@ -573,25 +558,23 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
             as_mfma<COS>(aE, b, cE);                      // tile 0
             int m = 1;
             for (; m + 1 < nm; m += 2) {
+                if (r == 0 && m == m_pf) prefetch();
                 as_lds_a(sA, m + 1, col, kq, aE);
                 as_mfma<COS>(aO, b, cO);                  // tile m
                 amax(cE, m - 1, NoMask{});
-                AS_SCHED();
                 as_lds_a(sA, m + 2, col, kq, aO);
                 as_mfma<COS>(aE, b, cE);                  // tile m + 1
                 amax(cO, m, NoMask{});
-                AS_SCHED();
                 if (COS && (mg0 + m) % kAsGroup == kAsGroup - 1)
                     as_cos_close(gb, (mg0 + m) / kAsGroup, bv, bk);
             }
+            if (r == 0 && m_pf + 1 >= nm) prefetch();
             as_mfma<COS>(aO, b, cO);                      // tile nm - 1
             amax(cE, nm - 2, Mask{});
             amax(cO, nm - 1, Mask{});
             if (COS) as_cos_close(gb, (mg0 + nm - 1) / kAsGroup, bv, bk);
         };
         fill(0);
-        as_load_b((const u32x4 *)(kt + (int64_t)hp * Lp * kD), Lp,
-                  (int64_t)tp * kAsTok + wave * 64, col, kq, bn);
         run(0);
         for (int r = 1; r < nr; ++r) {
             fill(r);
