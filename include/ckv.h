@@ -248,6 +248,31 @@ int ckv_select_attn(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc, co
                     int32_t *n_sel, float *o, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* ------------------------------------------------- select_attn_noalloc --
+ * ckv_select_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments and results as ckv_select_attn (bitwise: the
+ * same kernels), except that the workspace is a static device array of
+ * CKV_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends. Nothing is allocated or freed by the call.
+ *
+ * The caller still owns and passes every input and output. A step whose
+ * workspace (ckv_select_attn_workspace) exceeds CKV_NOALLOC_SCRATCH_BYTES
+ * returns CKV_ERR_WORKSPACE before anything is enqueued. The array of the
+ * current device is used, so `stream` must belong to the current device.
+ * All calls on one GPU share that array: calls that may overlap on one GPU
+ * (on different streams, or from several threads) race and must not be
+ * made; calls ordered on one stream are fine. The first call on a device
+ * looks the array's address up once (hipGetSymbolAddress); if that fails
+ * the call returns CKV_ERR_LAUNCH.
+ */
+#define CKV_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+int ckv_select_attn_noalloc(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc,
+                            const void *q, const float *centroids, const int32_t *csr_offsets,
+                            const int32_t *csr_tokens, const void *K, const void *V,
+                            int32_t *idx, int32_t *n_sel, float *o, void *stream);
+
 /* --------------------------------------------------------------- cache --
  * Cluster-granular GPU cache of selected KV rows, for KV kept in host memory
  * [Caching the KV of selected tokens; system overview, Fig. 5]: the GPU keeps

@@ -28,12 +28,14 @@ __all__ = [
     "ckv_cluster_workspace", "ckv_select_workspace", "ckv_attn_workspace",
     "ckv_status_string", "ckv_abi_version", "ckv_select_attn", "ckv_select_attn_workspace",
     "ckv_cache_rows", "ckv_cache_workspace", "ckv_cache_step", "ckv_device_view",
-    "CacheDesc", "cache_desc", "cache_state",
+    "CacheDesc", "cache_desc", "cache_state", "ckv_select_attn_noalloc",
+    "CKV_NOALLOC_SCRATCH_BYTES",
 ]
 
 CKV_OK, CKV_ERR_INVALID_ARG, CKV_ERR_UNSUPPORTED, CKV_ERR_WORKSPACE, CKV_ERR_LAUNCH = range(5)
 CKV_F32, CKV_BF16 = 0, 1
 CKV_COSINE, CKV_INNER_PRODUCT, CKV_L2 = 0, 1, 2
+CKV_NOALLOC_SCRATCH_BYTES = 8 << 20        # include/ckv.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libckv.so")
@@ -92,6 +94,8 @@ _SIGS = {
     "ckv_cache_step": (ct.c_int, [ct.POINTER(CacheDesc), ct.c_int64, _P, _P, _P, _P, _P, _P, _P,
                                   _P, _P, _P, _P, _P, _P, _P, ct.c_size_t, _P]),
     "ckv_device_view": (ct.c_int, [_P, ct.POINTER(ct.c_void_p)]),
+    "ckv_select_attn_noalloc": (ct.c_int, [ct.POINTER(SelectDesc), ct.POINTER(AttnDesc), _P, _P,
+                                           _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -463,4 +467,48 @@ def ckv_select_attn(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch
                                _ptr(csr_offsets), _ptr(csr_tokens), _kv_ptr(K), _kv_ptr(V), _ptr(idx),
                                _ptr(n_sel), _ptr(out), _ptr(ws), nb, _stream(stream)),
            "ckv_select_attn")
+    return idx, n_sel, out
+
+
+def ckv_select_attn_noalloc(q: torch.Tensor, centroids: torch.Tensor, csr_offsets: torch.Tensor,
+                            csr_tokens: torch.Tensor, C: int, B: int, K: torch.Tensor,
+                            V: torch.Tensor, *, idx: torch.Tensor, n_sel: torch.Tensor,
+                            out: torch.Tensor, n_sink: int = 16, pending_begin: int = 0,
+                            n_pending: int = 0, kv_rows: Optional[int] = None,
+                            scale: float = 0.0, stream=None):
+    """ckv_select_attn without any allocation: the workspace is the
+    library's static per-GPU scratch (CKV_NOALLOC_SCRATCH_BYTES), and the
+    caller passes the outputs idx [H][B] int32, n_sel [H] int32 and out
+    [H*G][d] fp32. Calls that may overlap on one GPU must not be made.
+    Returns (idx, n_sel, out), bitwise what ckv_select_attn returns."""
+    _on_gpu(q=q, centroids=centroids, csr_offsets=csr_offsets, csr_tokens=csr_tokens, idx=idx,
+            n_sel=n_sel, out=out)
+    lib = load()
+    H, c_cap, d = centroids.shape
+    hs = _rows(K, "K")
+    _need(V.shape == K.shape and V.stride() == K.stride() and V.dtype == K.dtype,
+          "V must match K in shape, strides and dtype")
+    _need(K.shape[0] == H and K.shape[2] == d, "K must be [H][rows][d] for the centroids' H, d")
+    _need(q.dim() == 2 and q.is_contiguous() and q.shape[1] == d and q.shape[0] % H == 0
+          and q.dtype == K.dtype, "q must be [H*G][d] contiguous, dtype of K")
+    _need(centroids.dtype == torch.float32 and centroids.is_contiguous(), "bad centroids")
+    _need(csr_offsets.dtype == torch.int32 and csr_offsets.is_contiguous()
+          and csr_offsets.shape == (H, c_cap + 1), "bad csr_offsets")
+    _need(csr_tokens.dtype == torch.int32 and csr_tokens.is_contiguous()
+          and csr_tokens.shape[0] == H, "bad csr_tokens")
+    G = q.shape[0] // H
+    _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.shape == (H, B), "bad idx")
+    _need(n_sel.dtype == torch.int32 and n_sel.numel() == H, "bad n_sel")
+    _need(out.dtype == torch.float32 and out.is_contiguous() and out.shape == (H * G, d),
+          "bad out")
+    sd = SelectDesc(H=H, G=G, d=d, C=C, c_cap=c_cap, n_sink=n_sink, t_cap=csr_tokens.shape[1],
+                    pending_begin=pending_begin, n_pending=n_pending, B=B,
+                    dtype=_dtype_code(q))
+    ad = AttnDesc(H=H, G=G, d=d, B=B, kv_head_stride=hs,
+                  kv_rows=K.shape[1] if kv_rows is None else kv_rows, scale=scale,
+                  dtype=_dtype_code(K))
+    _check(lib.ckv_select_attn_noalloc(ct.byref(sd), ct.byref(ad), _ptr(q), _ptr(centroids),
+                                       _ptr(csr_offsets), _ptr(csr_tokens), _kv_ptr(K),
+                                       _kv_ptr(V), _ptr(idx), _ptr(n_sel), _ptr(out),
+                                       _stream(stream)), "ckv_select_attn_noalloc")
     return idx, n_sel, out

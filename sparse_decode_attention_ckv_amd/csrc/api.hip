@@ -364,6 +364,29 @@ int ckv_sparse_attn(const ckv_attn_desc *desc, const void *q, const void *K, con
     return launch_status(launch_attn(p, q, Kd, Vd, idx, n_sel, o, (hipStream_t)stream));
 }
 
+namespace {
+// Workspace of ckv_select_attn_noalloc: one copy per device, for the life of
+// the process. Its name is a host-side stand-in in host code; kernels get
+// the device address found by hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[CKV_NOALLOC_SCRATCH_BYTES];
+
+// scratch's device address on the current device (looked up once per
+// device, with that device current), or nullptr if the lookup fails
+void *scratch_ptr() {
+    static std::atomic<void *> ptr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+    if (dev < 64) {
+        void *p = ptr[dev].load(std::memory_order_acquire);
+        if (p) return p;
+    }
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    if (dev < 64) ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+}  // namespace
+
 size_t ckv_select_attn_workspace(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc) {
     if (check_select_attn(sdesc, adesc) != CKV_OK) return 0;
     return select_bytes(sdesc) + attn_bytes(adesc);
@@ -395,6 +418,22 @@ int ckv_select_attn(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc, co
     ap.host_kv = hk || hv;
     return launch_status(launch_select_attn(sp, ap, q, centroids, csr_offsets, csr_tokens, Kd,
                                             Vd, idx, n_sel, o, (hipStream_t)stream));
+}
+
+int ckv_select_attn_noalloc(const ckv_select_desc *sdesc, const ckv_attn_desc *adesc,
+                            const void *q, const float *centroids, const int32_t *csr_offsets,
+                            const int32_t *csr_tokens, const void *K, const void *V,
+                            int32_t *idx, int32_t *n_sel, float *o, void *stream) {
+    const int st = check_select_attn(sdesc, adesc);
+    if (st != CKV_OK) return st;
+    const size_t need = select_bytes(sdesc) + attn_bytes(adesc);
+    if (need > CKV_NOALLOC_SCRATCH_BYTES) return CKV_ERR_WORKSPACE;
+    if (!q || !centroids || !csr_offsets || !csr_tokens || !K || !V || !idx || !n_sel || !o)
+        return CKV_ERR_INVALID_ARG;
+    void *ws = scratch_ptr();
+    if (!ws) return CKV_ERR_LAUNCH;
+    return ckv_select_attn(sdesc, adesc, q, centroids, csr_offsets, csr_tokens, K, V, idx, n_sel,
+                           o, ws, CKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int ckv_device_view(const void *ptr, const void **device_ptr) {
