@@ -72,45 +72,13 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def decode_schedule(wl, T, lag=0):
-    """Per decode step t = s - 1 of T: (clusters in use, first pending row,
-    pending count). Increment k clusters rows L + m k .. L + m (k + 1) - 1,
-    which step m (k + 1) completes; its clusters are used from step
-    m (k + 1) + lag + 1 on. Until then the rows from the first not yet
-    clustered one up to the step's own row are pending."""
-    if wl.append_steps == 0:
-        assert lag == 0
-        return [(wl.C, 0, 0)] * T
-    m = wl.m_every
-    assert 0 <= lag < m, f"lag {lag} must be below the clustering period {m}"
-    assert wl.n_sink + m + lag <= wl.B, f"lag {lag}: n_sink + m + lag exceeds the budget"
-    sched = []
-    for t in range(T):
-        ev = (t - lag) // m if t >= lag else 0
-        sched.append((wl.C + wl.c_plus * ev, wl.L + m * ev, t + 1 - m * ev))
-    return sched
-
-
 class Case:
-    """Device-resident inputs and preallocated outputs/workspaces.
-
-    For the incremental workload the cache has room for the appended rows:
-    decode step s (counting from 1) writes row L + s - 1 of K and V, selects
-    with the rows not yet clustered as pending tokens, attends, and after
-    steps m, 2m, ... clusters the newest m rows into c_plus clusters that are
-    appended to the centroids and the CSR.
-
-    With lag D > 0 the clusters of the rows completed by step m(k + 1) are
-    first used at step m(k + 1) + D + 1; until then those rows stay pending
-    (at most m + D pending rows, so n_sink + m + D <= B). With `side` set to a
-    stream, each increment runs there, forked after step m(k + 1) and joined
-    before step m(k + 1) + D + 1, overlapping the D decode steps between.
-    The two streams write disjoint memory: the increment writes centroid
-    slots, CSR offsets and token slots past those the decode steps read
-    (the one shared word, the offset that ends the last older cluster, is
-    rewritten with the value it holds), and reads K rows no step writes
-    after the fork. Without `side` the increment runs on the decode stream at
-    the fork point, which gives the same results in sequence."""
+    """Device-resident inputs and preallocated outputs/workspaces of one
+    workload. The prompt's clustering, the decode steps and, for the
+    incremental workload, the decode-time increments (forked onto `side`
+    and joined `lag` steps later) run through the package's
+    IncrementalDecoder; decode step t first appends row L + t of K and V.
+    The host-resident K/V variants (`kv_host`) run their own steps."""
 
     def __init__(self, wl, T, dev, fused=True, lag=0, side=None, kv_host=None, cache_R=1,
                  rho=None):
@@ -143,36 +111,18 @@ class Case:
             app = [synth.make_appended(wl, h, T) for h in range(H)]
             self.KVa = bf(np.stack([np.stack([x[0] for x in app]), np.stack([x[1] for x in app])]))
         log(f"inputs drawn in {time.time() - t0:.1f}s")
-        c_cap = C + (wl.c_plus * self.n_ev if self.inc else 0)
-        t_cap = (L - wl.n_sink) + (wl.m_every * self.n_ev if self.inc else 0)
-        i32 = dict(dtype=torch.int32, device=dev)
-        self.cent = torch.zeros((H, c_cap, d), dtype=torch.float32, device=dev)
-        self.asg = torch.empty((H, L), **i32)
-        self.off = torch.zeros((H, c_cap + 1), **i32)
-        self.tok = torch.zeros((H, t_cap), **i32)
-        self.idx = torch.empty((T, H, B), **i32)
-        self.nsel = torch.empty((T, H), **i32)
-        self.O = torch.empty((T, H * G, d), dtype=torch.float32, device=dev)
-        cd = ck.ClusterDesc(H=H, d=d, L=L, k_head_stride=Lcap * d, token_base=0,
-                            n_sink=wl.n_sink, C=C, iters=wl.iters, dtype=ck.CKV_BF16,
-                            c_base=0, c_cap=c_cap, t_base=0, t_cap=t_cap)
-        sd = ck.SelectDesc(H=H, G=G, d=d, C=c_cap, c_cap=c_cap, n_sink=wl.n_sink,
-                           t_cap=t_cap, pending_begin=0, n_pending=0, B=B,
-                           dtype=ck.CKV_BF16)
-        ad = ck.AttnDesc(H=H, G=G, d=d, B=B, kv_head_stride=Lcap * d, kv_rows=Lcap,
-                         scale=0.0, dtype=ck.CKV_BF16)
+        from sparse_decode_attention_ckv_amd.incremental import IncrementalDecoder
+        # the prompt's clustering, the decode steps and (incremental workload)
+        # the decode-time increments on their own stream: the package's helper
+        self.dec = IncrementalDecoder(
+            self.K, self.V, self.Q, L=L, n_sink=wl.n_sink, C=C, iters=wl.iters, B=B,
+            m=wl.m_every if self.inc else 0, c_plus=wl.c_plus, fused=fused,
+            before_step=self.append if self.inc else None)
+        d_ = self.dec
+        self.cent, self.asg, self.off, self.tok = d_.cent, d_.asg, d_.off, d_.tok
+        self.idx, self.nsel, self.O = d_.idx, d_.nsel, d_.out
+        self.ws_c, self.ws_s, self.ws_a, self.ws_f = d_.ws_c, d_.ws_s, d_.ws_a, d_.ws_f
         u8 = dict(dtype=torch.uint8, device=dev)
-        self.ws_c = torch.empty(ck.ckv_cluster_workspace(cd), **u8)
-        self.ws_s = torch.empty(max(ck.ckv_select_workspace(sd), 1), **u8)
-        self.ws_a = torch.empty(ck.ckv_attn_workspace(ad), **u8)
-        self.ws_f = torch.empty(ck.ckv_select_attn_workspace(sd, ad), **u8)
-        if self.inc:
-            m = wl.m_every
-            wd = ck.ClusterDesc(H=H, d=d, L=m, k_head_stride=Lcap * d, token_base=L,
-                                n_sink=0, C=wl.c_plus, iters=wl.iters, dtype=ck.CKV_BF16,
-                                c_base=C, c_cap=c_cap, t_base=L - wl.n_sink, t_cap=t_cap)
-            self.ws_w = torch.empty(ck.ckv_cluster_workspace(wd), **u8)
-            self.asg_w = torch.empty((H, m), **i32)
         self.ck = ck
         self.set_lag(lag, side)
         # K/V in pinned host memory: attention reads the selected rows from
@@ -195,28 +145,17 @@ class Case:
                 self.ws_ac = torch.empty(ck.ckv_attn_workspace(ad_c), **u8)
 
     def set_lag(self, lag, side):
-        if lag or side is not None:
-            assert self.inc, "a clustering lag applies to the incremental workload only"
-        self.lag, self.side = lag, side
-        self.sched = decode_schedule(self.wl, self.T, lag)
+        self.dec.set_lag(lag, side)
+        self.lag, self.side, self.sched = lag, side, self.dec.schedule
 
     def cluster(self):
-        wl = self.wl
-        self.ck.ckv_cluster(self.K[:, :wl.L], wl.n_sink, wl.C, wl.iters, centroids=self.cent,
-                            assign=self.asg, csr_offsets=self.off, csr_tokens=self.tok,
-                            workspace=self.ws_c)
+        self.dec.prefill()
 
     def append(self, t):
         self.KV[:, :, self.wl.L + t].copy_(self.KVa[:, :, t])
 
-    def increment(self, ev):
-        """Cluster rows L + m ev .. L + m (ev + 1) - 1 into c_plus clusters."""
-        wl = self.wl
-        m, base = wl.m_every, wl.L + wl.m_every * ev
-        self.ck.ckv_cluster(self.K[:, base:base + m], 0, wl.c_plus, wl.iters, token_base=base,
-                            centroids=self.cent, assign=self.asg_w, csr_offsets=self.off,
-                            csr_tokens=self.tok, c_base=wl.C + wl.c_plus * ev,
-                            t_base=base - wl.n_sink, workspace=self.ws_w)
+    def increment(self, k):
+        self.dec.increment(k)
 
     def select(self, t):
         wl = self.wl
@@ -264,93 +203,18 @@ class Case:
             for t in range(a, b):
                 self.host_step(t)
             return
-        for t in range(a, b):
-            if self.inc:
-                self.append(t)
-            if self.fused:
-                self.select_attn(t)
-            else:
-                self.select(t)
-                self.attn(t)
+        self.dec.run_steps(a, b)
 
     def decode(self):
-        import torch
-        main, join_t = torch.cuda.current_stream(), None
-        for t in range(self.T):
-            if t == join_t:
-                main.wait_stream(self.side)
-                join_t = None
-            self.steps(t, t + 1)
-            if self.inc and (t + 1) % self.wl.m_every == 0:
-                k = (t + 1) // self.wl.m_every - 1
-                if self.side is None:
-                    self.increment(k)
-                else:
-                    self.side.wait_stream(main)
-                    with torch.cuda.stream(self.side):
-                        self.increment(k)
-                    join_t = t + 1 + self.lag
-        if join_t is not None:
-            main.wait_stream(self.side)
+        if self.kv_host is not None:
+            self.steps(0, self.T)
+            return
+        self.dec.decode()
 
     def split_graphs(self):
-        """The decode loop with side-stream increments as linear HIP graphs:
-        the decode steps cut at every fork and join point, one graph per
-        piece, and one graph per increment. Returns a function that replays
-        them on the current stream and forks each increment onto the side
-        stream, joining it through an event before the step that first uses
-        its clusters.
-
-        The fork is paced from the host: the steps after the fork point are
-        submitted first, then the host waits for the decode stream to reach
-        the fork point and only then submits the increment, whose wait is by
-        then satisfied. A side queue holding a wait that is not yet
-        satisfied slows every launch of the decode chain for as long as it
-        waits (measured: about 4.5 us per step), and so does a single graph
-        with the side branch inside."""
-        import torch
-        wl, T, D = self.wl, self.T, self.lag
-        m = wl.m_every
-        fork = {m * (k + 1): k for k in range(self.n_ev)}          # after step index b - 1
-        join = {m * (k + 1) + D: k for k in range(self.n_ev)}      # before step index a
-        cuts = sorted({0, T} | {c for c in list(fork) + list(join) if 0 < c < T})
-        pieces = [(a, b, capture(lambda a=a, b=b: self.steps(a, b)))
-                  for a, b in zip(cuts, cuts[1:])]
-        incs = [capture(lambda k=k: self.increment(k)) for k in range(self.n_ev)]
-        forked = [torch.cuda.Event() for _ in range(self.n_ev)]
-        done = [torch.cuda.Event() for _ in range(self.n_ev)]
-        side = self.side
-
-        def submit(k):
-            forked[k].synchronize()
-            side.wait_event(forked[k])
-            with torch.cuda.stream(side):
-                incs[k].replay()
-            done[k].record(side)
-
-        def replay():
-            main, due, open_ = torch.cuda.current_stream(), None, []
-            for a, b, g in pieces:
-                if a in join:
-                    k = join[a]
-                    if due == k:                    # no step between fork and join
-                        submit(k)
-                        due = None
-                    main.wait_event(done[k])
-                    open_.remove(k)
-                g.replay()
-                if due is not None:                 # the steps after the fork are queued
-                    submit(due)
-                    due = None
-                if b in fork:
-                    due = fork[b]
-                    forked[due].record(main)
-                    open_.append(due)
-            if due is not None:
-                submit(due)
-            for k in open_:
-                main.wait_event(done[k])
-        return replay
+        """The decode loop as linear graphs with side-stream increments (the
+        package's IncrementalDecoder.split_graphs)."""
+        return self.dec.split_graphs()
 
     def snapshot(self):
         extra = [] if self.kv_host is None else [self.stats_acc]
@@ -358,12 +222,7 @@ class Case:
                                     self.nsel, self.O, *extra)]
 
 
-def capture(fn):
-    import torch
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        fn()
-    return g
+from sparse_decode_attention_ckv_amd.incremental import capture  # noqa: E402
 
 
 def time_graph(g, reps=1):

@@ -9,10 +9,14 @@ increment covers must be pending, and nothing else.
 """
 import pytest
 
-import bench
 import synth
+from sparse_decode_attention_ckv_amd.incremental import decode_schedule
 
 WL = synth.workload("llama8b_layer_32k_incremental")
+
+
+def _schedule(wl, T, lag=0):
+    return decode_schedule(wl.C, wl.L, wl.m_every, wl.c_plus, wl.n_sink, wl.B, T, lag)
 
 
 def _simulate(wl, T, lag):
@@ -29,7 +33,7 @@ def _simulate(wl, T, lag):
 @pytest.mark.parametrize("lag", [0, 1, 32, 319])
 def test_schedule_matches_event_simulation(lag):
     T = WL.append_steps
-    sched = bench.decode_schedule(WL, T, lag)
+    sched = _schedule(WL, T, lag)
     sim = _simulate(WL, T, lag)
     assert len(sched) == T
     for t, ((C, pb, npend), (C_s, pend)) in enumerate(zip(sched, sim)):
@@ -46,12 +50,12 @@ def test_schedule_matches_event_simulation(lag):
 
 @pytest.mark.parametrize("lag", [-1, WL.m_every, WL.B])
 def test_schedule_rejects_bad_lag(lag):
-    with pytest.raises(AssertionError):
-        bench.decode_schedule(WL, WL.append_steps, lag)
+    with pytest.raises(ValueError):
+        _schedule(WL, WL.append_steps, lag)
 
 
 def test_schedule_static_workload():
     wl = synth.workload("llama8b_layer_32k")
-    assert bench.decode_schedule(wl, 4) == [(wl.C, 0, 0)] * 4
-    with pytest.raises(AssertionError):
-        bench.decode_schedule(wl, 4, lag=3)
+    assert decode_schedule(wl.C, wl.L, 0, 0, wl.n_sink, wl.B, 4) == [(wl.C, 0, 0)] * 4
+    with pytest.raises(ValueError):
+        decode_schedule(wl.C, wl.L, 0, 0, wl.n_sink, wl.B, 4, lag=3)
