@@ -32,6 +32,7 @@ METRIC = ("ms per layer ckv_cluster at L=32k; µs/decode step select+sparse attn
           "% roofline")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (256 CUs, 2.4 GHz), TFLOP/s
 
 
 def parse():
@@ -47,6 +48,9 @@ def parse():
     ap.add_argument("--cluster-reps", type=int, default=20,
                     help="warm clustering replays timed one by one (mean, p50, p99)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure the headline workload only (by default the 32k layer's run "
+                         "also reports the other four workloads under \"configs\")")
     ap.add_argument("--separate", action="store_true",
                     help="decode with ckv_select + ckv_sparse_attn instead of ckv_select_attn")
     ap.add_argument("--async-cluster", type=int, default=None, metavar="D",
@@ -100,9 +104,10 @@ class Case:
             Q, _ = synth.make_query_stream(wl, T, rho)
 
         def bf(a):
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
-                torch.bfloat16).to(dev)
-        assert wl.dtype == "bf16"
+            if wl.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                    torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
         # K and V as the two halves of one cache tensor (same strides), so an
         # appended row of both is one copy
         self.KV = bf(np.stack([K, V]))
@@ -332,100 +337,143 @@ def recorded_traffic(kernel, workload):
     return int(float(rec["bytes_per_launch"]))
 
 
-def cpu_baseline(case, sample_steps, cluster_heads, threads):
-    """The oracle as it stands on a bounded sample of the same workload:
-    `sample_steps` decode steps (all KV heads, selection on the GPU's
-    centroids/CSR) and one K-means iteration on `cluster_heads` heads, first
-    on one core, then as independent per-head instances on `threads` host
-    threads (the oracle itself stays single-threaded; its C calls release the
-    interpreter lock)."""
+def host_cpu():
+    """The host's CPU model (/proc/cpuinfo) and its logical CPU count."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def cpu_baseline(case, sample_steps, cluster_heads, threads, cluster_tokens=None,
+                 full_cluster=False, increment=False):
+    """The oracle as it stands on a bounded sample of the same workload.
+
+    Decode: `sample_steps` steps (all KV heads, each step's selection on the
+    GPU's centroids and CSR with that step's cluster count and pending rows,
+    then attention), timed on one core. Clustering: with `full_cluster` the
+    whole K-means of the layer (every iteration, every head), measured;
+    otherwise one K-means iteration on `cluster_heads` heads -- on their first
+    `cluster_tokens` rows when given, which scales linearly with the rows --
+    extrapolated to the layer and labelled so. With `increment`, one
+    decode-time clustering event (the newest window into c_plus clusters,
+    all iterations, all heads) is timed as well. With threads > 1 the decode
+    sample and the clustering sample also run as independent per-head oracle
+    instances on that many host threads (the oracle stays single-threaded;
+    its C calls release the interpreter lock)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     wl = case.wl
     G = wl.G
+    sample_steps = max(1, min(sample_steps, case.T))
+    cluster_heads = max(1, min(cluster_heads, wl.H))
     mu = case.cent.double().cpu().numpy()
     off = case.off.cpu().numpy()
     tok = case.tok.cpu().numpy()
     Kf = case.K.double().cpu().numpy()
     Vf = case.V.double().cpu().numpy()
     Qf = case.Q[:sample_steps].double().cpu().numpy()
+    sched = case.sched
     oracle.select(Qf[0], mu, off, tok, wl.C, wl.n_sink, wl.B, G=G)   # load the library
 
-    def decode_head(h):
-        for t in range(sample_steps):
-            q = Qf[t, h * G:(h + 1) * G]
-            idx, ns, _ = oracle.select(q, mu[h:h + 1], off[h:h + 1], tok[h:h + 1], wl.C,
-                                       wl.n_sink, wl.B, G=G)
-            oracle.attn(q, Kf[h:h + 1], Vf[h:h + 1], idx, ns, G=G)
+    def step(t, h0=0, h1=None):
+        h1 = wl.H if h1 is None else h1
+        C, pb, npend = sched[t]
+        q = Qf[t, h0 * G:h1 * G]
+        idx, ns, _ = oracle.select(q, mu[h0:h1], off[h0:h1], tok[h0:h1], C, wl.n_sink, wl.B,
+                                   G=G, pending_begin=pb, n_pending=npend)
+        oracle.attn(q, Kf[h0:h1], Vf[h0:h1], idx, ns, G=G)
+
+    Lc = wl.L if cluster_tokens is None else min(wl.L, wl.n_sink + cluster_tokens)
 
     def iterate_head(h):
-        mu0 = oracle.init_centroids(Kf[h], wl.n_sink, wl.C)
-        a, _ = oracle.assign(Kf[h], wl.n_sink, mu0, mode=oracle.MIRROR)
-        oracle.update(Kf[h], wl.n_sink, a, mu0, mode=oracle.MIRROR)
+        K = Kf[h, :Lc]
+        mu0 = oracle.init_centroids(Kf[h, :wl.L], wl.n_sink, wl.C)
+        a, _ = oracle.assign(K, wl.n_sink, mu0, mode=oracle.MIRROR)
+        oracle.update(K, wl.n_sink, a, mu0, mode=oracle.MIRROR)
 
-    def timed(fn, heads, n):
+    def timed(fn, items, n):
         t0 = time.perf_counter()
         if n == 1:
-            for h in heads:
-                fn(h)
+            for x in items:
+                fn(x)
         else:
             with ThreadPoolExecutor(max_workers=n) as ex:
-                list(ex.map(fn, heads))
+                list(ex.map(fn, items))
         return time.perf_counter() - t0
 
     t0 = time.perf_counter()
     for t in range(sample_steps):
-        idx, ns, _ = oracle.select(Qf[t], mu, off, tok, wl.C, wl.n_sink, wl.B, G=G)
-        oracle.attn(Qf[t], Kf, Vf, idx, ns, G=G)
+        step(t)
     dec_s = (time.perf_counter() - t0) / sample_steps
-    it_s = timed(iterate_head, range(cluster_heads), 1) / cluster_heads
+    Lp = wl.L - wl.n_sink
+    out = {"value": round(dec_s * 1e6, 1), "unit": "us/decode_step", "cores": 1,
+           "kind": "oracle"}
+    if full_cluster:
+        t0 = time.perf_counter()
+        oracle.cluster(Kf[:, :wl.L], wl.n_sink, wl.C, wl.iters, mode=oracle.EXACT
+                       if wl.dtype != "bf16" else oracle.MIRROR)
+        out["cluster_ms_per_layer"] = round((time.perf_counter() - t0) * 1e3, 2)
+        clus = f"the whole K-means of the layer ({wl.iters} iterations, {wl.H} heads), measured"
+    else:
+        it_s = timed(iterate_head, range(cluster_heads), 1) / cluster_heads
+        scale = Lp / (Lc - wl.n_sink)
+        out["cluster_ms_per_layer_extrapolated"] = round(it_s * scale * wl.H * wl.iters * 1e3, 1)
+        clus = (f"1 K-means iteration on {cluster_heads} of {wl.H} heads"
+                + (f" over their first {Lc - wl.n_sink} of {Lp} rows" if Lc < wl.L else "")
+                + f", extrapolated to {wl.H} heads x {wl.iters} iterations"
+                + (" x the rows" if Lc < wl.L else ""))
+    if increment:
+        m = wl.m_every
+        t0 = time.perf_counter()
+        oracle.cluster(Kf[:, wl.L:wl.L + m], 0, wl.c_plus, wl.iters, mode=oracle.MIRROR,
+                       token_base=wl.L)
+        out["increment_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        clus += f"; one decode-time increment ({m} rows into {wl.c_plus} clusters, all heads)"
+    out["sample"] = (f"{sample_steps} decode steps (select + sparse attention, all {wl.H} KV "
+                     f"heads) and {clus}; C oracle (fp64), single-threaded")
     n = max(1, min(threads, wl.H))
-    dec_n = timed(decode_head, range(wl.H), n) / sample_steps
-    it_n = timed(iterate_head, range(cluster_heads), n) * wl.H / cluster_heads
-    return {
-        "value": round(dec_s * 1e6, 1), "unit": "us/decode_step", "cores": 1,
-        "kind": "oracle",
-        "sample": (f"{sample_steps} decode steps (select + sparse attention, all {wl.H} KV "
-                   f"heads) and 1 K-means iteration on {cluster_heads} of {wl.H} heads, "
-                   f"C oracle (fp64), single-threaded"),
-        "cluster_ms_per_layer_extrapolated": round(it_s * wl.H * wl.iters * 1e3, 1),
-        "per_head_threads": {
+    if n > 1:
+        dec_n = timed(lambda h: [step(t, h, h + 1) for t in range(sample_steps)],
+                      range(wl.H), n) / sample_steps
+        it_n = timed(iterate_head, range(cluster_heads), n) * wl.H / cluster_heads
+        out["per_head_threads"] = {
             "cores": n, "value": round(dec_n * 1e6, 1), "unit": "us/decode_step",
-            "cluster_ms_per_layer_extrapolated": round(it_n * wl.iters * 1e3, 1),
-            "sample": f"the same sample as independent per-head oracle calls on {n} threads"},
-        "host_cpu": platform.processor() or platform.machine(),
-        "host_threads": os.cpu_count(),
-    }
+            "cluster_ms_per_layer_extrapolated": round(
+                it_n * (Lp / (Lc - wl.n_sink)) * wl.iters * 1e3, 1),
+            "sample": f"the same sample as independent per-head oracle calls on {n} threads"}
+    out["host_cpu"] = host_cpu()
+    out["host_threads"] = os.cpu_count()
+    return out
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}): every KV head is an independent problem, so a multi-GPU run would "
-              "shard heads with no communication; it is not built or measured here.",
-              flush=True)
-        sys.exit(2)
-
+def run_workload(name, args, peaks, *, steps, warmup, reps, cluster_reps, decode_steps=None,
+                 async_cluster=None, kv_host_mode=None, cpu_sample=None):
+    """Everything measured on one workload: the whole step (clustering +
+    decode loop) replayed from HIP graphs checked bitwise against an eager
+    run, clustering latency over warm replays, cold decode steps, live
+    per-call timings and their rooflines, and the oracle on a bounded
+    sample. Returns the workload's record."""
     import torch
 
     import synth
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
     dev = "cuda:0"
-    wl = synth.workload(args.workload)
-    T = wl.steps if args.decode_steps is None else args.decode_steps
+    wl = synth.workload(name)
+    T = wl.steps if decode_steps is None else decode_steps
     lag, side = 0, None
-    if args.async_cluster is not None:
-        lag, side = args.async_cluster, torch.cuda.Stream(device=dev)
+    if async_cluster is not None:
+        lag, side = async_cluster, torch.cuda.Stream(device=dev)
     rho = args.query_rho
-    if args.kv_host is not None and rho is None:
+    if kv_host_mode is not None and rho is None:
         rho = 0.9
-    case = Case(wl, T, dev, fused=not args.separate, lag=lag, side=side, kv_host=args.kv_host,
+    case = Case(wl, T, dev, fused=not args.separate, lag=lag, side=side, kv_host=kv_host_mode,
                 cache_R=args.cache_steps, rho=rho)
 
     # eager reference run
@@ -486,15 +534,15 @@ def main():
         g_cluster.replay()
         decode_replay()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
     t_wall = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
-    for k in range(args.steps):
+    for k in range(steps):
         ev[3 * k].record()
         g_cluster.replay()
         ev[3 * k + 1].record()
@@ -503,9 +551,9 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms_step = start.elapsed_time(stop) / args.steps
-    cl_ms = sum(ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(args.steps)) / args.steps
-    dec_ms = sum(ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(args.steps)) / args.steps
+    ms_step = start.elapsed_time(stop) / steps
+    cl_ms = sum(ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(steps)) / steps
+    dec_ms = sum(ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(steps)) / steps
     dec_us = dec_ms * 1e3 / T
     if kv_host is not None:
         kv_host["host_GB/s_over_step"] = round(kv_host["host_bytes_per_step"] / dec_us / 1e3, 2)
@@ -513,12 +561,12 @@ def main():
             f"step ({kv_host['host_GB/s_over_step']} GB/s over the step)"
             + (f", {kv_host['cluster_rows_from_cache']:.3f} of cluster rows from the cache"
                if kv_host["mode"] == "cache" else ""))
-    log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): cluster {cl_ms:.3f} ms, "
+    log(f"step {ms_step:.3f} ms (wall {wall / steps * 1e3:.3f} ms): cluster {cl_ms:.3f} ms, "
         f"decode {dec_us:.2f} us/step")
 
     # clustering latency distribution: warm replays, each between HIP events
     cl_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.cluster_reps)]
+             for _ in range(cluster_reps)]
     for a, b in cl_ev:
         a.record()
         g_cluster.replay()
@@ -539,12 +587,12 @@ def main():
         f"p99 {pct(cl_reps, 99):.3f} ms; cold decode step {cold_us:.2f} us")
 
     # live per-call timings (back-to-back launches of one call, HIP events)
-    g_sel = capture(lambda: [case.select(0) for _ in range(args.reps)])
-    g_att = capture(lambda: [case.attn(0) for _ in range(args.reps)])
-    g_fus = capture(lambda: [case.select_attn(0) for _ in range(args.reps)])
-    sel_us = time_graph(g_sel) * 1e3 / args.reps
-    att_us = time_graph(g_att) * 1e3 / args.reps
-    fus_us = time_graph(g_fus) * 1e3 / args.reps
+    g_sel = capture(lambda: [case.select(0) for _ in range(reps)])
+    g_att = capture(lambda: [case.attn(0) for _ in range(reps)])
+    g_fus = capture(lambda: [case.select_attn(0) for _ in range(reps)])
+    sel_us = time_graph(g_sel) * 1e3 / reps
+    att_us = time_graph(g_att) * 1e3 / reps
+    fus_us = time_graph(g_fus) * 1e3 / reps
     inc_ms = None
     if case.inc:                          # one decode-time clustering event, back to back
         g_inc = capture(lambda: [case.increment(0) for _ in range(16)])
@@ -552,7 +600,7 @@ def main():
     torch.cuda.synchronize()
     H, G, d, C, B = wl.H, wl.G, wl.d, wl.C, wl.B
     n_sel = case.nsel[0].cpu()
-    e = 2  # bf16 bytes
+    e = 2 if wl.dtype == "bf16" else 4      # element bytes
     att_bytes = sum(2 * int(n) * d * e + 4 * B + G * d * e + G * d * 4 for n in n_sel)
     sel_bytes = sum(C * d * 4 + 4 * (C + 1) + 4 * (int(n) - wl.n_sink) + 4 * B + G * d * e
                     for n in n_sel)
@@ -584,7 +632,11 @@ def main():
         kernels["ckv_cluster_increment"] = {"ms_per_call": round(inc_ms, 4),
                                             "calls_per_step": case.n_ev}
     dom = max(share, key=share.get)
-    if dom == "ckv_cluster":
+    if dom == "ckv_cluster" and wl.dtype != "bf16":
+        # fp32 keys: the assignment's dot products are vector fp32 FMAs
+        roof = {"kernel": dom, "bound": "alu", "achieved": round(assign_flop / cl_ms / 1e9, 2),
+                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    elif dom == "ckv_cluster":
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(assign_flop / cl_ms / 1e9, 2),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     else:
@@ -592,18 +644,18 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": k["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    peaks = measured_peaks(dev)
-    roof["measured_peak"] = (peaks["bf16_gemm_TFLOP/s"] if roof["bound"] == "mfma"
-                             else peaks["hbm_copy_GB/s"])
-    roof["frac_of_measured_peak"] = round(roof["achieved"] / roof["measured_peak"], 4)
+    if roof["bound"] != "alu":
+        roof["measured_peak"] = (peaks["bf16_gemm_TFLOP/s"] if roof["bound"] == "mfma"
+                                 else peaks["hbm_copy_GB/s"])
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / roof["measured_peak"], 4)
     roof["traffic"] = recorded_traffic(dom, wl.name)
     kernels["ckv_cluster"]["assign_frac_of_measured_gemm"] = round(
         assign_flop / cl_ms / 1e9 / peaks["bf16_gemm_TFLOP/s"], 4)
     log(f"measured peaks: HBM copy {peaks['hbm_copy_GB/s']} GB/s, bf16 GEMM "
         f"{peaks['bf16_gemm_TFLOP/s']} TFLOP/s")
-    if dom == "ckv_select_attn" and not case.inc:
+    if dom in ("ckv_select_attn", "ckv_sparse_attn", "ckv_select"):
         # the same call with the MALL and L2 flushed before it
-        cold_gbs = fus_bytes / cold_us / 1e3
+        cold_gbs = (fus_bytes if case.fused else sel_bytes + att_bytes) / cold_us / 1e3
         roof["cold"] = {"us_per_call": round(cold_us, 3), "achieved": round(cold_gbs, 1),
                         "frac": round(cold_gbs / HBM_PEAK_GBS, 4),
                         "frac_of_measured_peak": round(cold_gbs / peaks["hbm_copy_GB/s"], 4)}
@@ -612,16 +664,13 @@ def main():
         + f"; dominant {dom}")
 
     cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(case, sample_steps=min(T, 128), cluster_heads=wl.H,
-                           threads=min(16, os.cpu_count() or 1))
+    if cpu_sample is not None:
+        log(f"{wl.name}: timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(case, **cpu_sample)
 
     out = {
-        "metric": METRIC, "value": round(dec_us, 3), "unit": "us/decode_step",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "value": round(dec_us, 3), "ms_per_step": round(ms_step, 4), "wl": wl,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "config": {"workload": wl.name, "kv_heads": H, "q_heads_per_kv": G, "d": d, "L": wl.L,
                    "n_sink": wl.n_sink, "C": C, "iters": wl.iters, "B": B,
                    "decode_steps": T, "parallelism": "none (1 GPU)",
@@ -635,9 +684,9 @@ def main():
                                  "p99": round(pct(cl_reps, 99), 4)},
         "decode_us_per_step": round(dec_us, 3),
         "decode_cold_us_per_step": round(cold_us, 3),
-        "decode_path": ("ckv_select + ckv_sparse_attn over host K/V" if args.kv_host == "direct"
+        "decode_path": ("ckv_select + ckv_sparse_attn over host K/V" if kv_host_mode == "direct"
                         else "ckv_select + ckv_cache_step + ckv_sparse_attn over the cache"
-                        if args.kv_host == "cache"
+                        if kv_host_mode == "cache"
                         else "ckv_select + ckv_sparse_attn" if args.separate
                         else "ckv_select_attn"),
         **({"kv_host": kv_host} if kv_host else {}),
@@ -646,6 +695,79 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
+    del case
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+# The other workloads reported beside the headline one, and the bounded
+# oracle sample of each (see cpu_baseline).
+OTHER_CONFIGS = {
+    "single_head_fp32_2k": dict(sample_steps=1, cluster_heads=1, threads=1, full_cluster=True),
+    "llama8b_layer_32k_batch8": dict(sample_steps=4, cluster_heads=2, threads=1),
+    "llama8b_layer_32k_incremental": dict(sample_steps=16, cluster_heads=1, threads=1,
+                                          increment=True),
+    "llama8b_layer_128k": dict(sample_steps=4, cluster_heads=1, threads=1, cluster_tokens=4096),
+}
+
+
+def config_summary(rec):
+    """The part of a workload's record reported per config."""
+    keys = ("value", "dtype", "config", "cluster_ms_per_layer", "cluster_ms_warm_reps",
+            "decode_us_per_step", "decode_cold_us_per_step", "decode_path", "roofline",
+            "kernels", "cpu_baseline")
+    out = {k: rec[k] for k in keys if k in rec}
+    out["unit"] = "us/decode_step"
+    return out
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): every KV head is an independent problem, so a multi-GPU run would "
+              "shard heads with no communication; it is not built or measured here.",
+              flush=True)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    peaks = measured_peaks("cuda:0")
+    headline_cpu = None if args.no_cpu_baseline else dict(
+        sample_steps=128, cluster_heads=8, threads=min(16, os.cpu_count() or 1))
+    rec = run_workload(args.workload, args, peaks, steps=args.steps, warmup=args.warmup,
+                       reps=args.reps, cluster_reps=args.cluster_reps,
+                       decode_steps=args.decode_steps, async_cluster=args.async_cluster,
+                       kv_host_mode=args.kv_host, cpu_sample=headline_cpu)
+    configs = None
+    plain = (args.workload == "llama8b_layer_32k" and args.decode_steps is None
+             and args.async_cluster is None and args.kv_host is None and not args.separate)
+    if plain and not args.no_configs:
+        configs = {}
+        for name, sample in OTHER_CONFIGS.items():
+            log(f"config {name} ...")
+            r = run_workload(name, args, peaks, steps=2, warmup=1, reps=64, cluster_reps=5,
+                             cpu_sample=None if args.no_cpu_baseline else sample)
+            configs[name] = config_summary(r)
+    wl = rec["wl"]
+    out = {
+        "metric": METRIC, "value": rec["value"], "unit": "us/decode_step",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"], "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": rec["dtype"], "data": "synthetic",
+        "config": rec["config"],
+        **{k: v for k, v in rec.items() if k not in ("value", "ms_per_step", "wl", "dtype",
+                                                       "config")},
+    }
+    out["measured_peaks"] = peaks
+    if configs is not None:
+        out["configs"] = configs
+    del wl
     print(json.dumps(out), flush=True)
 
 
