@@ -530,9 +530,12 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
         // tiles (earlier, the waves whose rows came first would delay the
         // others' first rows with their prefetch), or after them when round
         // 0 is too short to reach that point
+        // (L2: no second register set -- its bias leaves no room -- so the
+        // next tile's rows are requested only once this tile is done)
         auto prefetch = [&]() {
-            as_load_b((const u32x4 *)(kt + (int64_t)hp * Lp * kD), Lp,
-                      (int64_t)tp * kAsTok + wave * 64, col, kq, bn);
+            if constexpr (!BIAS)
+                as_load_b((const u32x4 *)(kt + (int64_t)hp * Lp * kD), Lp,
+                          (int64_t)tp * kAsTok + wave * 64, col, kq, bn);
         };
         auto run = [&](int r) {
             const int rb = r * kAsRound;
@@ -585,10 +588,15 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
         for (int u = 0; u < 4; ++u) res[u] = as_merge(bv[u], COS ? as_cos_id(bk[u], kq) : bc[u]);
         // the next tile's fragments become current (this waits for them),
         // then the labels are stored
+        if constexpr (BIAS) {
+            as_load_b((const u32x4 *)(kt + (int64_t)hp * Lp * kD), Lp,
+                      (int64_t)tp * kAsTok + wave * 64, col, kq, b);
+        } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) b[u][s2] = bn[u][s2];
+                for (int s2 = 0; s2 < 4; ++s2) b[u][s2] = bn[u][s2];
+        }
         const int64_t tok = tok0 + lane;
         const int v = (kq == 0) ? res[0] : (kq == 1) ? res[1] : (kq == 2) ? res[2] : res[3];
         if (tok < Lp) assign[(int64_t)h * L + n_sink + tok] = v;
