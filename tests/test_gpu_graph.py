@@ -1,8 +1,9 @@
-"""GPU: decode calls reusing one workspace, and captured as a HIP graph.
+"""GPU: calls reusing one workspace, and captured as a HIP graph.
 
 These tests reuse one workspace for many calls and replay a captured decode
-loop several times (with eager work and synchronisations between replays),
-checking every result bitwise against eager calls.
+loop and a captured clustering call several times (with eager work and
+synchronisations between replays), checking every result bitwise against
+eager calls.
 """
 import numpy as np
 import pytest
@@ -81,4 +82,50 @@ def test_decode_graph_replay_matches_eager():
         loop()                                                 # eager work between replays
         torch.cuda.synchronize()
         for a, b in zip(ref, (idx, ns, O)):
+            assert torch.equal(a, b), rep
+
+
+@pytest.mark.parametrize("H,L,C", [
+    (4, 8192, 101),      # C <= 512: the two-launch CSR over 2048-token tiles
+    (2, 12000, 600),     # C > 512: the three-pass CSR, two LDS rounds in the assignment
+])
+def test_cluster_graph_replay_matches_eager(H, L, C):
+    """The whole Lloyd loop (normalisation, initial centroids, 10 x assignment,
+    counting sort and update) captured once and replayed 3 times, with eager
+    work between the replays: every replay equals the eager call bitwise."""
+    say(f"ckv_cluster captured as a HIP graph: H={H} L={L} C={C}, 3 replays")
+    wl = synth.workload(1)
+    K, _, _ = synth.make_kv(wl, L=L, heads=range(H))
+    Kd = to_dev(K, "bf16")
+    ref = ck.ckv_cluster(Kd, 16, C, 10)
+    torch.cuda.synchronize()
+    out = [torch.empty_like(x) for x in ref]
+    desc = ck.ClusterDesc(H=H, d=128, L=L, k_head_stride=Kd.stride(0), token_base=0, n_sink=16,
+                          C=C, iters=10, dtype=ck.CKV_BF16, c_base=0, c_cap=C, t_base=0,
+                          t_cap=L - 16, metric=ck.CKV_COSINE)
+    ws = torch.empty(ck.ckv_cluster_workspace(desc), dtype=torch.uint8, device=DEV)
+
+    def call():
+        ck.ckv_cluster(Kd, 16, C, 10, centroids=out[0], assign=out[1], csr_offsets=out[2],
+                       csr_tokens=out[3], workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    junk = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+    for rep in range(3):
+        for x in out:
+            x.view(torch.uint8).fill_(0xA5)
+        junk.fill_(rep)                                  # eager work between the replays
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, out):
             assert torch.equal(a, b), rep
