@@ -181,40 +181,81 @@ __global__ __launch_bounds__(kNkRows) void k_normalize_keys_bf16(
     }
 }
 
+// fp32 keys: the same scheme with 64-row blocks (512 B rows, padded to 528 B
+// in LDS) and the quotients kept in fp32: one thread per row runs the fp64
+// chain of |x|^2 over j = 0..127 in order, then x_j / |x| in fp64, rounded
+// once to fp32.
+constexpr int kNfRows = 64;              // rows per workgroup (one per thread)
+constexpr int kNfStride = 33;            // LDS row stride in 16-byte chunks
+
 template <bool UNIT>
-__global__ __launch_bounds__(256) void k_normalize_keys_f32(
+__global__ __launch_bounds__(kNfRows) void k_normalize_keys_f32(
     const float *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
     float *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
-    const int h = blockIdx.y;
+    __shared__ float4 rows[kNfRows * kNfStride];
+    const int h = blockIdx.y, tid = threadIdx.x;
     if (blockIdx.x == 0)   // sink rows are labelled -1
-        for (int i = threadIdx.x; i < n_sink; i += 256) assign[(int64_t)h * L + i] = -1;
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= Lp) return;
-    const float *src = K + h * head_stride + (n_sink + r) * kD;
-    float *dst = kt + ((int64_t)h * Lp + r) * kD;
-    if (!UNIT) {
-        for (int j = 0; j < kD; ++j) dst[j] = src[j];
-        return;
+        for (int i = tid; i < n_sink; i += kNfRows) assign[(int64_t)h * L + i] = -1;
+    const int64_t r0 = (int64_t)blockIdx.x * kNfRows;
+    const int nrow = (int)(Lp - r0 < kNfRows ? Lp - r0 : kNfRows);
+    const float4 *src = (const float4 *)(K + h * head_stride + (n_sink + r0) * kD);
+    float4 *dst = (float4 *)(kt + ((int64_t)h * Lp + r0) * kD);
+    // coalesced loads: chunk e = 32 row + q, 8 in flight at a time
+#pragma unroll
+    for (int k0 = 0; k0 < 32; k0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = tid + kNfRows * (k0 + k);
+            v[k] = src[(e >> 5) < nrow ? e : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = tid + kNfRows * (k0 + k);
+            rows[(e >> 5) * kNfStride + (e & 31)] = v[k];
+        }
     }
-    double ss = 0.0;
-    for (int j = 0; j < kD; ++j) ss = __fma_rn((double)src[j], (double)src[j], ss);
-    const double n = sqrt(ss);
-    for (int j = 0; j < kD; ++j) dst[j] = (ss > 0.0) ? (float)((double)src[j] / n) : 0.f;
+    __syncthreads();
+    if (UNIT && tid < nrow) {
+        float4 *row = rows + tid * kNfStride;
+        double ss = 0.0;
+        for (int q = 0; q < 32; ++q) {
+            const float4 v = row[q];
+            ss = __fma_rn((double)v.x, (double)v.x, ss);
+            ss = __fma_rn((double)v.y, (double)v.y, ss);
+            ss = __fma_rn((double)v.z, (double)v.z, ss);
+            ss = __fma_rn((double)v.w, (double)v.w, ss);
+        }
+        const double n = sqrt(ss);
+        const bool nz = ss > 0.0;
+        for (int q = 0; q < 32; ++q) {
+            const float4 v = row[q];
+            row[q] = nz ? make_float4((float)((double)v.x / n), (float)((double)v.y / n),
+                                      (float)((double)v.z / n), (float)((double)v.w / n))
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        const int e = tid + kNfRows * k;
+        if ((e >> 5) < nrow) dst[e] = rows[(e >> 5) * kNfStride + (e & 31)];
+    }
 }
 
 hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *assign,
                                  hipStream_t s) {
-    dim3 grid((unsigned)((p.Lp + 255) / 256), p.H);
-    static_assert(kNkRows == 256, "one grid for both element types");
     const bool unit = p.metric == kCosine;
     if (p.dtype == 1)
         hipLaunchKernelGGL(unit ? k_normalize_keys_bf16<true> : k_normalize_keys_bf16<false>,
-                           grid, dim3(kNkRows), 0, s, (const uint16_t *)K, p.k_head_stride,
+                           dim3((unsigned)((p.Lp + kNkRows - 1) / kNkRows), p.H),
+                           dim3(kNkRows), 0, s, (const uint16_t *)K, p.k_head_stride,
                            p.n_sink, p.Lp, (uint16_t *)p.kt, assign, p.L);
     else
         hipLaunchKernelGGL(unit ? k_normalize_keys_f32<true> : k_normalize_keys_f32<false>,
-                           grid, dim3(256), 0, s, (const float *)K, p.k_head_stride,
-                           p.n_sink, p.Lp, (float *)p.kt, assign, p.L);
+                           dim3((unsigned)((p.Lp + kNfRows - 1) / kNfRows), p.H),
+                           dim3(kNfRows), 0, s, (const float *)K, p.k_head_stride, p.n_sink,
+                           p.Lp, (float *)p.kt, assign, p.L);
     return hipGetLastError();
 }
 
@@ -605,33 +646,79 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
     }
 }
 
-// assign (fp32): one thread per token, fp32 dot product over j = 0..127 of
-// the rows in kt and mt (unit rows for the cosine), plus the cluster's bias
-// when mb is given (L2), argmax with ties to the lower id. Used for fp32 keys.
-__global__ __launch_bounds__(256) void k_assign_f32(
+// assign (fp32): a workgroup takes 64 tokens; wave g scores them against the
+// clusters c = g, g + 8, g + 16, ... (one token per lane, the cluster rows
+// uniform across the wave, so they come through the scalar cache), each
+// score the fp32 dot product over j = 0..127 in order of the rows in kt and
+// mt (unit rows for the cosine), plus the cluster's bias when mb is given
+// (L2). Each wave keeps the strictly larger score in ascending id order;
+// the eight candidates of a token then merge on (score, lower id), which is
+// the argmax with ties to the lower id over all clusters (cluster 0 when no
+// score exceeds -inf, as in one sequential scan). Used for fp32 keys.
+constexpr int kAfTok = 64, kAfGroups = 8;
+
+__global__ __launch_bounds__(64 * kAfGroups) void k_assign_f32(
     const float *__restrict__ kt, const float *__restrict__ mt, const float *__restrict__ mb,
     int64_t Lp, int C, int Cpad, int32_t *__restrict__ assign, int64_t L, int n_sink) {
+    __shared__ float sbest[kAfGroups][kAfTok];
+    __shared__ int sarg[kAfGroups][kAfTok];
     const int h = blockIdx.y;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= Lp) return;
+    const int lane = threadIdx.x & 63;
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t i = (int64_t)blockIdx.x * kAfTok + lane;
+    const int64_t ii = i < Lp ? i : Lp - 1;
     float k[kD];
-    const float *src = kt + ((int64_t)h * Lp + i) * kD;
+    const float *src = kt + ((int64_t)h * Lp + ii) * kD;
 #pragma unroll
-    for (int j = 0; j < kD; ++j) k[j] = src[j];
+    for (int j = 0; j < kD; j += 4) {
+        const float4 v = *(const float4 *)(src + j);
+        k[j] = v.x;
+        k[j + 1] = v.y;
+        k[j + 2] = v.z;
+        k[j + 3] = v.w;
+    }
     float best = -INFINITY;
-    int arg = 0;
-    for (int c = 0; c < C; ++c) {
-        const float *m = mt + ((int64_t)h * Cpad + c) * kD;
-        float s = 0.f;
+    int arg = 0x7fffffff;
+    // two of the wave's clusters at a time: two independent chains, both
+    // rows requested together
+    for (int c = g; c < C; c += 2 * kAfGroups) {
+        const int c2 = c + kAfGroups;
+        const float *m1 = mt + ((int64_t)h * Cpad + c) * kD;
+        const float *m2 = mt + ((int64_t)h * Cpad + (c2 < C ? c2 : c)) * kD;
+        float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-        for (int j = 0; j < kD; ++j) s = __fmaf_rn(k[j], m[j], s);
-        if (mb) s += mb[(int64_t)h * Cpad + c];
-        if (s > best) {
-            best = s;
+        for (int j = 0; j < kD; ++j) {
+            s1 = __fmaf_rn(k[j], m1[j], s1);
+            s2 = __fmaf_rn(k[j], m2[j], s2);
+        }
+        if (mb) {
+            s1 += mb[(int64_t)h * Cpad + c];
+            s2 += mb[(int64_t)h * Cpad + (c2 < C ? c2 : c)];
+        }
+        if (s1 > best) {
+            best = s1;
             arg = c;
         }
+        if (c2 < C && s2 > best) {
+            best = s2;
+            arg = c2;
+        }
     }
-    assign[(int64_t)h * L + n_sink + i] = arg;
+    sbest[g][lane] = best;
+    sarg[g][lane] = arg;
+    __syncthreads();
+    if (g == 0 && i < Lp) {
+        for (int q = 1; q < kAfGroups; ++q) {
+            const float b2 = sbest[q][lane];
+            const int a2 = sarg[q][lane];
+            if (a2 != 0x7fffffff && (b2 > best || (b2 == best && a2 < arg))) {
+                best = b2;
+                arg = a2;
+            }
+        }
+        // no score above -inf anywhere (as a sequential scan from cluster 0)
+        assign[(int64_t)h * L + n_sink + i] = arg == 0x7fffffff ? 0 : arg;
+    }
 }
 
 hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s) {
@@ -646,8 +733,8 @@ hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s) {
                            (const uint16_t *)p.kt, (const uint16_t *)p.mt, (const float *)p.mb,
                            p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink, tph, n_tiles);
     } else {
-        dim3 grid((unsigned)((p.Lp + 255) / 256), p.H);
-        hipLaunchKernelGGL(k_assign_f32, grid, dim3(256), 0, s, (const float *)p.kt,
+        dim3 grid((unsigned)((p.Lp + kAfTok - 1) / kAfTok), p.H);
+        hipLaunchKernelGGL(k_assign_f32, grid, dim3(64 * kAfGroups), 0, s, (const float *)p.kt,
                            (const float *)p.mt, p.metric == kL2 ? (const float *)p.mb : nullptr,
                            p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink);
     }
