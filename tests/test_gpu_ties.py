@@ -16,7 +16,8 @@ also be the oracle's.
 The pairs sit at every distance the kernel distinguishes: the same lane's
 rows, another lane group of the same M tile, another M tile, another argmax
 group and another LDS round (C = 600 holds two rounds); the small-window
-kernel (C <= 16) and the fp32 kernel are covered too.
+kernel (C <= 16) and the fp32 kernel are covered too (its eight cluster
+groups: pairs (0, 1) and (2, 6) sit in different groups, (3, 19) in one).
 """
 import numpy as np
 import pytest
