@@ -78,10 +78,11 @@ int ckv_abi_version(void);
  * The page's C0 = L/80 and, for decode-time increments, C+ = 4 clusters
  * over the newest m = 320 tokens with n_sink = 0, are the caller's choice.
  *
- * Assignment scores are computed on bf16 unit vectors (each vector scaled by
- * 1/|x| in fp64, rounded to fp32 then to bf16) with fp32 accumulation for
- * CKV_BF16 keys, and on fp32 unit vectors with fp32 accumulation for
- * CKV_F32 keys. Centroid means are accumulated in fp64 and stored as fp32.
+ * A key's cosine with mu is <k, mu/|mu|> / |k|, and |k| is common to all of
+ * its scores, so the assignment takes the largest <k, mu/|mu|>: the key as
+ * stored against the unit centroid (mu/|mu| in fp64, rounded to fp32, then
+ * to bf16 for CKV_BF16 keys), with fp32 accumulation. Keys are never
+ * normalised. Centroid means are accumulated in fp64 and stored as fp32.
  *
  * desc->metric selects the distance of the assignment (the update is the
  * mean of the raw keys for every metric):
@@ -129,7 +130,9 @@ size_t ckv_cluster_workspace(const ckv_cluster_desc *desc);
 
 /* K: window row 0 of head 0, element type desc->dtype, row r of head h at
  * K + (h * k_head_stride + r) * d. Device memory, or pinned host memory (read
- * through its device mapping); any other pointer is CKV_ERR_INVALID_ARG. */
+ * through its device mapping; its clustered rows are first copied to the
+ * workspace, which is sized for that copy whatever K is); any other pointer
+ * is CKV_ERR_INVALID_ARG. */
 int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
                 int32_t *assign, int32_t *csr_offsets, int32_t *csr_tokens,
                 void *workspace, size_t workspace_bytes, void *stream);

@@ -132,8 +132,10 @@ def assign(K, n_sink, mu, mode=MIRROR, metric=COSINE):
     """Assignment step [ClusterKV, clustering in semantic space]: cosine by
     default; INNER_PRODUCT and L2 are the page's ablation. K: [L][d],
     mu: [C][d]. Returns (assign [L] int32, margin [L]); the margin is the
-    gap between the best and second-best candidate (squared-distance gap
-    for L2)."""
+    gap between the best and second-best candidate: in cosine units for the
+    cosine (MIRROR scores the key as stored against the rounded unit
+    centroid and divides the gap by |k|), the score gap for the inner
+    product, the squared-distance gap for L2."""
     K, pk = _d(K)
     mu, pm = _d(mu)
     L, d = K.shape

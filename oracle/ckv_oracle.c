@@ -20,11 +20,12 @@
  * Arithmetic is fp64 throughout. Two modes:
  *   ORC_EXACT  -- no intermediate rounding beyond fp64: cosine scores from
  *                 fp64 unit vectors, centroids kept in fp64.
- *   ORC_MIRROR -- identical steps, but the operands of the cosine scores are
- *                 rounded the way the GPU stores them (fp64 -> fp32 -> bf16,
- *                 nearest-even each time) and centroids are stored as fp32.
+ *   ORC_MIRROR -- identical steps, but the operands of the scores are the
+ *                 ones the GPU stores: the key as stored (bf16), and for
+ *                 the cosine the unit centroid rounded fp64 -> fp32 -> bf16
+ *                 (nearest-even each time); centroids are stored as fp32.
  *                 The scores themselves are still fp64 dot products of those
- *                 rounded operands.
+ *                 operands.
  *
  * Readings taken where the page is silent (each one is listed with its
  * reason in the design notes of the repository):
@@ -157,9 +158,15 @@ static double orc_dist2(const double *a, const double *b, int d)
  *   ORC_L2           : the centroid of smallest sum_j (k_j - mu_j)^2.
  * Ties go to the lower cluster id. Writes assign[0..L) (-1 for sinks) and,
  * if margin is not NULL, margin[i] = the gap between the best and the
- * second-best candidate (score gap for cosine and inner product, squared
- * distance gap for L2; +inf when C == 1, and for sinks). K is one head
- * [L][d]; mu is [C][d]. */
+ * second-best candidate (cosine gap for the cosine, score gap for the inner
+ * product, squared distance gap for L2; +inf when C == 1, and for sinks).
+ * K is one head [L][d]; mu is [C][d].
+ * Cosine: EXACT compares the cosines themselves, dot products of the two
+ * fp64 unit vectors. cos(k, mu) = <k, mu/|mu|> / |k|, and |k| > 0 is the
+ * same for every centroid, so the largest cosine is also the largest
+ * <k, mu/|mu|>: MIRROR compares those, with the key as stored and the
+ * rounded unit centroid, and divides the gap by |k| to give it in cosine
+ * units (a zero key has gap 0: all its scores are 0). */
 void orc_assign_metric(int64_t L, int d, const double *K, int n_sink, int C,
                        const double *mu, int metric, int mode, int32_t *assign,
                        double *margin)
@@ -178,7 +185,7 @@ void orc_assign_metric(int64_t L, int d, const double *K, int n_sink, int C,
             if (margin) margin[i] = INFINITY;
             continue;
         }
-        if (metric == ORC_COSINE)
+        if (metric == ORC_COSINE && mode == ORC_EXACT)
             orc_unit(K + i * d, d, mode, kt);
         else
             orc_store(K + i * d, d, mode, kt);
@@ -197,7 +204,14 @@ void orc_assign_metric(int64_t L, int d, const double *K, int n_sink, int C,
             }
         }
         assign[i] = arg;
-        if (margin) margin[i] = (C == 1) ? INFINITY : best - second;
+        if (margin) {
+            double gap = best - second;
+            if (metric == ORC_COSINE && mode == ORC_MIRROR) {
+                double nk = sqrt(orc_sumsq(kt, d));
+                gap = nk > 0.0 ? gap / nk : 0.0;
+            }
+            margin[i] = (C == 1) ? INFINITY : gap;
+        }
     }
     free(kt);
     free(mt);

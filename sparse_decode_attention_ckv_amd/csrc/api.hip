@@ -79,6 +79,8 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     p->token_base = d->token_base;
     p->t_base = d->t_base;
     p->t_cap = d->t_cap;
+    p->ka = nullptr;          // set by ckv_cluster once K is resolved
+    p->ka_stride = 0;
     p->csr_wide = d->C <= kCsrWideMaxC;
     const int tile = p->csr_wide ? kCsrWideTile : kCsrTile;
     p->ntiles = (p->Lp + tile - 1) / tile;
@@ -298,16 +300,29 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
     // K as the kernels read it: device memory, or pinned host memory through
     // its device mapping; pageable host memory and unknown pointers are refused
     const void *Kv;
-    if (device_view(K, &Kv) != CKV_OK || !aligned16(Kv)) return CKV_ERR_INVALID_ARG;
+    bool k_host = false;
+    if (device_view(K, &Kv, &k_host) != CKV_OK || !aligned16(Kv)) return CKV_ERR_INVALID_ARG;
     K = Kv;
     p.n_cu = device_cu_count();
     hipStream_t s = (hipStream_t)stream;
+    // the assignment reads device keys where they are; host keys are copied
+    // to the workspace once, so the iterations do not cross the host link
+    const size_t es = p.dtype == CKV_BF16 ? 2 : 4;
+    hipError_t e = hipSuccess;
+    if (k_host) {
+        p.ka = p.kt;
+        p.ka_stride = p.Lp * kD;
+        e = launch_copy_keys(p, K, s);
+        if (e != hipSuccess) return launch_status(e);
+    } else {
+        p.ka = (const char *)K + (size_t)p.n_sink * kD * es;
+        p.ka_stride = p.k_head_stride;
+    }
 
     if (p.dtype == CKV_BF16 && p.Lp <= kSmallRows && p.C <= kSmallC)
         return launch_status(launch_cluster_small(p, K, centroids, assign, csr_offsets,
                                                   csr_tokens, s));
-    hipError_t e = launch_normalize_keys(p, K, assign, s);
-    if (e == hipSuccess) e = launch_init_centroids(p, K, centroids, s);
+    e = launch_init_centroids(p, K, centroids, assign, s);
     for (int t = 0; t < p.iters && e == hipSuccess; ++t) {
         e = launch_assign(p, assign, s);
         if (e == hipSuccess) e = launch_csr(p, assign, csr_offsets, csr_tokens, s);

@@ -7,11 +7,12 @@
 // label-sorted token indices kept as metadata).
 //
 // One call runs, per independent KV head:
-//   normalize_keys            unit keys, once (raw copy for the
-//                             inner-product and L2 ablation)  (HBM-bound)
+//   copy_keys                 only for keys in pinned host memory: one copy
+//                             to device memory               (HBM-bound)
 //   init_centroids            mu_c = k_{n_sink + s*c}
 //   iters x {
-//     assign                  cosine GEMM on bf16 MFMA + fused row argmax
+//     assign                  cosine GEMM on bf16 MFMA (keys as stored,
+//                             unit centroids) + fused row argmax
 //     csr count/scan/scatter  atomic-free stable counting sort -> CSR
 //     update                  per-cluster fp64 segmented sum of raw keys,
 //                             mean -> fp32 centroid, unit centroid for the
@@ -80,196 +81,60 @@ __device__ void block_store_row(float x, int j, void *out_row, float *sx, float 
 }
 
 // --------------------------------------------------------------------------
-// normalize_keys: the fp64 norm is a sequential chain, so one thread owns a
-// row; the rows of a 256-row block are moved through LDS so that global
-// loads and stores stay coalesced (consecutive lanes, consecutive 16-byte
-// chunks). LDS rows are padded to 272 B to spread a column over the banks.
-constexpr int kNkRows = 256;             // rows per workgroup (one per thread)
-constexpr int kNkStride = 17;            // LDS row stride in 16-byte chunks
+// copy_keys: rows n_sink .. L-1 of every head copied into the workspace
+// [H][Lp][d], for keys in pinned host memory only (device keys are read where
+// they are). The assignment then reads them from device memory in every
+// iteration instead of over the host link. Plain 16-byte chunks, four per
+// thread in flight.
+constexpr int kCkThreads = 256, kCkPer = 4;
 
-// One LDS row (16 chunks of 8 bf16): the chain over it (chunks in order),
-// |x| its fp64 square root, then the unit row bf16(fp32(x_j / |x|)) written
-// back in place.
-__device__ __forceinline__ void nk_unit_row(u32x4 *row) {
-    double ss = 0.0;
-#pragma unroll 2
-    for (int i = 0; i < 16; ++i) {
-        float f[8];
-        unpack8(row[i], f);
+__global__ __launch_bounds__(kCkThreads) void k_copy_keys(const u32x4 *__restrict__ K,
+                                                          int64_t head_stride16,
+                                                          int64_t row0_16, int64_t n16,
+                                                          u32x4 *__restrict__ kt) {
+    const int h = blockIdx.y;
+    const int64_t e0 = (int64_t)blockIdx.x * (kCkThreads * kCkPer) + threadIdx.x;
+    const u32x4 *src = K + h * head_stride16 + row0_16;
+    u32x4 *dst = kt + h * n16;
+    u32x4 v[kCkPer];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = __fma_rn((double)f[e], (double)f[e], ss);
+    for (int k = 0; k < kCkPer; ++k) {
+        const int64_t e = e0 + kCkThreads * k;
+        v[k] = src[e < n16 ? e : 0];
     }
-    const double n = sqrt(ss);
-    const bool nz = ss > 0.0;
-    const double r = nz ? 1.0 / n : 0.0;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-        float f[8];
-        unpack8(row[i], f);
-        // x * (1/|x|) is within two fp64 ulps of the quotient x / |x|, so it
-        // rounds to the same fp32 value unless it lies within a few ulps of
-        // a point halfway between two fp32 values (its 29 bits below fp32
-        // precision near 2^28) or in fp32's subnormal range; only then is
-        // the division carried out.
-        double qv[8];
-        bool amb = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            qv[e] = (double)f[e] * r;
-            const uint64_t u = (uint64_t)__double_as_longlong(qv[e]);
-            const uint32_t lo = (uint32_t)u & 0x1FFFFFFFu;
-            const uint32_t ex = (uint32_t)(u >> 52) & 0x7FFu;   // biased exponent
-            // bitwise, not short-circuit: no branch per element (a zero
-            // also takes the division, which gives it exactly)
-            amb = amb | ((lo - (0x10000000u - 4u)) <= 8u) | (ex < 1023u - 125u);
-        }
-        if (amb) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] = (double)f[e] / n;
-        }
-        uint32_t o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = nz ? f32_to_bf16_rne((float)qv[e]) : 0u;
-        u32x4 v;
-        v.x = o[0] | (o[1] << 16);
-        v.y = o[2] | (o[3] << 16);
-        v.z = o[4] | (o[5] << 16);
-        v.w = o[6] | (o[7] << 16);
-        row[i] = v;
+    for (int k = 0; k < kCkPer; ++k) {
+        const int64_t e = e0 + kCkThreads * k;
+        if (e < n16) dst[e] = v[k];
     }
 }
 
-// UNIT = false copies the rows unchanged (inner-product and L2 assignment).
-template <bool UNIT>
-__global__ __launch_bounds__(kNkRows) void k_normalize_keys_bf16(
-    const uint16_t *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
-    uint16_t *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
-    __shared__ u32x4 rows[kNkRows * kNkStride];
-    __shared__ int32_t stok[kSmallRows];
-    __shared__ int32_t soff[kSmallC + 1];
-    const int h = blockIdx.y, tid = threadIdx.x;
-    if (blockIdx.x == 0)   // sink rows are labelled -1
-        for (int i = tid; i < n_sink; i += kNkRows) assign[(int64_t)h * L + i] = -1;
-    const int64_t r0 = (int64_t)blockIdx.x * kNkRows;
-    const int nrow = (int)(Lp - r0 < kNkRows ? Lp - r0 : kNkRows);
-    const u32x4 *src = (const u32x4 *)(K + h * head_stride + (n_sink + r0) * kD);
-    u32x4 *dst = (u32x4 *)(kt + ((int64_t)h * Lp + r0) * kD);
-    // coalesced loads: chunk e = 16 row + q
-#pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 8) {
-        u32x4 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = tid + kNkRows * (k0 + k);
-            v[k] = src[(e >> 4) < nrow ? e : 0];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = tid + kNkRows * (k0 + k);
-            rows[(e >> 4) * kNkStride + (e & 15)] = v[k];
-        }
-    }
-    __syncthreads();
-    if (UNIT) {
-        nk_unit_row(rows + tid * kNkStride);
-        __syncthreads();
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int e = tid + kNkRows * k;
-        if ((e >> 4) < nrow) dst[e] = rows[(e >> 4) * kNkStride + (e & 15)];
-    }
-}
-
-// fp32 keys: the same scheme with 64-row blocks (512 B rows, padded to 528 B
-// in LDS) and the quotients kept in fp32: one thread per row runs the fp64
-// chain of |x|^2 over j = 0..127 in order, then x_j / |x| in fp64, rounded
-// once to fp32.
-constexpr int kNfRows = 64;              // rows per workgroup (one per thread)
-constexpr int kNfStride = 33;            // LDS row stride in 16-byte chunks
-
-template <bool UNIT>
-__global__ __launch_bounds__(kNfRows) void k_normalize_keys_f32(
-    const float *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp,
-    float *__restrict__ kt, int32_t *__restrict__ assign, int64_t L) {
-    __shared__ float4 rows[kNfRows * kNfStride];
-    const int h = blockIdx.y, tid = threadIdx.x;
-    if (blockIdx.x == 0)   // sink rows are labelled -1
-        for (int i = tid; i < n_sink; i += kNfRows) assign[(int64_t)h * L + i] = -1;
-    const int64_t r0 = (int64_t)blockIdx.x * kNfRows;
-    const int nrow = (int)(Lp - r0 < kNfRows ? Lp - r0 : kNfRows);
-    const float4 *src = (const float4 *)(K + h * head_stride + (n_sink + r0) * kD);
-    float4 *dst = (float4 *)(kt + ((int64_t)h * Lp + r0) * kD);
-    // coalesced loads: chunk e = 32 row + q, 8 in flight at a time
-#pragma unroll
-    for (int k0 = 0; k0 < 32; k0 += 8) {
-        float4 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = tid + kNfRows * (k0 + k);
-            v[k] = src[(e >> 5) < nrow ? e : 0];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = tid + kNfRows * (k0 + k);
-            rows[(e >> 5) * kNfStride + (e & 31)] = v[k];
-        }
-    }
-    __syncthreads();
-    if (UNIT && tid < nrow) {
-        float4 *row = rows + tid * kNfStride;
-        double ss = 0.0;
-        for (int q = 0; q < 32; ++q) {
-            const float4 v = row[q];
-            ss = __fma_rn((double)v.x, (double)v.x, ss);
-            ss = __fma_rn((double)v.y, (double)v.y, ss);
-            ss = __fma_rn((double)v.z, (double)v.z, ss);
-            ss = __fma_rn((double)v.w, (double)v.w, ss);
-        }
-        const double n = sqrt(ss);
-        const bool nz = ss > 0.0;
-        for (int q = 0; q < 32; ++q) {
-            const float4 v = row[q];
-            row[q] = nz ? make_float4((float)((double)v.x / n), (float)((double)v.y / n),
-                                      (float)((double)v.z / n), (float)((double)v.w / n))
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-        const int e = tid + kNfRows * k;
-        if ((e >> 5) < nrow) dst[e] = rows[(e >> 5) * kNfStride + (e & 31)];
-    }
-}
-
-hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *assign,
-                                 hipStream_t s) {
-    const bool unit = p.metric == kCosine;
-    if (p.dtype == 1)
-        hipLaunchKernelGGL(unit ? k_normalize_keys_bf16<true> : k_normalize_keys_bf16<false>,
-                           dim3((unsigned)((p.Lp + kNkRows - 1) / kNkRows), p.H),
-                           dim3(kNkRows), 0, s, (const uint16_t *)K, p.k_head_stride,
-                           p.n_sink, p.Lp, (uint16_t *)p.kt, assign, p.L);
-    else
-        hipLaunchKernelGGL(unit ? k_normalize_keys_f32<true> : k_normalize_keys_f32<false>,
-                           dim3((unsigned)((p.Lp + kNfRows - 1) / kNfRows), p.H),
-                           dim3(kNfRows), 0, s, (const float *)K, p.k_head_stride, p.n_sink,
-                           p.Lp, (float *)p.kt, assign, p.L);
+hipError_t launch_copy_keys(const ClusterPlan &p, const void *K, hipStream_t s) {
+    const int64_t es = p.dtype == 1 ? 2 : 4;           // bytes per element
+    const int64_t per_row = kD * es / 16;               // 16-byte chunks per row
+    const int64_t n16 = p.Lp * per_row;
+    const int64_t blk = kCkThreads * kCkPer;
+    hipLaunchKernelGGL(k_copy_keys, dim3((unsigned)((n16 + blk - 1) / blk), p.H),
+                       dim3(kCkThreads), 0, s, (const u32x4 *)K,
+                       p.k_head_stride * es / 16, (int64_t)p.n_sink * per_row, n16,
+                       (u32x4 *)p.kt);
     return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
 // init_centroids: mu_c = raw key at window row n_sink + s*c, s = floor(Lp/C)
 // (the page samples keys as initial centroids; evenly spaced tokens here).
+// The first workgroup of a head also labels its sink rows -1.
 template <bool BF16, int M>
 __global__ __launch_bounds__(128) void k_init_centroids(
     const void *__restrict__ K, int64_t head_stride, int n_sink, int64_t Lp, int C,
     float *__restrict__ cent, int c_base, int c_cap, void *__restrict__ mt,
-    float *__restrict__ mb, int Cpad) {
+    float *__restrict__ mb, int Cpad, int32_t *__restrict__ assign, int64_t L) {
     __shared__ float sx[kD];
     __shared__ double snrm;
     const int c = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
+    if (c == 0)
+        for (int i = j; i < n_sink; i += 128) assign[(int64_t)h * L + i] = -1;
     const int64_t row = n_sink + (Lp / C) * (int64_t)c;
     const int64_t e = h * head_stride + row * kD + j;
     const float x = BF16 ? bf16_to_f32(((const uint16_t *)K)[e]) : ((const float *)K)[e];
@@ -283,32 +148,37 @@ __global__ __launch_bounds__(128) void k_init_centroids(
 }
 
 template <int M>
-static void launch_init_m(const ClusterPlan &p, const void *K, float *cent, hipStream_t s) {
+static void launch_init_m(const ClusterPlan &p, const void *K, float *cent, int32_t *assign,
+                          hipStream_t s) {
     dim3 grid(p.C, p.H);
     if (p.dtype == 1)
         hipLaunchKernelGGL((k_init_centroids<true, M>), grid, dim3(128), 0, s, K,
                            p.k_head_stride, p.n_sink, p.Lp, p.C, cent, p.c_base,
-                           p.c_cap, p.mt, p.mb, p.Cpad);
+                           p.c_cap, p.mt, p.mb, p.Cpad, assign, p.L);
     else
         hipLaunchKernelGGL((k_init_centroids<false, M>), grid, dim3(128), 0, s, K,
                            p.k_head_stride, p.n_sink, p.Lp, p.C, cent, p.c_base,
-                           p.c_cap, p.mt, p.mb, p.Cpad);
+                           p.c_cap, p.mt, p.mb, p.Cpad, assign, p.L);
 }
 
 hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cent,
-                                 hipStream_t s) {
+                                 int32_t *assign, hipStream_t s) {
     if (p.metric == kCosine)
-        launch_init_m<kCosine>(p, K, cent, s);
+        launch_init_m<kCosine>(p, K, cent, assign, s);
     else if (p.metric == kInnerProduct)
-        launch_init_m<kInnerProduct>(p, K, cent, s);
+        launch_init_m<kInnerProduct>(p, K, cent, assign, s);
     else
-        launch_init_m<kL2>(p, K, cent, s);
+        launch_init_m<kL2>(p, K, cent, assign, s);
     return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
-// assign (bf16): scores = Kt . Mt^T on v_mfma_f32_16x16x32_bf16 with fp32
+// assign (bf16): scores = K . Mt^T on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation, fused with a per-token argmax (ties -> lower cluster id).
+// For the cosine, Mt holds the unit centroids and K the keys as stored: a
+// key's cosine with mu is <k, mu/|mu|> / |k|, and the positive factor 1/|k|
+// is common to all its scores, so the largest <k, mu/|mu|> is the largest
+// cosine and the keys are never normalised.
 //
 // Persistent workgroups of 8 waves (two per SIMD, 256 registers each), one
 // per CU, each walking a contiguous range of 512-token tiles (head-major, so
@@ -333,15 +203,18 @@ hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cen
 // (l & 15) and rows 4*(l >> 4) + i, i = 0..3.
 //
 // The argmax is exact up to the fp32 accumulation of the scores:
-//  * cosine: the accumulation starts from 2.0, so every score 2 + s lies in
-//    [0.99, 3.01] and orders like its bit pattern. Within a group of
+//  * cosine: a token's accumulations start from beta = 2 |k| (its squared
+//    norm summed from its own B fragments), so every score beta + s lies in
+//    [0.99, 3.01] |k| and orders like its bit pattern. Within a group of
 //    kAsGroup consecutive M tiles a lane's candidates carry a 5-bit key in
 //    their low bits (larger for the lower id) and are reduced with float max;
 //    the group's winner then replaces the running best only if its score with
 //    the key bits cleared is strictly larger, and lanes merge on (truncated
-//    score, id). Every decision therefore compares 2 + s truncated to 2^-17
-//    of its magnitude (7.6e-6 absolute at most) and resolves equal truncated
-//    scores -- exact ties included -- to the lower id.
+//    score, id). Every decision therefore compares beta + s truncated to
+//    2^-18 of its magnitude (1.2e-5 |k| at most, so 1.2e-5 in cosine units)
+//    and resolves equal truncated scores -- exact ties included -- to the
+//    lower id. A key whose squared norm is below 2^-100 takes beta = 2^-49:
+//    a zero key then ties everywhere and joins cluster 0.
 //  * inner product and L2: a plain compare-and-select per score (strict >
 //    in ascending id order), then the same lane merge on (score, id).
 constexpr int kAsWaves = 8;
@@ -352,8 +225,8 @@ constexpr int kAsGroup = 8;             // M tiles per packed-argmax group
 constexpr uint32_t kAsKey = 4 * kAsGroup - 1;   // key bits of a group (5)
 static_assert(kAsRound % (16 * kAsGroup) == 0, "groups never straddle a round");
 
-// B fragments of the wave's 64 tokens from row tok0 (rows past the window
-// read the last row; their results are not stored).
+// B fragments of the wave's 64 tokens from row tok0 of a head's rows K4
+// (rows past the window read the last row; their results are not stored).
 __device__ __forceinline__ void as_load_b(const u32x4 *K4, int64_t Lp, int64_t tok0, int col,
                                           int kq, bf16x8 (&b)[4][4]) {
 #pragma unroll
@@ -373,16 +246,48 @@ __device__ __forceinline__ void as_lds_a(const u32x4 *sA, int m, int col, int kq
     for (int s = 0; s < 4; ++s) a[s] = __builtin_bit_cast(bf16x8, sA[r * 16 + ((4 * s + kq) ^ col)]);
 }
 
+// Cosine offsets of the wave's tokens: beta[t] = 2 |k| for the token in
+// column (l & 15) of N tile t. Each lane sums the squares of its 32 elements
+// of the row (bf16 pairs on v_dot2), then the four lanes holding the row add
+// their sums in a butterfly, so all four get the same value. Deterministic,
+// so every path that clusters the same rows starts from the same offsets.
+__device__ __forceinline__ float as_sq2(uint32_t u, float acc) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    bf16x2 v;
+    __builtin_memcpy(&v, &u, 4);
+    return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
+__device__ __forceinline__ void as_beta(const bf16x8 (&b)[4][4], float (&beta)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float n2 = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const u32x4 w = __builtin_bit_cast(u32x4, b[t][s]);
+            n2 = as_sq2(w.x, n2);
+            n2 = as_sq2(w.y, n2);
+            n2 = as_sq2(w.z, n2);
+            n2 = as_sq2(w.w, n2);
+        }
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        // a normal argument: the hardware square root needs no rescaling
+        beta[t] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(n2, 0x1p-100f));
+    }
+}
+
 // The 16 MFMAs of one M tile against the wave's four N tiles, k steps in
-// order for every N tile; the cosine's accumulation starts from 2.0.
+// order for every N tile; the cosine's accumulation starts from beta.
 template <bool COS>
 __device__ __forceinline__ void as_mfma(const bf16x8 (&a)[4], const bf16x8 (&b)[4][4],
-                                        f32x4 (&acc)[4]) {
-    const float c0 = COS ? 2.f : 0.f;
+                                        const float (&beta)[4], f32x4 (&acc)[4]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+        const float c0 = COS ? beta[t] : 0.f;
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[t][0], (f32x4){c0, c0, c0, c0},
                                                          0, 0, 0);
+    }
 #pragma unroll
     for (int s = 1; s < 4; ++s)
 #pragma unroll
@@ -392,32 +297,26 @@ __device__ __forceinline__ void as_mfma(const bf16x8 (&a)[4], const bf16x8 (&b)[
 
 // Cosine, one M tile at position mm of its group: the lane's rows c0 .. c0+3
 // get keys kAsKey - (4 mm + i) in their low bits and join the group maxima
-// gb[t]; MASK drops ids >= C (0 never wins against 2 + s).
-// vmask is ~kAsKey held in a vector register: with the key (uniform, a
-// scalar register) the insert is one v_and_or_b32, which may read only one
-// scalar operand.
+// gb[t]; MASK drops ids >= C (0 never wins against beta + s > 0).
+// The insert (x & ~kAsKey) | key is one v_bitop3_b32 with kAsKey as an
+// inline constant and the key (uniform) in a scalar register: truth table
+// 0xBA, bit 4 a + 2 b + c of it being (a & ~b) | c for operand bits a, b, c.
 template <bool MASK>
 __device__ __forceinline__ void as_cos_tile(const f32x4 (&acc)[4], int mm, int c0, int C,
-                                            uint32_t vmask, float (&gb)[4]) {
+                                            float (&gb)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t key = kAsKey - (uint32_t)(4 * mm + i);
-            p[i] = __uint_as_float((__float_as_uint(acc[t][i]) & vmask) | key);
+            p[i] = __uint_as_float(
+                __builtin_amdgcn_bitop3_b32(__float_as_uint(acc[t][i]), kAsKey, key, 0xBA));
             if (MASK && c0 + i >= C) p[i] = 0.f;
         }
         gb[t] = fmaxf(fmaxf(gb[t], p[0]), p[1]);
         gb[t] = fmaxf(fmaxf(gb[t], p[2]), p[3]);
     }
-}
-
-// ~kAsKey in a vector register (opaque to the compiler, so it stays there).
-__device__ __forceinline__ uint32_t as_vmask() {
-    uint32_t v;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(~kAsKey));
-    return v;
 }
 
 // Cosine, end of group g: its winner replaces the running best (bv: the
@@ -503,9 +402,10 @@ __device__ __forceinline__ void as_fill(u32x4 *sA, float *sB, const u32x4 *M4,
     __syncthreads();
 }
 
+// ka: the first clustered row of head 0, heads ka_stride elements apart.
 template <int M>
 __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
-    const uint16_t *__restrict__ kt, const uint16_t *__restrict__ mt,
+    const uint16_t *__restrict__ ka, int64_t ka_stride, const uint16_t *__restrict__ mt,
     const float *__restrict__ mb, int64_t Lp, int C, int Cpad, int32_t *__restrict__ assign,
     int64_t L, int n_sink, int tiles_per_head, int n_tiles) {
     constexpr bool COS = M == kCosine, BIAS = M == kL2;
@@ -519,7 +419,6 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
     const int col = lane & 15, kq = lane >> 4;
     const int crows = (C + 31) / 32 * 32;                 // even number of M tiles, <= Cpad
     const int nr = (crows + kAsRound - 1) / kAsRound;     // rounds per tile
-    const uint32_t vmask = as_vmask();
     int h = t_begin / tiles_per_head;
     int tile = t_begin - h * tiles_per_head;
     // A single round stays resident while the head does not change: fill it
@@ -534,10 +433,12 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
         loaded = h;
     }
     bf16x8 b[4][4], bn[4][4];
-    as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, (int64_t)tile * kAsTok + wave * 64,
+    as_load_b((const u32x4 *)(ka + (int64_t)h * ka_stride), Lp, (int64_t)tile * kAsTok + wave * 64,
               col, kq, b);
     for (int t = t_begin; t < t_end; ++t) {
         const int64_t tok0 = (int64_t)tile * kAsTok + wave * 64;
+        float beta[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (COS) as_beta(b, beta);
         const u32x4 *M4 = (const u32x4 *)(mt + (int64_t)h * Cpad * kD);
         // the next tile (the last one requests its own rows again: harmless)
         int hn = h, tilen = tile + 1;
@@ -575,7 +476,7 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
         // next tile's rows are requested only once this tile is done)
         auto prefetch = [&]() {
             if constexpr (!BIAS)
-                as_load_b((const u32x4 *)(kt + (int64_t)hp * Lp * kD), Lp,
+                as_load_b((const u32x4 *)(ka + (int64_t)hp * ka_stride), Lp,
                           (int64_t)tp * kAsTok + wave * 64, col, kq, bn);
         };
         auto run = [&](int r) {
@@ -591,7 +492,7 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
                 constexpr bool MK = decltype(mask)::value;
                 const int mg = mg0 + m;
                 if (COS)
-                    as_cos_tile<MK>(acc, mg % kAsGroup, 16 * mg + 4 * kq, C, vmask, gb);
+                    as_cos_tile<MK>(acc, mg % kAsGroup, 16 * mg + 4 * kq, C, gb);
                 else
                     as_exact_tile<MK, BIAS>(acc, sB, m, kq, 16 * mg + 4 * kq, C, bv, bc);
             };
@@ -599,21 +500,21 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
             using Mask = std::integral_constant<bool, true>;
             as_lds_a(sA, 0, col, kq, aE);
             as_lds_a(sA, 1, col, kq, aO);
-            as_mfma<COS>(aE, b, cE);                      // tile 0
+            as_mfma<COS>(aE, b, beta, cE);                // tile 0
             int m = 1;
             for (; m + 1 < nm; m += 2) {
                 if (r == 0 && m == m_pf) prefetch();
                 as_lds_a(sA, m + 1, col, kq, aE);
-                as_mfma<COS>(aO, b, cO);                  // tile m
+                as_mfma<COS>(aO, b, beta, cO);            // tile m
                 amax(cE, m - 1, NoMask{});
                 as_lds_a(sA, m + 2, col, kq, aO);
-                as_mfma<COS>(aE, b, cE);                  // tile m + 1
+                as_mfma<COS>(aE, b, beta, cE);            // tile m + 1
                 amax(cO, m, NoMask{});
                 if (COS && (mg0 + m) % kAsGroup == kAsGroup - 1)
                     as_cos_close(gb, (mg0 + m) / kAsGroup, bv, bk);
             }
             if (r == 0 && m_pf + 1 >= nm) prefetch();
-            as_mfma<COS>(aO, b, cO);                      // tile nm - 1
+            as_mfma<COS>(aO, b, beta, cO);                // tile nm - 1
             amax(cE, nm - 2, Mask{});
             amax(cO, nm - 1, Mask{});
             if (COS) as_cos_close(gb, (mg0 + nm - 1) / kAsGroup, bv, bk);
@@ -630,7 +531,7 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
         // the next tile's fragments become current (this waits for them),
         // then the labels are stored
         if constexpr (BIAS) {
-            as_load_b((const u32x4 *)(kt + (int64_t)hp * Lp * kD), Lp,
+            as_load_b((const u32x4 *)(ka + (int64_t)hp * ka_stride), Lp,
                       (int64_t)tp * kAsTok + wave * 64, col, kq, b);
         } else {
 #pragma unroll
@@ -649,8 +550,9 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
 // assign (fp32): a workgroup takes 64 tokens; wave g scores them against the
 // clusters c = g, g + 8, g + 16, ... (one token per lane, the cluster rows
 // uniform across the wave, so they come through the scalar cache), each
-// score the fp32 dot product over j = 0..127 in order of the rows in kt and
-// mt (unit rows for the cosine), plus the cluster's bias when mb is given
+// score the fp32 dot product over j = 0..127 in order of the key as stored
+// and the row in mt (the unit centroid for the cosine, whose argmax needs no
+// unit key, as in the bf16 kernel), plus the cluster's bias when mb is given
 // (L2). Each wave keeps the strictly larger score in ascending id order;
 // the eight candidates of a token then merge on (score, lower id), which is
 // the argmax with ties to the lower id over all clusters (cluster 0 when no
@@ -658,8 +560,9 @@ __global__ __launch_bounds__(kAsThreads) void k_assign_bf16(
 constexpr int kAfTok = 64, kAfGroups = 8;
 
 __global__ __launch_bounds__(64 * kAfGroups) void k_assign_f32(
-    const float *__restrict__ kt, const float *__restrict__ mt, const float *__restrict__ mb,
-    int64_t Lp, int C, int Cpad, int32_t *__restrict__ assign, int64_t L, int n_sink) {
+    const float *__restrict__ ka, int64_t ka_stride, const float *__restrict__ mt,
+    const float *__restrict__ mb, int64_t Lp, int C, int Cpad, int32_t *__restrict__ assign,
+    int64_t L, int n_sink) {
     __shared__ float sbest[kAfGroups][kAfTok];
     __shared__ int sarg[kAfGroups][kAfTok];
     const int h = blockIdx.y;
@@ -668,7 +571,7 @@ __global__ __launch_bounds__(64 * kAfGroups) void k_assign_f32(
     const int64_t i = (int64_t)blockIdx.x * kAfTok + lane;
     const int64_t ii = i < Lp ? i : Lp - 1;
     float k[kD];
-    const float *src = kt + ((int64_t)h * Lp + ii) * kD;
+    const float *src = ka + (int64_t)h * ka_stride + ii * kD;
 #pragma unroll
     for (int j = 0; j < kD; j += 4) {
         const float4 v = *(const float4 *)(src + j);
@@ -730,13 +633,15 @@ hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s) {
                   : p.metric == kL2     ? k_assign_bf16<kL2>
                                         : k_assign_bf16<kInnerProduct>;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kAsThreads), 0, s,
-                           (const uint16_t *)p.kt, (const uint16_t *)p.mt, (const float *)p.mb,
-                           p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink, tph, n_tiles);
+                           (const uint16_t *)p.ka, p.ka_stride, (const uint16_t *)p.mt,
+                           (const float *)p.mb, p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink, tph,
+                           n_tiles);
     } else {
         dim3 grid((unsigned)((p.Lp + kAfTok - 1) / kAfTok), p.H);
-        hipLaunchKernelGGL(k_assign_f32, grid, dim3(64 * kAfGroups), 0, s, (const float *)p.kt,
-                           (const float *)p.mt, p.metric == kL2 ? (const float *)p.mb : nullptr,
-                           p.Lp, p.C, p.Cpad, assign, p.L, p.n_sink);
+        hipLaunchKernelGGL(k_assign_f32, grid, dim3(64 * kAfGroups), 0, s, (const float *)p.ka,
+                           p.ka_stride, (const float *)p.mt,
+                           p.metric == kL2 ? (const float *)p.mb : nullptr, p.Lp, p.C, p.Cpad,
+                           assign, p.L, p.n_sink);
     }
     return hipGetLastError();
 }
@@ -1282,13 +1187,13 @@ hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *off
 // workgroup barriers where the general path has kernel boundaries. Every
 // step is the general path's device code with the same thread-to-data
 // mapping, so the results are bitwise those of the general path:
-//  * unit (or raw) rows: nk_unit_row on rows staged through LDS, 256 at a time;
+//  * the assignment reads the keys where the general one does (ka);
 //  * initial centroids: the chain of block_unit_row / block_store_row, eight
 //    128-thread groups at a time; centroids stay in LDS and the rows the
 //    assignment reads go straight into its LDS tile;
 //  * assignment: wave w takes tokens 64 w .. 64 w + 63 against the one
-//    16-cluster M tile (as_load_b, as_mfma and the general kernel's argmax:
-//    the same comparisons in the same order);
+//    16-cluster M tile (as_load_b, as_beta, as_mfma and the general kernel's
+//    argmax: the same comparisons in the same order);
 //  * CSR: the stable counting sort (ballot ranks inside a wave, wave counts,
 //    prefix over clusters), tokens in ascending order inside a cluster;
 //  * update: four 256-thread groups run k_update's two halves for clusters
@@ -1302,7 +1207,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
     const uint16_t *__restrict__ K, int64_t head_stride, int64_t L, int n_sink, int64_t Lp,
     int C, int iters, int64_t token_base, float *__restrict__ cent, int c_base, int c_cap,
     int32_t *__restrict__ assign, int32_t *__restrict__ offsets, int32_t *__restrict__ tokens,
-    int64_t t_base, int64_t t_cap, uint16_t *__restrict__ kt) {
+    int64_t t_base, int64_t t_cap, const uint16_t *__restrict__ ka, int64_t ka_stride) {
     constexpr bool BIAS = M == kL2;
     __shared__ u32x4 sA[16 * 16];
     __shared__ __align__(16) float sB[16];
@@ -1311,43 +1216,13 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
     __shared__ __align__(16) float sx[8][kD];
     __shared__ double snrm[8];
     __shared__ float scent[kSmallC][kD];
-    __shared__ u32x4 rows[kNkRows * kNkStride];
     __shared__ int32_t stok[kSmallRows];
     __shared__ int32_t soff[kSmallC + 1];
     const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int32_t *as = assign + (int64_t)h * L;
 
-    // unit (or raw) rows of the window, 256 rows at a time through LDS as in
-    // k_normalize_keys_bf16 (coalesced 16-byte chunks; thread r < 256 runs
-    // the chain of row r); sinks labelled -1
-    for (int i = tid; i < n_sink; i += kSmallThreads) as[i] = -1;
-    for (int64_t r0 = 0; r0 < Lp; r0 += kNkRows) {
-        const int nrow = (int)(Lp - r0 < kNkRows ? Lp - r0 : kNkRows);
-        const u32x4 *src = (const u32x4 *)(K + h * head_stride + (n_sink + r0) * kD);
-        u32x4 *dst = (u32x4 *)(kt + ((int64_t)h * Lp + r0) * kD);
-        constexpr int PER = kNkRows * 16 / kSmallThreads;        // chunks per thread
-        u32x4 v[PER];
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + kSmallThreads * k;
-            v[k] = src[(e >> 4) < nrow ? e : 0];
-        }
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + kSmallThreads * k;
-            rows[(e >> 4) * kNkStride + (e & 15)] = v[k];
-        }
-        __syncthreads();
-        if (M == kCosine && tid < kNkRows) nk_unit_row(rows + tid * kNkStride);
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + kSmallThreads * k;
-            if ((e >> 4) < nrow) dst[e] = rows[(e >> 4) * kNkStride + (e & 15)];
-        }
-        __syncthreads();
-    }
+    for (int i = tid; i < n_sink; i += kSmallThreads) as[i] = -1;   // sinks
     // initial centroids mu_c = row n_sink + s c, s = floor(Lp / C), eight at
     // a time (group g of 128 threads, channel j), as in k_init_centroids: the
     // centroid into LDS, the row the assignment reads into the LDS tile
@@ -1399,16 +1274,21 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
         // assignment: wave w's 64 tokens against the one M tile
         {
             bf16x8 b[4][4], afr[4];
-            as_load_b((const u32x4 *)(kt + (int64_t)h * Lp * kD), Lp, (int64_t)wave * 64, col,
-                      kq, b);
+            // the rows are read again in every iteration: kept in registers
+            // across the CSR and the update they would spill
+            const uint16_t *kh = ka + (int64_t)h * ka_stride;
+            asm volatile("" : "+s"(kh));
+            as_load_b((const u32x4 *)kh, Lp, (int64_t)wave * 64, col, kq, b);
+            float beta[4] = {0.f, 0.f, 0.f, 0.f};
+            if (M == kCosine) as_beta(b, beta);
             as_lds_a(sA, 0, col, kq, afr);
             f32x4 acc[4];
-            as_mfma<M == kCosine>(afr, b, acc);
+            as_mfma<M == kCosine>(afr, b, beta, acc);
             int res[4];
             if (M == kCosine) {
                 float gb[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
                 uint32_t bk[4] = {kAsKey, kAsKey, kAsKey, kAsKey};
-                as_cos_tile<true>(acc, 0, 4 * kq, C, as_vmask(), gb);
+                as_cos_tile<true>(acc, 0, 4 * kq, C, gb);
                 as_cos_close(gb, 0, bv, bk);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) res[u] = as_merge(bv[u], as_cos_id(bk[u], kq));
@@ -1484,22 +1364,22 @@ hipError_t launch_cluster_small(const ClusterPlan &p, const void *K, float *cent
                                 int32_t *assign, int32_t *offsets, int32_t *tokens,
                                 hipStream_t s) {
     const uint16_t *Kb = (const uint16_t *)K;
-    uint16_t *kt = (uint16_t *)p.kt;
+    const uint16_t *ka = (const uint16_t *)p.ka;
     if (p.metric == kCosine)
         hipLaunchKernelGGL(k_cluster_small<kCosine>, dim3(p.H), dim3(kSmallThreads), 0, s, Kb,
                            p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
                            cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           kt);
+                           ka, p.ka_stride);
     else if (p.metric == kInnerProduct)
         hipLaunchKernelGGL(k_cluster_small<kInnerProduct>, dim3(p.H), dim3(kSmallThreads), 0, s,
                            Kb, p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
                            cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           kt);
+                           ka, p.ka_stride);
     else
         hipLaunchKernelGGL(k_cluster_small<kL2>, dim3(p.H), dim3(kSmallThreads), 0, s, Kb,
                            p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
                            cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           kt);
+                           ka, p.ka_stride);
     return hipGetLastError();
 }
 

@@ -14,9 +14,12 @@ struct ClusterPlan {
     int64_t ntiles;           // CSR tiles per head
     bool csr_wide;            // C <= kCsrWideMaxC: the two-launch CSR over wide tiles
     int n_cu;                 // compute units of the device (persistent grids)
+    // the rows the assignment reads: the first clustered row of head 0 (the
+    // keys where they are, or their copy kt), heads ka_stride elements apart
+    const void *ka;
+    int64_t ka_stride;
     // workspace carve-up (device pointers)
-    void *kt;                 // keys as the assignment reads them [H][Lp][d]
-                              // (bf16 or f32; unit rows for the cosine)
+    void *kt;                 // copy of keys in pinned host memory [H][Lp][d]
     void *mt;                 // centroids as the assignment reads them [H][Cpad][d]
                               // (bf16 or f32; unit rows for the cosine)
     float *mb;                // per-cluster score bias [H][Cpad] (L2: -|mu|^2 / 2)
@@ -29,9 +32,9 @@ constexpr int kCsrTile = 512;          // tokens per CSR tile (one workgroup)
 constexpr int kCsrWideTile = 2048;     // tokens per tile of the two-launch CSR
 constexpr int kCsrWideMaxC = 512;      // clusters it handles (one per scatter thread)
 
-hipError_t launch_normalize_keys(const ClusterPlan &p, const void *K, int32_t *assign,
-                                 hipStream_t s);
-hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cent, hipStream_t s);
+hipError_t launch_copy_keys(const ClusterPlan &p, const void *K, hipStream_t s);
+hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cent,
+                                 int32_t *assign, hipStream_t s);
 hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s);
 hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offsets,
                       int32_t *tokens, hipStream_t s);

@@ -47,10 +47,11 @@ def gpu_cluster(K, n_sink, C, iters, **kw):
     return out
 
 
-# Label parity margin of the cosine assignment (scores in [-1, 1]): the
-# tolerance the assignment is held to. The bf16 kernel's own error is far
-# below it: fp32 accumulation of exact bf16 products, and an argmax that
-# compares 2 + s truncated to 2^-17 of its magnitude (7.6e-6 at most).
+# Label parity margin of the cosine assignment, in cosine units (the
+# oracle's cosine margins are): the tolerance the assignment is held to.
+# The bf16 kernel's own error is far below it: fp32 accumulation of exact
+# bf16 products, and an argmax that compares 2|k| + <k, mu~> truncated to
+# 2^-18 of its magnitude (1.2e-5 |k| at most, 1.2e-5 in cosine units).
 ASSIGN_MARGIN = 1e-4
 
 # the library's metric codes for the oracle's
@@ -59,8 +60,8 @@ CK_METRIC = {oracle.COSINE: ck.CKV_COSINE, oracle.INNER_PRODUCT: ck.CKV_INNER_PR
 
 
 def margin_threshold(metric, Kw, mu, labels, margin, mode):
-    """Per-token margin below which a label is not compared. Cosine scores
-    lie in [-1, 1]: the absolute `margin`. Inner-product and L2 scores are
+    """Per-token margin below which a label is not compared. Cosine margins
+    are in cosine units: the absolute `margin`. Inner-product and L2 scores are
     unbounded and compared exactly by the kernel, so the threshold is the
     worst-case fp32 accumulation error of two scores (the operands as the
     kernel reads them: mu rounded to bf16 under MIRROR): 128 products, each

@@ -76,12 +76,18 @@ def _keys(H, Lp, C, dtype, seed):
 
 def _scores(Kw, mu, metric, mode):
     """The scores the oracle compares (larger is better), from its operands:
-    unit rows for the cosine, else the rows rounded to bf16 under MIRROR.
-    L2 through the expansion |k|^2 - 2 k.m + |m|^2 (only gaps are used)."""
-    if metric == oracle.COSINE:
-        return oracle.unit_rows(Kw, mode=mode) @ oracle.unit_rows(mu, mode=mode).T
+    rows rounded to bf16 under MIRROR; for the cosine the unit centroids,
+    and the unit keys under EXACT, or under MIRROR the keys as stored with
+    each row divided by |k| (cosine units, as the oracle's margin). L2
+    through the expansion |k|^2 - 2 k.m + |m|^2 (only gaps are used)."""
     rnd = (lambda x: synth.bf16_to_f32(synth.bf16_bits(x)).astype(np.float64)) \
         if mode == oracle.MIRROR else (lambda x: x)
+    if metric == oracle.COSINE:
+        mt = oracle.unit_rows(mu, mode=mode)
+        if mode == oracle.EXACT:
+            return oracle.unit_rows(Kw, mode=mode) @ mt.T
+        k = rnd(Kw)
+        return (k @ mt.T) / np.linalg.norm(k, axis=1)[:, None]
     m, k = rnd(mu), rnd(Kw)
     if metric == oracle.INNER_PRODUCT:
         return k @ m.T

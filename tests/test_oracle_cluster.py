@@ -179,19 +179,45 @@ def test_mirror_operands_are_bf16_of_fp32_of_unit_vector():
 
 
 def test_mirror_operands_of_centroids_in_assignment():
-    """The assignment's margin is the fp64 dot product of the MIRROR operands:
-    with one key and two centroids it equals the difference of the two dot
-    products of the independently rounded unit rows."""
+    """The MIRROR cosine compares fp64 dot products of the key as stored
+    (bf16, rounded here by torch) with the independently rounded unit
+    centroids, and its margin is their gap divided by |k|. The label is the
+    EXACT cosine's wherever the cosines are not near a tie, and the margin
+    is within the rounding of the unit centroids of the exact cosine gap."""
     r = np.random.default_rng(11)
     for _ in range(20):
-        k = r.standard_normal((1, D)) * 5
+        k = r.standard_normal((1, D)) * 5 * 10.0 ** r.uniform(-2, 2)
         mu = r.standard_normal((2, D)) * 3
         a, m = oracle.assign(k, 0, mu, mode=oracle.MIRROR)
-        ku, _ = _bf16_of_fp32_of_quotient(k)
-        mt, _ = _bf16_of_fp32_of_quotient(mu)
-        s = np.array([np.dot(ku[0], mt[c]) for c in range(2)])
+        kb = torch.from_numpy(k).to(torch.bfloat16).double().numpy()
+        mt, mq = _bf16_of_fp32_of_quotient(mu)
+        s = np.array([np.dot(kb[0], mt[c]) for c in range(2)])
+        nk = np.sqrt(np.sum(kb[0] ** 2))
         assert a[0] == int(np.argmax(s))
-        assert abs(m[0] - abs(s[0] - s[1])) <= 1e-15
+        assert abs(m[0] - abs(s[0] - s[1]) / nk) <= 1e-15
+        # each rounded unit element is within 2^-8 (relative) of the exact
+        # one, so each cosine moves by at most 2^-8 |k||u| / |k| = 2^-8
+        cos = np.array([np.dot(kb[0], mq[c]) / nk for c in range(2)])
+        bound = 2 * 2.0 ** -8 * (1 + 2.0 ** -20)
+        assert abs(m[0] - abs(cos[0] - cos[1])) <= bound
+        if abs(cos[0] - cos[1]) > bound:
+            assert a[0] == int(np.argmax(cos))
+
+
+def test_mirror_cosine_key_scale_and_zero_key():
+    """Scaling a key by a power of two scales every MIRROR score and leaves
+    the labels and cosine margins unchanged; a zero key ties everywhere,
+    goes to cluster 0 with margin 0."""
+    r = np.random.default_rng(12)
+    K = torch.from_numpy(r.standard_normal((300, D))).to(torch.bfloat16).double().numpy()
+    mu = r.standard_normal((17, D))
+    a1, m1 = oracle.assign(K, 0, mu, mode=oracle.MIRROR)
+    for sc in (2.0 ** -20, 2.0 ** 7):
+        a2, m2 = oracle.assign(K * sc, 0, mu, mode=oracle.MIRROR)
+        assert np.array_equal(a1, a2)
+        assert np.allclose(m1, m2, rtol=1e-12, atol=0)
+    a0, m0 = oracle.assign(np.zeros((1, D)), 0, mu, mode=oracle.MIRROR)
+    assert a0[0] == 0 and m0[0] == 0.0
 
 
 def test_objective_closed_forms():
