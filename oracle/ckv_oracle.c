@@ -123,8 +123,8 @@ static double orc_dot(const double *a, const double *b, int d)
 /* ----------------------------------------------------- K-means pieces -- */
 
 /* Initial centroids: mu_c = k_{n_sink + s*c}, s = floor(L'/C)
- * [Clustering in semantic space: "randomly sample keys as initial
- * centroids"; read as evenly spaced tokens]. K is one head [L][d]. */
+ * [Clustering in semantic space: the initial centroids are keys sampled at
+ * random; read here as evenly spaced tokens]. K is one head [L][d]. */
 void orc_init_centroids(int64_t L, int d, const double *K, int n_sink, int C,
                         double *mu)
 {
@@ -244,8 +244,8 @@ void orc_csr(int64_t L, int n_sink, int C, const int32_t *assign,
 }
 
 /* Update step: each centroid becomes the mean of the keys assigned to it
- * [Clustering in semantic space: "the average of the keys assigned to the
- * same centroid"]. Raw keys, fp64 sum in ascending token order, then one
+ * [Clustering in semantic space: a centroid is replaced by the average of
+ * its cluster's keys]. Raw keys, fp64 sum in ascending token order, then one
  * division. MIRROR stores the mean rounded to fp32. A cluster with no keys
  * keeps mu_old. */
 void orc_update(int64_t L, int d, const double *K, int n_sink, int C,
