@@ -79,8 +79,8 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     p->token_base = d->token_base;
     p->t_base = d->t_base;
     p->t_cap = d->t_cap;
-    p->ka = nullptr;          // set by ckv_cluster once K is resolved
-    p->ka_stride = 0;
+    p->ka = p->ku = nullptr;  // set by ckv_cluster once K is resolved
+    p->ka_stride = p->ku_stride = p->ku_rows = p->ku_base = 0;
     p->csr_wide = d->C <= kCsrWideMaxC;
     const int tile = p->csr_wide ? kCsrWideTile : kCsrTile;
     p->ntiles = (p->Lp + tile - 1) / tile;
@@ -305,18 +305,27 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
     K = Kv;
     p.n_cu = device_cu_count();
     hipStream_t s = (hipStream_t)stream;
-    // the assignment reads device keys where they are; host keys are copied
-    // to the workspace once, so the iterations do not cross the host link
+    // the assignment and the update read device keys where they are; host
+    // keys are copied to the workspace once, so the iterations do not cross
+    // the host link
     const size_t es = p.dtype == CKV_BF16 ? 2 : 4;
     hipError_t e = hipSuccess;
     if (k_host) {
         p.ka = p.kt;
         p.ka_stride = p.Lp * kD;
+        p.ku = p.kt;                          // row t - token_base - n_sink
+        p.ku_stride = p.Lp * kD;
+        p.ku_rows = p.Lp;
+        p.ku_base = p.token_base + p.n_sink;
         e = launch_copy_keys(p, K, s);
         if (e != hipSuccess) return launch_status(e);
     } else {
         p.ka = (const char *)K + (size_t)p.n_sink * kD * es;
         p.ka_stride = p.k_head_stride;
+        p.ku = K;
+        p.ku_stride = p.k_head_stride;
+        p.ku_rows = p.L;
+        p.ku_base = p.token_base;
     }
 
     if (p.dtype == CKV_BF16 && p.Lp <= kSmallRows && p.C <= kSmallC)
@@ -326,7 +335,7 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
     for (int t = 0; t < p.iters && e == hipSuccess; ++t) {
         e = launch_assign(p, assign, s);
         if (e == hipSuccess) e = launch_csr(p, assign, csr_offsets, csr_tokens, s);
-        if (e == hipSuccess) e = launch_update(p, K, csr_offsets, csr_tokens, centroids, s);
+        if (e == hipSuccess) e = launch_update(p, csr_offsets, csr_tokens, centroids, s);
     }
     return launch_status(e);
 }

@@ -1157,27 +1157,27 @@ __global__ __launch_bounds__(256) void k_update(
 }
 
 template <int M>
-static void launch_update_m(const ClusterPlan &p, const void *K, const int32_t *offsets,
-                            const int32_t *tokens, float *cent, hipStream_t s) {
+static void launch_update_m(const ClusterPlan &p, const int32_t *offsets, const int32_t *tokens,
+                            float *cent, hipStream_t s) {
     dim3 grid(p.C, p.H);
     if (p.dtype == 1)
-        hipLaunchKernelGGL((k_update<true, M>), grid, dim3(256), 0, s, K, p.k_head_stride, p.L,
-                           p.token_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap, cent,
-                           p.mt, p.mb, p.Cpad);
+        hipLaunchKernelGGL((k_update<true, M>), grid, dim3(256), 0, s, p.ku, p.ku_stride,
+                           p.ku_rows, p.ku_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap,
+                           cent, p.mt, p.mb, p.Cpad);
     else
-        hipLaunchKernelGGL((k_update<false, M>), grid, dim3(256), 0, s, K, p.k_head_stride,
-                           p.L, p.token_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap,
+        hipLaunchKernelGGL((k_update<false, M>), grid, dim3(256), 0, s, p.ku, p.ku_stride,
+                           p.ku_rows, p.ku_base, offsets, tokens, p.c_base, p.c_cap, p.t_cap,
                            cent, p.mt, p.mb, p.Cpad);
 }
 
-hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
-                         const int32_t *tokens, float *cent, hipStream_t s) {
+hipError_t launch_update(const ClusterPlan &p, const int32_t *offsets, const int32_t *tokens,
+                         float *cent, hipStream_t s) {
     if (p.metric == kCosine)
-        launch_update_m<kCosine>(p, K, offsets, tokens, cent, s);
+        launch_update_m<kCosine>(p, offsets, tokens, cent, s);
     else if (p.metric == kInnerProduct)
-        launch_update_m<kInnerProduct>(p, K, offsets, tokens, cent, s);
+        launch_update_m<kInnerProduct>(p, offsets, tokens, cent, s);
     else
-        launch_update_m<kL2>(p, K, offsets, tokens, cent, s);
+        launch_update_m<kL2>(p, offsets, tokens, cent, s);
     return hipGetLastError();
 }
 
@@ -1187,7 +1187,8 @@ hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *off
 // workgroup barriers where the general path has kernel boundaries. Every
 // step is the general path's device code with the same thread-to-data
 // mapping, so the results are bitwise those of the general path:
-//  * the assignment reads the keys where the general one does (ka);
+//  * the assignment and the update read the keys where the general ones do
+//    (ka, ku);
 //  * initial centroids: the chain of block_unit_row / block_store_row, eight
 //    128-thread groups at a time; centroids stay in LDS and the rows the
 //    assignment reads go straight into its LDS tile;
@@ -1207,7 +1208,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
     const uint16_t *__restrict__ K, int64_t head_stride, int64_t L, int n_sink, int64_t Lp,
     int C, int iters, int64_t token_base, float *__restrict__ cent, int c_base, int c_cap,
     int32_t *__restrict__ assign, int32_t *__restrict__ offsets, int32_t *__restrict__ tokens,
-    int64_t t_base, int64_t t_cap, const uint16_t *__restrict__ ka, int64_t ka_stride) {
+    int64_t t_base, int64_t t_cap, const uint16_t *__restrict__ ka, int64_t ka_stride,
+    const uint16_t *__restrict__ ku, int64_t ku_stride, int64_t ku_rows, int64_t ku_base) {
     constexpr bool BIAS = M == kL2;
     __shared__ u32x4 sA[16 * 16];
     __shared__ __align__(16) float sB[16];
@@ -1345,8 +1347,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
                 const int c = c0 + g;
                 int64_t n = 0;
                 if (c < C)
-                    n = upd_partial<true>(K, head_stride, L, token_base, soff + c, stok, Lp, h,
-                                          ltid, red[g]);
+                    n = upd_partial<true>(ku, ku_stride, ku_rows, ku_base, soff + c, stok, Lp,
+                                          h, ltid, red[g]);
                 __syncthreads();
                 if (c < C && (ltid >> 6) == 0)
                     upd_final<true, M>(c, lane, n, red[g], sx[g], scent[c], nullptr, nullptr, sA,
@@ -1369,17 +1371,20 @@ hipError_t launch_cluster_small(const ClusterPlan &p, const void *K, float *cent
         hipLaunchKernelGGL(k_cluster_small<kCosine>, dim3(p.H), dim3(kSmallThreads), 0, s, Kb,
                            p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
                            cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           ka, p.ka_stride);
+                           ka, p.ka_stride, (const uint16_t *)p.ku, p.ku_stride, p.ku_rows,
+                           p.ku_base);
     else if (p.metric == kInnerProduct)
         hipLaunchKernelGGL(k_cluster_small<kInnerProduct>, dim3(p.H), dim3(kSmallThreads), 0, s,
                            Kb, p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
                            cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           ka, p.ka_stride);
+                           ka, p.ka_stride, (const uint16_t *)p.ku, p.ku_stride, p.ku_rows,
+                           p.ku_base);
     else
         hipLaunchKernelGGL(k_cluster_small<kL2>, dim3(p.H), dim3(kSmallThreads), 0, s, Kb,
                            p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
                            cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           ka, p.ka_stride);
+                           ka, p.ka_stride, (const uint16_t *)p.ku, p.ku_stride, p.ku_rows,
+                           p.ku_base);
     return hipGetLastError();
 }
 

@@ -18,6 +18,10 @@ struct ClusterPlan {
     // keys where they are, or their copy kt), heads ka_stride elements apart
     const void *ka;
     int64_t ka_stride;
+    // the rows the update reads: token t of head h is row t - ku_base of
+    // ku + h * ku_stride, rows [0, ku_rows) (the keys where they are, or kt)
+    const void *ku;
+    int64_t ku_stride, ku_rows, ku_base;
     // workspace carve-up (device pointers)
     void *kt;                 // copy of keys in pinned host memory [H][Lp][d]
     void *mt;                 // centroids as the assignment reads them [H][Cpad][d]
@@ -38,8 +42,8 @@ hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cen
 hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s);
 hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offsets,
                       int32_t *tokens, hipStream_t s);
-hipError_t launch_update(const ClusterPlan &p, const void *K, const int32_t *offsets,
-                         const int32_t *tokens, float *cent, hipStream_t s);
+hipError_t launch_update(const ClusterPlan &p, const int32_t *offsets, const int32_t *tokens,
+                         float *cent, hipStream_t s);
 
 // Whole K-means of a small bf16 window in one launch (one workgroup per
 // head), bitwise the general path's result.

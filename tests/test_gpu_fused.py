@@ -175,21 +175,29 @@ def test_host_kv_and_pageable_refusal():
     torch.cuda.synchronize()
 
 
-def test_cluster_reads_pinned_host_keys_and_refuses_pageable():
-    """ckv_cluster over pinned host keys (read through their device mapping)
-    equals the clustering of the same keys in device memory; a pageable host
+@pytest.mark.parametrize("L,C,dtype,metric,token_base", [
+    (2064, 25, "bf16", "cosine", 0), (2064, 25, "bf16", "l2", 100), (336, 4, "bf16", "cosine", 7),
+    (336, 4, "bf16", "inner_product", 0), (2064, 25, "fp32", "cosine", 3)])
+def test_cluster_reads_pinned_host_keys_and_refuses_pageable(L, C, dtype, metric, token_base):
+    """ckv_cluster over pinned host keys (copied once to the workspace, the
+    assignment and the update then reading that copy) equals the clustering
+    of the same keys in device memory, on the general and the small-window
+    path, for every distance and a nonzero token base; a pageable host
     pointer is refused by the C entry point before anything is launched."""
-    say("ckv_cluster over pinned host keys; pageable keys refused")
-    wl = synth.workload(1)
-    K, _, _ = synth.make_kv(wl, L=2064, heads=range(2))
-    Kd = to_dev(K, "bf16")
-    ref = gpu_cluster(Kd, 16, 25, 3)
+    say(f"ckv_cluster over pinned host keys: L={L} C={C} {dtype} {metric} base={token_base}")
+    wl = synth.workload(1 if dtype == "bf16" else 0)
+    K, _, _ = synth.make_kv(wl, L=L, heads=range(2)) if dtype == "bf16" else synth.make_kv(wl, L=L)
+    Kd = to_dev(K, dtype)
+    H = Kd.shape[0]
+    m = {"cosine": ck.CKV_COSINE, "inner_product": ck.CKV_INNER_PRODUCT, "l2": ck.CKV_L2}[metric]
+    ref = gpu_cluster(Kd, 16, C, 3, token_base=token_base, metric=m)
     Kh = torch.empty(Kd.shape, dtype=Kd.dtype, pin_memory=True)
     Kh.copy_(Kd.cpu())
     outs = [torch.empty_like(x) for x in ref]
-    desc = ck.ClusterDesc(H=2, d=D, L=Kd.shape[1], k_head_stride=Kd.stride(0), token_base=0,
-                          n_sink=16, C=25, iters=3, dtype=ck.CKV_BF16, c_base=0, c_cap=25,
-                          t_base=0, t_cap=Kd.shape[1] - 16, metric=ck.CKV_COSINE)
+    desc = ck.ClusterDesc(H=H, d=D, L=Kd.shape[1], k_head_stride=Kd.stride(0),
+                          token_base=token_base, n_sink=16, C=C, iters=3,
+                          dtype=ck.CKV_BF16 if dtype == "bf16" else ck.CKV_F32, c_base=0, c_cap=C,
+                          t_base=0, t_cap=Kd.shape[1] - 16, metric=m)
     lib = ck.load()
     ws = torch.empty(max(ck.ckv_cluster_workspace(desc), 1), dtype=torch.uint8, device=DEV)
     p = lambda t: ct.c_void_p(t.data_ptr())
