@@ -65,7 +65,7 @@ def test_random_decode_shapes(seed):
     fused_case(*cfg)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_cluster_shapes(seed):
     H, n_sink, C, L, iters, dtype = _cluster_cfg(seed)
     say(f"random cluster shape seed {seed}: H={H} sink={n_sink} C={C} L={L} iters={iters} {dtype}")
