@@ -58,7 +58,7 @@ def _cluster_cfg(seed):
     return H, n_sink, C, L, iters, dtype
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(160))
 def test_random_decode_shapes(seed):
     cfg = _decode_cfg(seed)
     say(f"random decode shape seed {seed}: H,G,C,Lp,B,sink,pend,dtype = {cfg}")
