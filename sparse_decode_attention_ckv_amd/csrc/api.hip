@@ -82,7 +82,7 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     p->ka = p->ku = nullptr;  // set by ckv_cluster once K is resolved
     p->ka_stride = p->ku_stride = p->ku_rows = p->ku_base = 0;
     p->csr_wide = d->C <= kCsrWideMaxC;
-    const int tile = p->csr_wide ? kCsrWideTile : kCsrTile;
+    const int tile = kCsrWideTile;
     p->ntiles = (p->Lp + tile - 1) / tile;
     const size_t es = d->dtype == CKV_BF16 ? 2 : 4;
     size_t o = 0;

@@ -648,54 +648,19 @@ hipError_t launch_assign(const ClusterPlan &p, int32_t *assign, hipStream_t s) {
 
 // --------------------------------------------------------------------------
 // CSR (cluster sizes, prefix sums, label-sorted token ids) by a stable
-// counting sort in three passes, no atomics:
-//  count:   per 512-token tile, each wave finds, for every lane, the lanes
-//           holding the same label (one ballot per label bit), giving the
-//           lane's rank among equal labels inside the wave; per-wave label
-//           counts in LDS turn that into a rank inside the tile, and their
-//           sums are the tile's histogram.
-//  scan:    per head and cluster, exclusive prefix over tiles (tile bases)
-//           and the cluster size; exclusive prefix over clusters -> offsets.
-//  scatter: token i of tile T with label a goes to
-//           offsets[a] + base[T][a] + rank_i.
+// counting sort over tiles of 2048 tokens, no atomics:
+//  count:   per tile, each wave finds, for every lane, the lanes holding the
+//           same label (one ballot per label bit), giving the lane's rank
+//           among equal labels; per-wave label counts in LDS turn that into
+//           a rank inside the tile, and their sums are the tile's histogram.
+//  scan:    (C > 512) per head and cluster, exclusive prefix over tiles (tile
+//           bases) and the cluster size.
+//  scatter: offsets = exclusive prefix of the sizes over the clusters; token
+//           i of tile T with label a goes to offsets[a] + base[T][a] + rank_i.
+//           For C <= 512 the scatter also does the scan (one cluster per
+//           thread), so that path is two launches.
 // Ranks grow with the token position, so each cluster lists its tokens in
 // ascending order.
-__global__ __launch_bounds__(kCsrTile) void k_csr_count(
-    const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C, int nbits,
-    int64_t ntiles, int32_t *__restrict__ tile_hist, int32_t *__restrict__ tile_rank) {
-    extern __shared__ int32_t wcnt[];   // [8 waves][C]
-    const int h = blockIdx.y;
-    const int64_t tile = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6;
-    for (int e = tid; e < 8 * C; e += kCsrTile) wcnt[e] = 0;
-    __syncthreads();
-    const int64_t i = tile * kCsrTile + tid;
-    const bool valid = i < Lp;
-    int a = valid ? assign[(int64_t)h * L + n_sink + i] : 0;
-    a = a < 0 ? 0 : (a >= C ? C - 1 : a);
-    uint64_t eq = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        const int bit = (a >> b) & 1;
-        const uint64_t bb = __ballot(bit);
-        eq &= bit ? bb : ~bb;
-    }
-    const int rk = __popcll(eq & __lanemask_lt());
-    if (valid && rk == 0) wcnt[wave * C + a] = __popcll(eq);
-    __syncthreads();
-    if (valid) {
-        int base = 0;
-        for (int w = 0; w < wave; ++w) base += wcnt[w * C + a];
-        tile_rank[(int64_t)h * Lp + i] = rk + base;
-    }
-    int32_t *hist = tile_hist + ((int64_t)h * ntiles + tile) * C;
-    for (int c = tid; c < C; c += kCsrTile) {
-        int sacc = 0;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) sacc += wcnt[w * C + c];
-        hist[c] = sacc;
-    }
-}
-
 // scan: per head, for every cluster, exclusive prefix of its tile counts over
 // the tiles (in tile order) and its total count. Workgroup = 64 clusters x 16
 // parts; part p owns the contiguous tiles [p*R, (p+1)*R), R = ceil(T/16);
@@ -750,57 +715,7 @@ __global__ __launch_bounds__(1024) void k_csr_scan(int32_t *__restrict__ tile_hi
     }
 }
 
-// scatter: every workgroup first turns the cluster counts into offsets (an
-// exclusive scan over the clusters, in LDS; the tile-0 workgroup writes them
-// out), then token i of tile T with label a goes to
-// offsets[a] + base[T][a] + rank_i.
-__global__ __launch_bounds__(kCsrTile) void k_csr_scatter(
-    const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C,
-    int64_t ntiles, const int32_t *__restrict__ counts, const int32_t *__restrict__ tile_base,
-    const int32_t *__restrict__ tile_rank, int32_t *__restrict__ offsets, int c_base,
-    int c_cap, int64_t t_base, int64_t t_cap, int64_t token_base, int32_t *__restrict__ tokens) {
-    __shared__ int excl[kMaxC];
-    __shared__ int wsum[17];
-    const int h = blockIdx.y, tid = threadIdx.x;
-    const int64_t tile = blockIdx.x;
-    const int64_t i = tile * kCsrTile + tid;
-    const bool valid = i < Lp;
-    const int64_t ii = valid ? i : Lp - 1;
-    // this token's label and rank, and the counts, all in flight at once
-    int a = assign[(int64_t)h * L + n_sink + ii];
-    const int rk = tile_rank[(int64_t)h * Lp + ii];
-    constexpr int PER = kMaxC / kCsrTile;          // 4 counts per thread
-    int cv[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int c = tid * PER + k;
-        cv[k] = counts[(int64_t)h * C + (c < C ? c : C - 1)];
-    }
-    int loc = 0;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) loc += (tid * PER + k < C) ? cv[k] : 0;
-    int total;
-    int run = block_excl_scan(loc, wsum, &total);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int c = tid * PER + k;
-        if (c < C) excl[c] = run;
-        run += (c < C) ? cv[k] : 0;
-    }
-    __syncthreads();
-    if (tile == 0) {
-        int32_t *off = offsets + (int64_t)h * (c_cap + 1) + c_base;
-        for (int c = tid; c < C; c += kCsrTile) off[c] = (int32_t)(t_base + excl[c]);
-        if (tid == 0) off[C] = (int32_t)(t_base + total);
-    }
-    a = a < 0 ? 0 : (a >= C ? C - 1 : a);
-    const int64_t pos = (int64_t)excl[a] + tile_base[((int64_t)h * ntiles + tile) * C + a] + rk;
-    if (valid && pos >= 0 && pos < Lp)
-        tokens[(int64_t)h * t_cap + t_base + pos] = (int32_t)(token_base + n_sink + i);
-}
-
-// Two-launch CSR for C <= 512: the same stable counting sort over tiles of
-// 2048 tokens, with the scan folded into the scatter.
+// The kernels over 2048-token tiles (the scan above works on any tiling).
 //  count_wide: wave w of the tile's 512 threads takes its tokens
 //              [256 w, 256 w + 256) in 4 rounds of 64; a token's rank among
 //              equal labels of its wave is its ballot rank in the round plus
@@ -812,16 +727,17 @@ __global__ __launch_bounds__(kCsrTile) void k_csr_scatter(
 //              head (its size) and over the tiles before this one (its base
 //              here); an exclusive scan over the sizes gives the offsets, and
 //              token i of label a goes to offsets[a] + base[a] + rank_i.
-// Ranks grow with the token position, so each cluster lists its tokens in
-// ascending order, as in the three-pass version.
+// MAXC sizes the count's LDS: 512 clusters for the two-launch path, 2048 for
+// the three-launch one.
 constexpr int kCsrThreads = 512;
 constexpr int kCsrRounds = kCsrWideTile / kCsrThreads;   // rounds of 64 per wave
 
+template <int MAXC>
 __global__ __launch_bounds__(kCsrThreads) void k_csr_count_wide(
     const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C, int nbits,
     int64_t ntiles, int32_t *__restrict__ tile_hist, int32_t *__restrict__ tile_rank) {
     static_assert(kCsrRounds * kCsrThreads == kCsrWideTile, "tile = waves x rounds x 64");
-    __shared__ int32_t wcnt[kCsrThreads / 64][kCsrWideMaxC];
+    __shared__ int32_t wcnt[kCsrThreads / 64][MAXC];
     const int h = blockIdx.y;
     const int64_t tile = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -835,8 +751,7 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr_count_wide(
         const int v = valid[r] ? assign[(int64_t)h * L + n_sink + i] : 0;
         a[r] = v < 0 ? 0 : (v >= C ? C - 1 : v);
     }
-    for (int e = tid; e < (kCsrThreads / 64) * kCsrWideMaxC; e += kCsrThreads)
-        (&wcnt[0][0])[e] = 0;
+    for (int e = tid; e < (kCsrThreads / 64) * MAXC; e += kCsrThreads) (&wcnt[0][0])[e] = 0;
     __syncthreads();
     int rk[kCsrRounds];
 #pragma unroll
@@ -929,14 +844,74 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr_scatter_wide(
     }
 }
 
+// Scatter over the same 2048-token tiles for C > 512, after k_csr_scan has
+// turned the tile histograms into tile bases and cluster sizes: the offsets
+// are an exclusive scan of the sizes (four per thread, in LDS; the tile-0
+// workgroup writes them out), and token i of label a goes to
+// offsets[a] + base[T][a] + rank_i, the tokens of a thread taken in the
+// rounds of k_csr_scatter_wide.
+__global__ __launch_bounds__(kCsrThreads) void k_csr_scatter_tiles(
+    const int32_t *__restrict__ assign, int64_t L, int n_sink, int64_t Lp, int C,
+    int64_t ntiles, const int32_t *__restrict__ counts, const int32_t *__restrict__ tile_base,
+    const int32_t *__restrict__ tile_rank, int32_t *__restrict__ offsets, int c_base,
+    int c_cap, int64_t t_base, int64_t t_cap, int64_t token_base, int32_t *__restrict__ tokens) {
+    constexpr int PER = kMaxC / kCsrThreads;        // cluster sizes per thread
+    __shared__ int start[kMaxC];                    // offsets[c] + base of this tile
+    __shared__ int wsum[17];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    int a[kCsrRounds], rk[kCsrRounds];
+#pragma unroll
+    for (int r = 0; r < kCsrRounds; ++r) {
+        const int64_t i = tile * kCsrWideTile + (int64_t)kCsrThreads * r + tid;
+        const int64_t ii = i < Lp ? i : Lp - 1;
+        const int v = assign[(int64_t)h * L + n_sink + ii];
+        a[r] = v < 0 ? 0 : (v >= C ? C - 1 : v);
+        rk[r] = tile_rank[(int64_t)h * Lp + ii];
+    }
+    int cv[PER], bv[PER];
+    const int32_t *tb = tile_base + ((int64_t)h * ntiles + tile) * C;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int c = tid * PER + k;
+        const int cc = c < C ? c : C - 1;
+        cv[k] = counts[(int64_t)h * C + cc];
+        bv[k] = tb[cc];
+    }
+    int loc = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) loc += (tid * PER + k < C) ? cv[k] : 0;
+    int total;
+    int run = block_excl_scan(loc, wsum, &total);
+    int32_t *off = offsets + (int64_t)h * (c_cap + 1) + c_base;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int c = tid * PER + k;
+        if (c < C) {
+            start[c] = run + bv[k];
+            if (tile == 0) off[c] = (int32_t)(t_base + run);
+        }
+        run += (c < C) ? cv[k] : 0;
+    }
+    if (tile == 0 && tid == 0) off[C] = (int32_t)(t_base + total);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kCsrRounds; ++r) {
+        const int64_t i = tile * kCsrWideTile + (int64_t)kCsrThreads * r + tid;
+        const int64_t pos = (int64_t)start[a[r]] + rk[r];
+        if (i < Lp && pos >= 0 && pos < Lp)
+            tokens[(int64_t)h * t_cap + t_base + pos] = (int32_t)(token_base + n_sink + i);
+    }
+}
+
 hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offsets,
                       int32_t *tokens, hipStream_t s) {
     int nbits = 1;
     while ((1 << nbits) < p.C) ++nbits;
     dim3 grid((unsigned)p.ntiles, p.H);
     if (p.csr_wide) {
-        hipLaunchKernelGGL(k_csr_count_wide, grid, dim3(kCsrThreads), 0, s, assign, p.L,
-                           p.n_sink, p.Lp, p.C, nbits, p.ntiles, p.tile_hist, p.tile_rank);
+        hipLaunchKernelGGL(k_csr_count_wide<kCsrWideMaxC>, grid, dim3(kCsrThreads), 0, s, assign,
+                           p.L, p.n_sink, p.Lp, p.C, nbits, p.ntiles, p.tile_hist, p.tile_rank);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_csr_scatter_wide, grid, dim3(kCsrThreads), 0, s, assign, p.L,
@@ -945,19 +920,18 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
                            p.t_cap, p.token_base, tokens);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_csr_count, grid, dim3(kCsrTile), (size_t)8 * p.C * sizeof(int32_t), s,
-                       assign, p.L, p.n_sink, p.Lp, p.C, nbits, p.ntiles, p.tile_hist,
-                       p.tile_rank);
+    hipLaunchKernelGGL(k_csr_count_wide<kMaxC>, grid, dim3(kCsrThreads), 0, s, assign, p.L,
+                       p.n_sink, p.Lp, p.C, nbits, p.ntiles, p.tile_hist, p.tile_rank);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_csr_scan, dim3((p.C + 63) / 64, p.H), dim3(1024), 0, s, p.tile_hist,
                        p.ntiles, p.C, p.counts);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_csr_scatter, grid, dim3(kCsrTile), 0, s, assign, p.L, p.n_sink, p.Lp,
-                       p.C, p.ntiles, (const int32_t *)p.counts, (const int32_t *)p.tile_hist,
-                       (const int32_t *)p.tile_rank, offsets, p.c_base, p.c_cap, p.t_base,
-                       p.t_cap, p.token_base, tokens);
+    hipLaunchKernelGGL(k_csr_scatter_tiles, grid, dim3(kCsrThreads), 0, s, assign, p.L, p.n_sink,
+                       p.Lp, p.C, p.ntiles, (const int32_t *)p.counts,
+                       (const int32_t *)p.tile_hist, (const int32_t *)p.tile_rank, offsets,
+                       p.c_base, p.c_cap, p.t_base, p.t_cap, p.token_base, tokens);
     return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ struct ClusterPlan {
     int metric;               // kCosine, kInnerProduct or kL2
     int64_t L, Lp, k_head_stride, token_base, t_base, t_cap;
     int64_t ntiles;           // CSR tiles per head
-    bool csr_wide;            // C <= kCsrWideMaxC: the two-launch CSR over wide tiles
+    bool csr_wide;            // C <= kCsrWideMaxC: the two-launch CSR (else count, scan, scatter)
     int n_cu;                 // compute units of the device (persistent grids)
     // the rows the assignment reads: the first clustered row of head 0 (the
     // keys where they are, or their copy kt), heads ka_stride elements apart
@@ -32,9 +32,8 @@ struct ClusterPlan {
     int32_t *counts;          // [H][C] cluster sizes
 };
 
-constexpr int kCsrTile = 512;          // tokens per CSR tile (one workgroup)
-constexpr int kCsrWideTile = 2048;     // tokens per tile of the two-launch CSR
-constexpr int kCsrWideMaxC = 512;      // clusters it handles (one per scatter thread)
+constexpr int kCsrWideTile = 2048;     // tokens per CSR tile (one workgroup)
+constexpr int kCsrWideMaxC = 512;      // clusters of the two-launch CSR (one per scatter thread)
 
 hipError_t launch_copy_keys(const ClusterPlan &p, const void *K, hipStream_t s);
 hipError_t launch_init_centroids(const ClusterPlan &p, const void *K, float *cent,

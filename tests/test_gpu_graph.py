@@ -87,7 +87,7 @@ def test_decode_graph_replay_matches_eager():
 
 @pytest.mark.parametrize("H,L,C", [
     (4, 8192, 101),      # C <= 512: the two-launch CSR over 2048-token tiles
-    (2, 12000, 600),     # C > 512: the three-pass CSR, two LDS rounds in the assignment
+    (2, 12000, 600),     # C > 512: the three-launch CSR, two LDS rounds in the assignment
 ])
 def test_cluster_graph_replay_matches_eager(H, L, C):
     """The whole Lloyd loop (normalisation, initial centroids, 10 x assignment,

@@ -51,7 +51,7 @@ def _cluster_cfg(seed):
     elif kind == 1:                       # two-launch CSR
         C = int(r.integers(17, 513))
         L = n_sink + int(r.integers(max(C, 1100), 4000))
-    else:                                 # three-pass CSR
+    else:                                 # three-launch CSR
         C = int(r.integers(513, 800))
         L = n_sink + int(r.integers(C, 3500))
     iters = int(r.integers(1, 4))
