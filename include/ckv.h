@@ -83,6 +83,8 @@ int ckv_abi_version(void);
  * stored against the unit centroid (mu/|mu| in fp64, rounded to fp32, then
  * to bf16 for CKV_BF16 keys), with fp32 accumulation. Keys are never
  * normalised. Centroid means are accumulated in fp64 and stored as fp32.
+ * Scores are fp32, so keys and centroids must keep |k|^2 and the scores
+ * within fp32 range (|k| < 1.8e19).
  *
  * desc->metric selects the distance of the assignment (the update is the
  * mean of the raw keys for every metric):
