@@ -235,8 +235,8 @@ int ckv_sparse_attn(const ckv_attn_desc *desc, const void *q, const void *K,
  * & KV compression], with one launch and one round trip of idx through
  * memory fewer: the workgroup that writes 64 slots of a head's idx row also
  * runs the attention over those 64 rows. idx, n_sel and o are bitwise the
- * values the two separate calls produce (same device code, same order).
- * CKV_F32 runs the two separate calls' kernels.
+ * values the two separate calls produce (same device code, same order),
+ * for CKV_BF16 and CKV_F32 alike.
  *
  * sdesc and adesc describe the same step: equal H, G, B and dtype
  * (CKV_ERR_INVALID_ARG otherwise); each is also checked as by its own call.

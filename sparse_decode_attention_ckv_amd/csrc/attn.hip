@@ -23,172 +23,30 @@
 
 namespace ckv {
 
-constexpr int kRowsPerSlot = kAttnRows / 16;
-
-template <typename T> struct Acc;
-template <> struct Acc<uint16_t> { typedef float type; };
-template <> struct Acc<float> { typedef double type; };
-
-__device__ __forceinline__ float ex(float x) { return __expf(x); }
-__device__ __forceinline__ double ex(double x) { return exp(x); }
-
-// 8 consecutive elements held as 16-byte chunks (1 for bf16, 2 for fp32)
-template <typename T>
-__device__ __forceinline__ void unpack_chunks(const u32x4 *w, typename Acc<T>::type *f);
-template <>
-__device__ __forceinline__ void unpack_chunks<uint16_t>(const u32x4 *w, float *f) {
-    unpack8(w[0], f);
-}
-template <>
-__device__ __forceinline__ void unpack_chunks<float>(const u32x4 *w, double *f) {
-    f[0] = __uint_as_float(w[0].x); f[1] = __uint_as_float(w[0].y);
-    f[2] = __uint_as_float(w[0].z); f[3] = __uint_as_float(w[0].w);
-    f[4] = __uint_as_float(w[1].x); f[5] = __uint_as_float(w[1].y);
-    f[6] = __uint_as_float(w[1].z); f[7] = __uint_as_float(w[1].w);
-}
-
-template <typename T, int G>
-__global__ __launch_bounds__(256) void k_attn_partial(
-    const T *__restrict__ q, const T *__restrict__ K, const T *__restrict__ V,
+// partial, fp32: the rows of split s come from idx (thread (slot, q8) takes
+// split rows slot + 16 k); everything else is attn_rows_f32. idx is read
+// without waiting for n_sel.
+template <int G>
+__global__ __launch_bounds__(256) void k_attn_partial_f32(
+    const float *__restrict__ q, const float *__restrict__ K, const float *__restrict__ V,
     int64_t kv_head_stride, int64_t kv_rows, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ n_sel, int B, double scale,
-    typename Acc<T>::type *__restrict__ part, int H, int S) {
-    typedef typename Acc<T>::type A;
-    constexpr int PW = kD + 2;                    // partial record: m, l, acc[d]
-    __shared__ A zs[G][kAttnRows];
-    __shared__ A red[4][G][kD + 1];
+    const int32_t *__restrict__ n_sel, int B, double scale, double *__restrict__ part, int H,
+    int S) {
+    __shared__ double zs[G][kAttnRows];
+    __shared__ double red[4][G][kD + 1];
     int h, s;
     xcd_head_unit(blockIdx.x, S, h, s);
     if (h >= H) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = tid >> 4, q8 = tid & 15;
-    const int r0 = s * kAttnRows;
-
-    // rows r0 + slot + 16k. Every load below is issued unconditionally from a
-    // valid address (clamped) and masked afterwards, so a thread's loads are
-    // all in flight together; idx is read without waiting for n_sel.
+    const int slot = threadIdx.x >> 4;
     int tk[kRowsPerSlot];
 #pragma unroll
     for (int k = 0; k < kRowsPerSlot; ++k) {
-        const int r = r0 + slot + 16 * k;
+        const int r = s * kAttnRows + slot + 16 * k;
         tk[k] = idx[(int64_t)h * B + (r < B ? r : B - 1)];
     }
     int n = n_sel[h];
     n = n < 0 ? 0 : (n > B ? B : n);
-    int64_t row[kRowsPerSlot];
-    bool ok[kRowsPerSlot];
-#pragma unroll
-    for (int k = 0; k < kRowsPerSlot; ++k) {
-        const int r = r0 + slot + 16 * k;
-        ok[k] = r < n && tk[k] >= 0 && (int64_t)tk[k] < kv_rows;
-        row[k] = ok[k] ? tk[k] : 0;
-    }
-    // raw 16-byte chunks: K and V rows, then q; the scheduling barrier keeps
-    // every one of these loads ahead of the first use
-    constexpr int NV = sizeof(T) * 8 / 16;        // 16-byte chunks per 8 elements
-    u32x4 kr[kRowsPerSlot][NV], vr[kRowsPerSlot][NV], qr[G][NV];
-#pragma unroll
-    for (int k = 0; k < kRowsPerSlot; ++k) {
-        const int64_t base = (int64_t)h * kv_head_stride + row[k] * kD + 8 * q8;
-#pragma unroll
-        for (int c = 0; c < NV; ++c) {
-            kr[k][c] = *(const u32x4 *)(K + base + c * (16 / sizeof(T)));
-            vr[k][c] = *(const u32x4 *)(V + base + c * (16 / sizeof(T)));
-        }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int c = 0; c < NV; ++c)
-            qr[g][c] = *(const u32x4 *)(q + ((int64_t)h * G + g) * kD + 8 * q8 + c * (16 / sizeof(T)));
-    __builtin_amdgcn_sched_barrier(0);
-    A kf[kRowsPerSlot][8], vf[kRowsPerSlot][8], qf[G][8];
-#pragma unroll
-    for (int k = 0; k < kRowsPerSlot; ++k) {
-        unpack_chunks<T>(kr[k], kf[k]);
-        unpack_chunks<T>(vr[k], vf[k]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            kf[k][e] = ok[k] ? kf[k][e] : (A)0;
-            vf[k][e] = ok[k] ? vf[k][e] : (A)0;
-        }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) unpack_chunks<T>(qr[g], qf[g]);
-
-    A z[kRowsPerSlot][G];
-#pragma unroll
-    for (int k = 0; k < kRowsPerSlot; ++k)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            A a = (A)0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a += qf[g][e] * kf[k][e];
-#pragma unroll
-            for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m);
-            z[k][g] = ok[k] ? a * (A)scale : (A)(-INFINITY);
-        }
-    if (q8 == 0) {
-#pragma unroll
-        for (int k = 0; k < kRowsPerSlot; ++k)
-#pragma unroll
-            for (int g = 0; g < G; ++g) zs[g][slot + 16 * k] = z[k][g];
-    }
-    __syncthreads();
-    A mx[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        A m = (A)(-INFINITY);
-#pragma unroll 8
-        for (int r = 0; r < kAttnRows; ++r) m = zs[g][r] > m ? zs[g][r] : m;
-        mx[g] = m;
-    }
-    A acc[G][8], l[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] = (A)0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = (A)0;
-#pragma unroll
-        for (int k = 0; k < kRowsPerSlot; ++k) {
-            const A p = ok[k] ? ex(z[k][g] - mx[g]) : (A)0;
-            l[g] += p;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] += p * vf[k][e];
-        }
-    }
-    // the 4 slots of a wave (lanes q8, q8+16, q8+32, q8+48), then the 4 waves
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] += __shfl_xor(l[g], 16);
-        l[g] += __shfl_xor(l[g], 32);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            acc[g][e] += __shfl_xor(acc[g][e], 16);
-            acc[g][e] += __shfl_xor(acc[g][e], 32);
-        }
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[wave][g][8 * lane + e] = acc[g][e];
-            if (lane == 0) red[wave][g][kD] = l[g];
-        }
-    }
-    __syncthreads();
-    for (int w = tid; w < G * (kD + 1); w += 256) {
-        const int g = w / (kD + 1), j = w % (kD + 1);
-        const A v = ((red[0][g][j] + red[1][g][j]) + red[2][g][j]) + red[3][g][j];
-        A *dst = part + (((int64_t)h * G + g) * S + s) * PW;
-        if (j == kD) {
-            dst[0] = mx[g];
-            dst[1] = v;
-        } else {
-            dst[2 + j] = v;
-        }
-    }
-
+    attn_rows_f32<G>(q, K, V, kv_head_stride, kv_rows, h, s, tk, n, scale, part, S, zs, red);
 }
 
 // partial, bf16: the rows of split s come from idx (the V row of lane l is
@@ -279,9 +137,10 @@ static void launch_g(const AttnPlan &p, const void *q, const void *K, const void
                            (const uint16_t *)K, (const uint16_t *)V, p.kv_head_stride, p.kv_rows,
                            idx, n_sel, p.B, p.scale, (float *)p.partials, p.H, p.S);
     else
-        hipLaunchKernelGGL((k_attn_partial<T, G>), dim3(xcd_head_grid(p.H, p.S)), dim3(256), 0,
-                           s, (const T *)q, (const T *)K, (const T *)V, p.kv_head_stride,
-                           p.kv_rows, idx, n_sel, p.B, p.scale, (A *)p.partials, p.H, p.S);
+        hipLaunchKernelGGL((k_attn_partial_f32<G>), dim3(xcd_head_grid(p.H, p.S)), dim3(256), 0,
+                           s, (const float *)q, (const float *)K, (const float *)V,
+                           p.kv_head_stride, p.kv_rows, idx, n_sel, p.B, p.scale,
+                           (double *)p.partials, p.H, p.S);
 }
 
 template <typename T>

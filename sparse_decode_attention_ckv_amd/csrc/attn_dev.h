@@ -1,4 +1,4 @@
-// attn_dev.h -- device core of the bf16 split-K decode attention, shared by
+// attn_dev.h -- device core of the split-K decode attention (bf16 and fp32), shared by
 // the attention kernel (attn.hip) and the fused selection + attention kernel
 // (decode.hip). Internal; include/ckv.h is the public ABI.
 //
@@ -14,6 +14,170 @@ namespace ckv {
 
 constexpr int kAttnRows = kAttnSplitRows;   // rows of idx per workgroup (split)
 constexpr int kAttnPW = kD + 2;             // partial record: m, l, acc[d]
+
+constexpr int kRowsPerSlot = kAttnRows / 16;
+
+template <typename T> struct Acc;
+template <> struct Acc<uint16_t> { typedef float type; };
+template <> struct Acc<float> { typedef double type; };
+
+__device__ __forceinline__ float ex(float x) { return __expf(x); }
+__device__ __forceinline__ double ex(double x) { return exp(x); }
+
+// 8 consecutive elements held as 16-byte chunks (1 for bf16, 2 for fp32)
+template <typename T>
+__device__ __forceinline__ void unpack_chunks(const u32x4 *w, typename Acc<T>::type *f);
+template <>
+__device__ __forceinline__ void unpack_chunks<uint16_t>(const u32x4 *w, float *f) {
+    unpack8(w[0], f);
+}
+template <>
+__device__ __forceinline__ void unpack_chunks<float>(const u32x4 *w, double *f) {
+    f[0] = __uint_as_float(w[0].x); f[1] = __uint_as_float(w[0].y);
+    f[2] = __uint_as_float(w[0].z); f[3] = __uint_as_float(w[0].w);
+    f[4] = __uint_as_float(w[1].x); f[5] = __uint_as_float(w[1].y);
+    f[6] = __uint_as_float(w[1].z); f[7] = __uint_as_float(w[1].w);
+}
+
+// One split of 64 selected fp32 rows of KV head h for its G query heads, in
+// fp64, 256 threads: thread (slot = tid >> 4, q8 = tid & 15) holds channels
+// 8 q8 .. 8 q8 + 7 of split rows slot + 16 k (k < 4), whose tokens are tk[k];
+// a row is valid if its split position 64 s + slot + 16 k is below n and its
+// token lies in [0, kv_rows). Scores are 16-lane dot products, then the split
+// max, exp and the weighted V sum, reduced over the slots in a fixed order
+// (lane butterflies, then the four waves in order); the partial (m, l,
+// acc[128]) of query head hG + g goes to part[((hG + g) S + s) * kAttnPW ...].
+// Every K, V and q chunk of a thread is requested before the first is used.
+// zs and red are LDS; red is first written after a barrier that every thread
+// reaches after its own loads, so it may share LDS with data the caller read
+// before the call.
+template <int G>
+__device__ __forceinline__ void attn_rows_f32(const float *__restrict__ q,
+                                              const float *__restrict__ K,
+                                              const float *__restrict__ V, int64_t kv_head_stride,
+                                              int64_t kv_rows, int h, int s,
+                                              const int (&tk)[kRowsPerSlot], int n, double scale,
+                                              double *__restrict__ part, int S,
+                                              double (&zs)[G][kAttnRows],
+                                              double (&red)[4][G][kD + 1]) {
+    constexpr int PW = kAttnPW;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = tid >> 4, q8 = tid & 15;
+    const int r0 = s * kAttnRows;
+    int64_t row[kRowsPerSlot];
+    bool ok[kRowsPerSlot];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        const int r = r0 + slot + 16 * k;
+        ok[k] = r < n && tk[k] >= 0 && (int64_t)tk[k] < kv_rows;
+        row[k] = ok[k] ? tk[k] : 0;
+    }
+    // raw 16-byte chunks: K and V rows, then q; the scheduling barrier keeps
+    // every one of these loads ahead of the first use
+    constexpr int NV = 2;                         // 16-byte chunks per 8 fp32 elements
+    u32x4 kr[kRowsPerSlot][NV], vr[kRowsPerSlot][NV], qr[G][NV];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        const int64_t base = (int64_t)h * kv_head_stride + row[k] * kD + 8 * q8;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            kr[k][c] = *(const u32x4 *)(K + base + c * 4);
+            vr[k][c] = *(const u32x4 *)(V + base + c * 4);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+            qr[g][c] = *(const u32x4 *)(q + ((int64_t)h * G + g) * kD + 8 * q8 + c * 4);
+    __builtin_amdgcn_sched_barrier(0);
+    double kf[kRowsPerSlot][8], vf[kRowsPerSlot][8], qf[G][8];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) {
+        unpack_chunks<float>(kr[k], kf[k]);
+        unpack_chunks<float>(vr[k], vf[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kf[k][e] = ok[k] ? kf[k][e] : (double)0;
+            vf[k][e] = ok[k] ? vf[k][e] : (double)0;
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) unpack_chunks<float>(qr[g], qf[g]);
+
+    double z[kRowsPerSlot][G];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            double a = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a += qf[g][e] * kf[k][e];
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m);
+            z[k][g] = ok[k] ? a * (double)scale : (double)(-INFINITY);
+        }
+    if (q8 == 0) {
+#pragma unroll
+        for (int k = 0; k < kRowsPerSlot; ++k)
+#pragma unroll
+            for (int g = 0; g < G; ++g) zs[g][slot + 16 * k] = z[k][g];
+    }
+    __syncthreads();
+    double mx[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        double m = (double)(-INFINITY);
+#pragma unroll 8
+        for (int r = 0; r < kAttnRows; ++r) m = zs[g][r] > m ? zs[g][r] : m;
+        mx[g] = m;
+    }
+    double acc[G][8], l[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] = (double)0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = (double)0;
+#pragma unroll
+        for (int k = 0; k < kRowsPerSlot; ++k) {
+            const double p = ok[k] ? ex(z[k][g] - mx[g]) : (double)0;
+            l[g] += p;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] += p * vf[k][e];
+        }
+    }
+    // the 4 slots of a wave (lanes q8, q8+16, q8+32, q8+48), then the 4 waves
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] += __shfl_xor(l[g], 16);
+        l[g] += __shfl_xor(l[g], 32);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[g][e] += __shfl_xor(acc[g][e], 16);
+            acc[g][e] += __shfl_xor(acc[g][e], 32);
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wave][g][8 * lane + e] = acc[g][e];
+            if (lane == 0) red[wave][g][kD] = l[g];
+        }
+    }
+    __syncthreads();
+    for (int w = tid; w < G * (kD + 1); w += 256) {
+        const int g = w / (kD + 1), j = w % (kD + 1);
+        const double v = ((red[0][g][j] + red[1][g][j]) + red[2][g][j]) + red[3][g][j];
+        double *dst = part + (((int64_t)h * G + g) * S + s) * PW;
+        if (j == kD) {
+            dst[0] = mx[g];
+            dst[1] = v;
+        } else {
+            dst[2 + j] = v;
+        }
+    }
+}
 
 // One split of 64 selected rows of KV head h for its G query heads, 256
 // threads (4 waves). Partial (m, l, acc[128]) of query head hG + g goes to

@@ -7,7 +7,8 @@
 // the sparse decode attention softmax(q K_S^T / sqrt(d)) V_S (section
 // 背景知识与设计原则 / 长上下文推理与KV缓存压缩).
 //
-// Launches: k_sel_score (as in ckv_select), then k_sel_attn_bf16, whose
+// Launches: k_sel_score (as in ckv_select), then k_sel_attn_bf16 (fp32 rows:
+// k_sel_attn_f32, the same selection with the fp64 attention core), whose
 // workgroup (h, s) finds the cut of head h on its own, turns slots
 // [64 s, 64 s + 64) of the head's idx row into token ids (and writes them),
 // and right away runs the attention partial of that split on those rows;
@@ -59,6 +60,55 @@ __global__ __launch_bounds__(kCutThreads) void k_sel_attn_bf16(
                                    part, NS, s, zs, U.sv);
 }
 
+// fp32 rows: the same selection, then attn_rows_f32 on the window's rows
+// (fp64 arithmetic); the selection's LDS is dead once the slot is known, so
+// the attention's reduction buffer reuses it.
+template <int CMAX, int G>
+__global__ __launch_bounds__(kCutThreads) void k_sel_attn_f32(
+    const double *__restrict__ scores, int C, const int32_t *__restrict__ offsets, int c_cap,
+    const int32_t *__restrict__ tokens, int64_t t_cap, int n_sink, int64_t pending_begin,
+    int64_t n_pending, int B, int32_t *__restrict__ idx, int32_t *__restrict__ n_sel,
+    const float *__restrict__ q, const float *__restrict__ K, const float *__restrict__ V,
+    int64_t kv_head_stride, int64_t kv_rows, double scale, double *__restrict__ part, int H,
+    int NS) {
+    static_assert(kSelSlice == kAttnRows, "one selection window per attention split");
+    __shared__ union {
+        SelLds<CMAX> sel;
+        double red[4][G][kD + 1];
+    } U;
+    __shared__ double zs[G][kAttnRows];
+    int h, s;
+    xcd_head_unit(blockIdx.x, NS, h, s);
+    if (h >= H) return;
+    const SelSlot r = sel_cut_emit<CMAX>(U.sel, scores + (int64_t)h * C, C,
+                                         offsets + (int64_t)h * (c_cap + 1),
+                                         tokens + (int64_t)h * t_cap, t_cap, n_sink,
+                                         pending_begin, n_pending, B, s);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = s * kSelSlice + lane;
+    if (wave == 0 && e < B) idx[(int64_t)h * B + e] = r.val;
+    if (s == 0 && tid == 0) n_sel[h] = r.n_sel;
+    // every wave holds the token of split row `lane`; thread (slot, q8) takes
+    // split rows slot + 16 k
+    const int slot = tid >> 4;
+    int tk[kRowsPerSlot];
+#pragma unroll
+    for (int k = 0; k < kRowsPerSlot; ++k) tk[k] = __shfl(r.val, slot + 16 * k);
+    const int n = r.n_sel < 0 ? 0 : (r.n_sel < B ? r.n_sel : B);
+    attn_rows_f32<G>(q, K, V, kv_head_stride, kv_rows, h, s, tk, n, scale, part, NS, zs, U.red);
+}
+
+template <int CMAX, int G>
+static void launch_fused_f32_g(const SelectPlan &sp, const AttnPlan &ap, const void *q,
+                               const int32_t *offsets, const int32_t *tokens, const void *K,
+                               const void *V, int32_t *idx, int32_t *n_sel, hipStream_t s) {
+    hipLaunchKernelGGL((k_sel_attn_f32<CMAX, G>), dim3(xcd_head_grid(sp.H, ap.S)),
+                       dim3(kCutThreads), 0, s, sp.scores, sp.C, offsets, sp.c_cap, tokens,
+                       sp.t_cap, sp.n_sink, sp.pending_begin, sp.n_pending, sp.B, idx, n_sel,
+                       (const float *)q, (const float *)K, (const float *)V, ap.kv_head_stride,
+                       ap.kv_rows, ap.scale, (double *)ap.partials, sp.H, ap.S);
+}
+
 template <int CMAX, int G>
 static void launch_fused_g(const SelectPlan &sp, const AttnPlan &ap, const void *q,
                            const int32_t *offsets, const int32_t *tokens, const void *K,
@@ -74,19 +124,29 @@ static void launch_fused_g(const SelectPlan &sp, const AttnPlan &ap, const void 
                        sp.H, ap.S);
 }
 
-template <int CMAX>
+template <int CMAX, bool F32, int G>
+static void launch_fused(const SelectPlan &sp, const AttnPlan &ap, const void *q,
+                         const int32_t *offsets, const int32_t *tokens, const void *K,
+                         const void *V, int32_t *idx, int32_t *n_sel, hipStream_t s) {
+    if constexpr (F32)
+        launch_fused_f32_g<CMAX, G>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s);
+    else
+        launch_fused_g<CMAX, G>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s);
+}
+
+template <int CMAX, bool F32>
 static void launch_fused_c(const SelectPlan &sp, const AttnPlan &ap, const void *q,
                            const int32_t *offsets, const int32_t *tokens, const void *K,
                            const void *V, int32_t *idx, int32_t *n_sel, hipStream_t s) {
     switch (sp.G) {
-        case 1: launch_fused_g<CMAX, 1>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
-        case 2: launch_fused_g<CMAX, 2>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
-        case 3: launch_fused_g<CMAX, 3>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
-        case 4: launch_fused_g<CMAX, 4>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
-        case 5: launch_fused_g<CMAX, 5>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
-        case 6: launch_fused_g<CMAX, 6>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
-        case 7: launch_fused_g<CMAX, 7>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
-        default: launch_fused_g<CMAX, 8>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
+        case 1: launch_fused<CMAX, F32, 1>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
+        case 2: launch_fused<CMAX, F32, 2>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
+        case 3: launch_fused<CMAX, F32, 3>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
+        case 4: launch_fused<CMAX, F32, 4>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
+        case 5: launch_fused<CMAX, F32, 5>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
+        case 6: launch_fused<CMAX, F32, 6>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
+        case 7: launch_fused<CMAX, F32, 7>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
+        default: launch_fused<CMAX, F32, 8>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s); break;
     }
 }
 
@@ -94,17 +154,17 @@ hipError_t launch_select_attn(const SelectPlan &sp, const AttnPlan &ap, const vo
                               const float *cent, const int32_t *offsets, const int32_t *tokens,
                               const void *K, const void *V, int32_t *idx, int32_t *n_sel,
                               float *o, hipStream_t s) {
-    if (sp.dtype != 1) {
-        // fp32: the separate kernels (fp64 attention arithmetic)
-        hipError_t e = launch_select(sp, q, cent, offsets, tokens, idx, n_sel, s);
-        return e == hipSuccess ? launch_attn(ap, q, K, V, idx, n_sel, o, s) : e;
-    }
     hipError_t e = launch_sel_score(sp, q, cent, s);
     if (e != hipSuccess) return e;
-    if (sp.C <= 512)
-        launch_fused_c<512>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s);
+    const bool f32 = sp.dtype != 1;             // fp32: fp64 attention arithmetic
+    if (sp.C <= 512 && f32)
+        launch_fused_c<512, true>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s);
+    else if (sp.C <= 512)
+        launch_fused_c<512, false>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s);
+    else if (f32)
+        launch_fused_c<kMaxC, true>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s);
     else
-        launch_fused_c<kMaxC>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s);
+        launch_fused_c<kMaxC, false>(sp, ap, q, offsets, tokens, K, V, idx, n_sel, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_attn_combine(ap, o, s);

@@ -23,6 +23,8 @@ CHECKED = {
     "k_sel_cut": "select.hip",
     "k_attn_partial_bf16": "attn.hip",
     "k_attn_combine": "attn.hip",
+    "k_sel_attn_f32": "decode.hip",
+    "k_attn_partial_f32": "attn.hip",
 }
 
 
