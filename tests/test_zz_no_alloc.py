@@ -65,3 +65,25 @@ def test_noalloc_matches_select_attn_twice():
         torch.cuda.synchronize()
         for x, y in zip(got, ref):
             assert torch.equal(x, y), (H, L, C, B)
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_select_attn_fp32():
+    """fp32 rows run the fused fp32 kernel (fp64 attention) in both calls."""
+    wl = synth.workload(0)
+    for L, C, B in ((2048, 25, 256), (1040, 13, 128)):
+        say(f"noalloc decode step, fp32: L={L} C={C} B={B}")
+        K, V, _ = synth.make_kv(wl, L=L)
+        Kd, Vd = to_dev(K, "f32"), to_dev(V, "f32")
+        qs, _ = synth.make_queries(wl, 0)
+        qd = to_dev(qs, "f32")
+        cent, _, off, tok = ck.ckv_cluster(Kd, 16, C, 4)
+        ref = ck.ckv_select_attn(qd, cent, off, tok, C, B, Kd, Vd)
+        idx = torch.full((wl.H, B), -7, dtype=torch.int32, device=DEV)
+        ns = torch.full((wl.H,), -7, dtype=torch.int32, device=DEV)
+        out = torch.full((wl.H * wl.G, 128), float("nan"), dtype=torch.float32, device=DEV)
+        got = ck.ckv_select_attn_noalloc(qd, cent, off, tok, C, B, Kd, Vd, idx=idx, n_sel=ns,
+                                         out=out)
+        torch.cuda.synchronize()
+        for x, y in zip(got, ref):
+            assert torch.equal(x, y), (L, C, B)
