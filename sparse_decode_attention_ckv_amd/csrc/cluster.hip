@@ -947,32 +947,62 @@ hipError_t launch_csr(const ClusterPlan &p, const int32_t *assign, int32_t *offs
 // a group (ltid = thread in the group) into red; returns the cluster size.
 // off points at the cluster's offset pair and tok at its head's token list
 // (global memory, or LDS copies of both), t_cap bounds the list.
+// The pieces of the first half. upd_range: the cluster's CSR segment from
+// its offset pair, clamped to [0, t_cap].
+__device__ __forceinline__ void upd_range(const int32_t *off, int64_t t_cap, int64_t &beg,
+                                          int64_t &end) {
+    beg = off[0];
+    end = off[1];
+    beg = beg < 0 ? 0 : (beg > t_cap ? t_cap : beg);
+    end = end < beg ? beg : (end > t_cap ? t_cap : end);
+}
+
+// rows beg + slot + 16k in batches of kUpdNB: a batch's token ids (clamped
+// addresses; rows past the segment are masked when the keys are added)
+constexpr int kUpdNB = 8;
+
+__device__ __forceinline__ void upd_tokens(const int32_t *tok, int64_t r0, int64_t beg,
+                                           int64_t end, int32_t (&tk)[kUpdNB]) {
+    const int64_t last = end > beg ? end - 1 : beg;
+#pragma unroll
+    for (int k = 0; k < kUpdNB; ++k) {
+        const int64_t r = r0 + 16 * k;
+        tk[k] = tok[r < end ? r : last];
+    }
+}
+
+// the 16 slots' sums combined in a fixed order (lane butterflies here, the
+// waves in order in upd_final) into red[wave]
+__device__ __forceinline__ void upd_reduce(double (&acc)[8], int lane, int wave,
+                                           double (*red)[kD]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        acc[e] += __shfl_xor(acc[e], 16);
+        acc[e] += __shfl_xor(acc[e], 32);
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
+    }
+}
+
 template <bool BF16>
 __device__ __forceinline__ int64_t upd_partial(
     const void *__restrict__ K, int64_t head_stride, int64_t L, int64_t token_base,
     const int32_t *off, const int32_t *tok, int64_t t_cap, int h, int ltid, double (*red)[kD]) {
     const int lane = ltid & 63, wave = ltid >> 6;
     const int slot = ltid >> 4, q = ltid & 15;
-    int64_t beg = off[0], end = off[1];
-    beg = beg < 0 ? 0 : (beg > t_cap ? t_cap : beg);
-    end = end < beg ? beg : (end > t_cap ? t_cap : end);
-    const int64_t n = end - beg;
-
+    int64_t beg, end;
+    upd_range(off, t_cap, beg, end);
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    // rows beg + slot + 16k in batches of NB: the batch's token ids, then its
-    // key chunks, each set in flight at once (clamped addresses, masked values)
-    constexpr int NB = 8;
+    // a batch's token ids, then its key chunks, each set in flight at once
+    constexpr int NB = kUpdNB;
     constexpr int NV = BF16 ? 1 : 2;              // 16-byte chunks per 8 channels
-    const int64_t last = end > beg ? end - 1 : beg;
     for (int64_t r0 = beg + slot; r0 < end; r0 += 16 * NB) {
         int32_t tk[NB];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            const int64_t r = r0 + 16 * k;
-            tk[k] = tok[r < end ? r : last];
-        }
+        upd_tokens(tok, r0, beg, end, tk);
         int64_t row[NB];
         bool ok[NB];
 #pragma unroll
@@ -1007,16 +1037,8 @@ __device__ __forceinline__ int64_t upd_partial(
             for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
         }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        acc[e] += __shfl_xor(acc[e], 16);
-        acc[e] += __shfl_xor(acc[e], 32);
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
-    }
-    return n;
+    upd_reduce(acc, lane, wave, red);
+    return end - beg;
 }
 
 // Second half, by the group's first wave once red is complete: lane l owns
@@ -1162,7 +1184,8 @@ hipError_t launch_update(const ClusterPlan &p, const int32_t *offsets, const int
 // step is the general path's device code with the same thread-to-data
 // mapping, so the results are bitwise those of the general path:
 //  * the assignment and the update read the keys where the general ones do
-//    (ka, ku);
+//    (ka, ku), or, for windows of at most kSmallLdsRows rows, from an LDS
+//    copy made once per call (the same values in the same order);
 //  * initial centroids: the chain of block_unit_row / block_store_row, eight
 //    128-thread groups at a time; centroids stay in LDS and the rows the
 //    assignment reads go straight into its LDS tile;
@@ -1177,7 +1200,64 @@ hipError_t launch_update(const ClusterPlan &p, const int32_t *offsets, const int
 // the final centroids): a barrier after a global store waits for it.
 // Windows up to kSmallRows rows and kSmallC clusters, bf16 keys.
 
-template <int M>
+// Windows of at most kSmallLdsRows rows keep their key rows in LDS for the
+// whole call (96 KB): row r's 16-byte chunk q at srow[16 r + (q ^ (r & 15))],
+// so the 16 rows a wave reads at one chunk position fall in distinct banks.
+constexpr int kSmallLdsRows = 384;
+
+// as_load_b from those LDS rows
+__device__ __forceinline__ void as_lds_b(const u32x4 *srow, int64_t Lp, int64_t tok0, int col,
+                                         int kq, bf16x8 (&b)[4][4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t row = tok0 + 16 * t + col;
+        const int rr = (int)(row < Lp ? row : Lp - 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            b[t][s] = __builtin_bit_cast(bf16x8, srow[rr * 16 + ((4 * s + kq) ^ (rr & 15))]);
+    }
+}
+
+// upd_partial (bf16) with the rows from those LDS rows: the same rows added in
+// the same order; token t is window row t - row0
+__device__ __forceinline__ int64_t upd_partial_lds(const u32x4 *srow, int64_t Lp, int64_t row0,
+                                                   const int32_t *off, const int32_t *tok,
+                                                   int64_t t_cap, int ltid, double (*red)[kD]) {
+    const int lane = ltid & 63, wave = ltid >> 6;
+    const int slot = ltid >> 4, q = ltid & 15;
+    int64_t beg, end;
+    upd_range(off, t_cap, beg, end);
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int64_t r0 = beg + slot; r0 < end; r0 += 16 * kUpdNB) {
+        int32_t tk[kUpdNB];
+        upd_tokens(tok, r0, beg, end, tk);
+        // every chunk of the batch read before the first is added (clamped
+        // rows, masked values), as upd_partial keeps its loads in flight
+        bool ok[kUpdNB];
+        u32x4 w[kUpdNB];
+#pragma unroll
+        for (int k = 0; k < kUpdNB; ++k) {
+            int64_t i = (int64_t)tk[k] - row0;
+            ok[k] = r0 + 16 * k < end && i >= 0 && i < Lp;
+            i = ok[k] ? i : 0;
+            w[k] = srow[i * 16 + (q ^ (i & 15))];
+        }
+#pragma unroll
+        for (int k = 0; k < kUpdNB; ++k) {
+            if (!ok[k]) continue;
+            float f[8];
+            unpack8(w[k], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
+        }
+    }
+    upd_reduce(acc, lane, wave, red);
+    return end - beg;
+}
+
+template <int M, bool LR>
 __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
     const uint16_t *__restrict__ K, int64_t head_stride, int64_t L, int n_sink, int64_t Lp,
     int C, int iters, int64_t token_base, float *__restrict__ cent, int c_base, int c_cap,
@@ -1194,6 +1274,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
     __shared__ float scent[kSmallC][kD];
     __shared__ int32_t stok[kSmallRows];
     __shared__ int32_t soff[kSmallC + 1];
+    __shared__ u32x4 srow[LR ? kSmallLdsRows * 16 : 1];
     const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int32_t *as = assign + (int64_t)h * L;
@@ -1239,6 +1320,23 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
         }
     }
     __syncthreads();
+    // LR (a window of at most kSmallLdsRows rows): its key rows into LDS once
+    if constexpr (LR) {
+        const u32x4 *src = (const u32x4 *)(ka + (int64_t)h * ka_stride);
+        constexpr int PER = kSmallLdsRows * 16 / kSmallThreads;   // chunks per thread
+        u32x4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + kSmallThreads * k;
+            v[k] = src[e < Lp * 16 ? e : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + kSmallThreads * k, r = e >> 4;
+            if (e < Lp * 16) srow[r * 16 + ((e & 15) ^ (r & 15))] = v[k];
+        }
+        __syncthreads();
+    }
 
     const int col = lane & 15, kq = lane >> 4;
     const int64_t i = tid;                      // this thread's token
@@ -1254,7 +1352,20 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
             // across the CSR and the update they would spill
             const uint16_t *kh = ka + (int64_t)h * ka_stride;
             asm volatile("" : "+s"(kh));
-            as_load_b((const u32x4 *)kh, Lp, (int64_t)wave * 64, col, kq, b);
+            // a wave whose 64 tokens all lie past the window loads nothing
+            // (its labels are not kept): 11 of the 16 waves for a 320-row
+            // window, whose clamped loads would triple the CU's row traffic
+            if (wave * 64 < Lp) {
+                if constexpr (LR)
+                    as_lds_b(srow, Lp, (int64_t)wave * 64, col, kq, b);
+                else
+                    as_load_b((const u32x4 *)kh, Lp, (int64_t)wave * 64, col, kq, b);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) b[t][s2] = bf16x8{};
+            }
             float beta[4] = {0.f, 0.f, 0.f, 0.f};
             if (M == kCosine) as_beta(b, beta);
             as_lds_a(sA, 0, col, kq, afr);
@@ -1290,26 +1401,34 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
             const int rk = __popcll(eq & __lanemask_lt());
             if (valid && rk == 0) wcnt[wave][a] = __popcll(eq);
             __syncthreads();
-            int base = 0, excl = 0;
+            // the first wave turns the wave counts into the cluster offsets
+            // (lane c: the size of cluster c, then an exclusive scan over the
+            // lanes); the CSR offsets in LDS for the update, relative to the
+            // window's first token slot, in global memory after the last
+            // assignment
+            if (wave == 0) {
+                int sz = 0;
+                if (lane < C)
+#pragma unroll
+                    for (int w = 0; w < 16; ++w) sz += wcnt[w][lane];
+                const int ex = wave_incl_scan(sz) - sz;
+                if (lane <= C) {
+                    soff[lane] = ex;
+                    if (last)
+                        offsets[(int64_t)h * (c_cap + 1) + c_base + lane] = (int32_t)(t_base + ex);
+                }
+            }
+            int base = 0;
+#pragma unroll
             for (int w = 0; w < 16; ++w) base += w < wave ? wcnt[w][a] : 0;
-            for (int c = 0; c < a; ++c)
-                for (int w = 0; w < 16; ++w) excl += wcnt[w][c];
-            // the CSR in LDS for the update (offsets relative to the window's
-            // first token slot); in global memory after the last assignment
+            __syncthreads();
             if (valid) {
-                const int pos = excl + base + rk;
+                const int pos = soff[a] + base + rk;
                 if (pos >= 0 && pos < Lp) {
                     const int32_t t = (int32_t)(token_base + n_sink + i);
                     stok[pos] = t;
                     if (last) tokens[(int64_t)h * t_cap + t_base + pos] = t;
                 }
-            }
-            if (tid <= C) {
-                int e = 0;
-                for (int c = 0; c < tid; ++c)
-                    for (int w = 0; w < 16; ++w) e += wcnt[w][c];
-                soff[tid] = e;
-                if (last) offsets[(int64_t)h * (c_cap + 1) + c_base + tid] = (int32_t)(t_base + e);
             }
             __syncthreads();
         }
@@ -1320,11 +1439,18 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
             for (int c0 = 0; c0 < C; c0 += 4) {
                 const int c = c0 + g;
                 int64_t n = 0;
-                if (c < C)
-                    n = upd_partial<true>(ku, ku_stride, ku_rows, ku_base, soff + c, stok, Lp,
-                                          h, ltid, red[g]);
+                if (c < C) {
+                    if constexpr (LR)
+                        n = upd_partial_lds(srow, Lp, token_base + n_sink, soff + c, stok, Lp,
+                                            ltid, red[g]);
+                    else
+                        n = upd_partial<true>(ku, ku_stride, ku_rows, ku_base, soff + c, stok,
+                                              Lp, h, ltid, red[g]);
+                }
                 __syncthreads();
-                if (c < C && (ltid >> 6) == 0)
+                // wave g of group g finishes its cluster: waves 0, 5, 10 and
+                // 15, one on each SIMD, so the four fp64 chains run side by side
+                if (c < C && (ltid >> 6) == g)
                     upd_final<true, M>(c, lane, n, red[g], sx[g], scent[c], nullptr, nullptr, sA,
                                        BIAS ? sB : nullptr);
                 __syncthreads();
@@ -1336,29 +1462,34 @@ __global__ __launch_bounds__(kSmallThreads) void k_cluster_small(
         cent[((int64_t)h * c_cap + c_base + e / kD) * kD + e % kD] = scent[e / kD][e % kD];
 }
 
+template <int M, bool LR>
+static void launch_small_m(const ClusterPlan &p, const void *K, float *cent, int32_t *assign,
+                           int32_t *offsets, int32_t *tokens, hipStream_t s) {
+    hipLaunchKernelGGL((k_cluster_small<M, LR>), dim3(p.H), dim3(kSmallThreads), 0, s,
+                       (const uint16_t *)K, p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters,
+                       p.token_base, cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base,
+                       p.t_cap, (const uint16_t *)p.ka, p.ka_stride, (const uint16_t *)p.ku,
+                       p.ku_stride, p.ku_rows, p.ku_base);
+}
+
+template <int M>
+static void launch_small_lr(const ClusterPlan &p, const void *K, float *cent, int32_t *assign,
+                            int32_t *offsets, int32_t *tokens, hipStream_t s) {
+    if (p.Lp <= kSmallLdsRows)
+        launch_small_m<M, true>(p, K, cent, assign, offsets, tokens, s);
+    else
+        launch_small_m<M, false>(p, K, cent, assign, offsets, tokens, s);
+}
+
 hipError_t launch_cluster_small(const ClusterPlan &p, const void *K, float *cent,
                                 int32_t *assign, int32_t *offsets, int32_t *tokens,
                                 hipStream_t s) {
-    const uint16_t *Kb = (const uint16_t *)K;
-    const uint16_t *ka = (const uint16_t *)p.ka;
     if (p.metric == kCosine)
-        hipLaunchKernelGGL(k_cluster_small<kCosine>, dim3(p.H), dim3(kSmallThreads), 0, s, Kb,
-                           p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
-                           cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           ka, p.ka_stride, (const uint16_t *)p.ku, p.ku_stride, p.ku_rows,
-                           p.ku_base);
+        launch_small_lr<kCosine>(p, K, cent, assign, offsets, tokens, s);
     else if (p.metric == kInnerProduct)
-        hipLaunchKernelGGL(k_cluster_small<kInnerProduct>, dim3(p.H), dim3(kSmallThreads), 0, s,
-                           Kb, p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
-                           cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           ka, p.ka_stride, (const uint16_t *)p.ku, p.ku_stride, p.ku_rows,
-                           p.ku_base);
+        launch_small_lr<kInnerProduct>(p, K, cent, assign, offsets, tokens, s);
     else
-        hipLaunchKernelGGL(k_cluster_small<kL2>, dim3(p.H), dim3(kSmallThreads), 0, s, Kb,
-                           p.k_head_stride, p.L, p.n_sink, p.Lp, p.C, p.iters, p.token_base,
-                           cent, p.c_base, p.c_cap, assign, offsets, tokens, p.t_base, p.t_cap,
-                           ka, p.ka_stride, (const uint16_t *)p.ku, p.ku_stride, p.ku_rows,
-                           p.ku_base);
+        launch_small_lr<kL2>(p, K, cent, assign, offsets, tokens, s);
     return hipGetLastError();
 }
 
