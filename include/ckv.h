@@ -127,14 +127,24 @@ typedef struct {
     int32_t metric;         /* ckv_metric of the assignment (0: cosine) */
 } ckv_cluster_desc;
 
-/* Bytes of workspace ckv_cluster needs for `desc` (0 if desc is invalid). */
+/* Bytes of workspace ckv_cluster needs for `desc`, whatever memory K is in
+ * (0 if desc is invalid). Its last region holds a copy of the clustered rows
+ * of keys in pinned host memory. */
 size_t ckv_cluster_workspace(const ckv_cluster_desc *desc);
+
+/* Bytes of workspace ckv_cluster needs for `desc` when K is device memory:
+ * ckv_cluster_workspace() without the region for the copy of host keys
+ * (H * (L - n_sink) * d * element bytes less, 64 MiB at 8 x 32768 bf16 rows).
+ * ckv_cluster over pinned host keys with only this much returns
+ * CKV_ERR_WORKSPACE before anything is enqueued. 0 if desc is invalid. */
+size_t ckv_cluster_workspace_device(const ckv_cluster_desc *desc);
 
 /* K: window row 0 of head 0, element type desc->dtype, row r of head h at
  * K + (h * k_head_stride + r) * d. Device memory, or pinned host memory (read
- * through its device mapping; its clustered rows are first copied to the
- * workspace, which is sized for that copy whatever K is); any other pointer
- * is CKV_ERR_INVALID_ARG. */
+ * through its device mapping; its clustered rows are first copied to the last
+ * region of the workspace); any other pointer is CKV_ERR_INVALID_ARG.
+ * workspace_bytes below ckv_cluster_workspace_device(), or below
+ * ckv_cluster_workspace() for host keys, is CKV_ERR_WORKSPACE. */
 int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
                 int32_t *assign, int32_t *csr_offsets, int32_t *csr_tokens,
                 void *workspace, size_t workspace_bytes, void *stream);

@@ -25,7 +25,8 @@ __all__ = [
     "CKV_OK", "CKV_ERR_INVALID_ARG", "CKV_ERR_UNSUPPORTED", "CKV_ERR_WORKSPACE",
     "CKV_ERR_LAUNCH", "CKVError", "lib_path", "load", "ClusterDesc", "SelectDesc",
     "AttnDesc", "ckv_cluster", "ckv_select", "ckv_sparse_attn",
-    "ckv_cluster_workspace", "ckv_select_workspace", "ckv_attn_workspace",
+    "ckv_cluster_workspace", "ckv_cluster_workspace_device", "ckv_select_workspace",
+    "ckv_attn_workspace",
     "ckv_status_string", "ckv_abi_version", "ckv_select_attn", "ckv_select_attn_workspace",
     "ckv_cache_rows", "ckv_cache_workspace", "ckv_cache_step", "ckv_device_view",
     "CacheDesc", "cache_desc", "cache_state", "ckv_select_attn_noalloc",
@@ -81,6 +82,7 @@ _SIGS = {
     "ckv_status_string": (ct.c_char_p, [ct.c_int]),
     "ckv_abi_version": (ct.c_int, []),
     "ckv_cluster_workspace": (ct.c_size_t, [ct.POINTER(ClusterDesc)]),
+    "ckv_cluster_workspace_device": (ct.c_size_t, [ct.POINTER(ClusterDesc)]),
     "ckv_cluster": (ct.c_int, [ct.POINTER(ClusterDesc), _P, _P, _P, _P, _P, _P, ct.c_size_t, _P]),
     "ckv_select_workspace": (ct.c_size_t, [ct.POINTER(SelectDesc)]),
     "ckv_select": (ct.c_int, [ct.POINTER(SelectDesc), _P, _P, _P, _P, _P, _P, _P, ct.c_size_t, _P]),
@@ -197,6 +199,12 @@ def ckv_cluster_workspace(desc: ClusterDesc) -> int:
     return load().ckv_cluster_workspace(ct.byref(desc))
 
 
+def ckv_cluster_workspace_device(desc: ClusterDesc) -> int:
+    """Workspace bytes for ckv_cluster when K is device memory (no room for
+    the copy of host keys)."""
+    return load().ckv_cluster_workspace_device(ct.byref(desc))
+
+
 def ckv_select_workspace(desc: SelectDesc) -> int:
     return load().ckv_select_workspace(ct.byref(desc))
 
@@ -250,7 +258,9 @@ def ckv_cluster(K: torch.Tensor, n_sink: int, C: int, iters: int, *, token_base:
                        C=C, iters=iters, dtype=_dtype_code(K), c_base=c_base,
                        c_cap=centroids.shape[1], t_base=t_base, t_cap=csr_tokens.shape[1],
                        metric=metric)
-    nb = lib.ckv_cluster_workspace(ct.byref(desc))
+    # device keys need no room for the copy that pinned host keys get
+    nb = (lib.ckv_cluster_workspace_device if K.is_cuda else lib.ckv_cluster_workspace)(
+        ct.byref(desc))
     if nb == 0:
         # report the reason through the call itself (no launch happens)
         _check(lib.ckv_cluster(ct.byref(desc), _ptr(K), _ptr(centroids), _ptr(assign),

@@ -63,7 +63,10 @@ int check_cluster(const ckv_cluster_desc *d) {
     return CKV_OK;
 }
 
-void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char *ws) {
+// Workspace carve-up. *bytes: the whole workspace; *bytes_dev (if given): its
+// prefix without the copy of pinned host keys, all that device keys need.
+void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char *ws,
+                  size_t *bytes_dev = nullptr) {
     p->H = d->H;
     p->C = d->C;
     p->Cpad = (d->C + 63) / 64 * 64;
@@ -86,8 +89,6 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     p->ntiles = (p->Lp + tile - 1) / tile;
     const size_t es = d->dtype == CKV_BF16 ? 2 : 4;
     size_t o = 0;
-    p->kt = ws ? ws + o : nullptr;
-    o += align_up((size_t)p->H * p->Lp * kD * es);
     p->mt = ws ? ws + o : nullptr;
     o += align_up((size_t)p->H * p->Cpad * kD * es);
     p->mb = ws ? (float *)(ws + o) : nullptr;
@@ -98,6 +99,9 @@ void plan_cluster(const ckv_cluster_desc *d, ClusterPlan *p, size_t *bytes, char
     o += align_up((size_t)p->H * p->Lp * sizeof(int32_t));
     p->counts = ws ? (int32_t *)(ws + o) : nullptr;
     o += align_up((size_t)p->H * p->C * sizeof(int32_t));
+    if (bytes_dev) *bytes_dev = o;
+    p->kt = ws ? ws + o : nullptr;            // last: only keys in host memory use it
+    o += align_up((size_t)p->H * p->Lp * kD * es);
     *bytes = o;
 }
 
@@ -275,7 +279,7 @@ const char *ckv_status_string(int status) {
     }
 }
 
-int ckv_abi_version(void) { return 3; }
+int ckv_abi_version(void) { return 4; }
 
 size_t ckv_cluster_workspace(const ckv_cluster_desc *desc) {
     if (check_cluster(desc) != CKV_OK) return 0;
@@ -283,6 +287,14 @@ size_t ckv_cluster_workspace(const ckv_cluster_desc *desc) {
     size_t bytes;
     plan_cluster(desc, &p, &bytes, nullptr);
     return bytes;
+}
+
+size_t ckv_cluster_workspace_device(const ckv_cluster_desc *desc) {
+    if (check_cluster(desc) != CKV_OK) return 0;
+    ClusterPlan p;
+    size_t bytes, dev;
+    plan_cluster(desc, &p, &bytes, nullptr, &dev);
+    return dev;
 }
 
 int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
@@ -294,14 +306,15 @@ int ckv_cluster(const ckv_cluster_desc *desc, const void *K, float *centroids,
     if (!aligned16(K) || !aligned16(centroids) || !stride_ok(desc->k_head_stride, desc->dtype))
         return CKV_ERR_INVALID_ARG;
     ClusterPlan p;
-    size_t need;
-    plan_cluster(desc, &p, &need, (char *)workspace);
-    if (!workspace || workspace_bytes < need) return CKV_ERR_WORKSPACE;
+    size_t need, need_dev;
+    plan_cluster(desc, &p, &need, (char *)workspace, &need_dev);
+    if (!workspace || workspace_bytes < need_dev) return CKV_ERR_WORKSPACE;
     // K as the kernels read it: device memory, or pinned host memory through
     // its device mapping; pageable host memory and unknown pointers are refused
     const void *Kv;
     bool k_host = false;
     if (device_view(K, &Kv, &k_host) != CKV_OK || !aligned16(Kv)) return CKV_ERR_INVALID_ARG;
+    if (k_host && workspace_bytes < need) return CKV_ERR_WORKSPACE;   // room for the copy
     K = Kv;
     p.n_cu = device_cu_count();
     hipStream_t s = (hipStream_t)stream;

@@ -33,7 +33,7 @@ from typing import Callable, List, Optional, Tuple
 import torch
 
 from . import (CKV_BF16, CKV_F32, AttnDesc, ClusterDesc, SelectDesc, ckv_attn_workspace,
-               ckv_cluster, ckv_cluster_workspace, ckv_select, ckv_select_attn,
+               ckv_cluster, ckv_cluster_workspace_device, ckv_select, ckv_select_attn,
                ckv_select_attn_workspace, ckv_select_workspace, ckv_sparse_attn)
 
 __all__ = ["decode_schedule", "IncrementalDecoder", "capture"]
@@ -124,7 +124,7 @@ class IncrementalDecoder:
         ad = AttnDesc(H=H, G=self.G, d=d, B=B, kv_head_stride=hs, kv_rows=rows, scale=0.0,
                       dtype=dt)
         u8 = dict(dtype=torch.uint8, device=dev)
-        self.ws_c = torch.empty(max(ckv_cluster_workspace(cd), 1), **u8)
+        self.ws_c = torch.empty(max(ckv_cluster_workspace_device(cd), 1), **u8)
         self.ws_s = torch.empty(max(ckv_select_workspace(sd), 1), **u8)
         self.ws_a = torch.empty(max(ckv_attn_workspace(ad), 1), **u8)
         self.ws_f = torch.empty(max(ckv_select_attn_workspace(sd, ad), 1), **u8)
@@ -132,7 +132,7 @@ class IncrementalDecoder:
             wd = ClusterDesc(H=H, d=d, L=m, k_head_stride=hs, token_base=L, n_sink=0, C=c_plus,
                              iters=iters, dtype=dt, c_base=C, c_cap=c_cap, t_base=L - n_sink,
                              t_cap=t_cap)
-            self.ws_w = torch.empty(max(ckv_cluster_workspace(wd), 1), **u8)
+            self.ws_w = torch.empty(max(ckv_cluster_workspace_device(wd), 1), **u8)
             self.asg_w = torch.empty((H, m), **i32)
         self.set_lag(lag, side)
 

@@ -64,7 +64,7 @@ def test_status_strings():
     for s in range(5):
         assert ck.ckv_status_string(s)
     assert ck.ckv_status_string(99) == "unknown status"
-    assert ck.ckv_abi_version() == 3
+    assert ck.ckv_abi_version() == 4
 
 
 def _cl(**kw):
@@ -114,11 +114,16 @@ def test_cluster_rejects_bad_descriptors(kw, status):
 
 def test_cluster_workspace_and_pointer_checks():
     d = _cl()
-    need = ck.load().ckv_cluster_workspace(ct.byref(d))
-    # unit keys (bf16) + unit centroids + tile histograms + tile ranks
-    assert need >= 2 * 984 * 128 * 2 + 2 * 64 * 128 * 2 + 2 * 2 * 12 * 4 + 2 * 984 * 4
-    assert _call_cluster(d, ws_bytes=need - 1) == ck.CKV_ERR_WORKSPACE
+    lib = ck.load()
+    need = lib.ckv_cluster_workspace(ct.byref(d))
+    need_dev = lib.ckv_cluster_workspace_device(ct.byref(d))
+    # unit centroids + tile histograms + tile ranks, then the host-key copy
+    assert need_dev >= 2 * 64 * 128 * 2 + 2 * 1 * 12 * 4 + 2 * 984 * 4
+    assert need - need_dev == 2 * 984 * 128 * 2           # H * L' * d * bf16, 256-aligned
+    # below the device-key size: refused before the key pointer is looked at
+    assert _call_cluster(d, ws_bytes=need_dev - 1) == ck.CKV_ERR_WORKSPACE
     assert _call_cluster(d, nullK=True) == ck.CKV_ERR_INVALID_ARG
+    assert lib.ckv_cluster_workspace_device(ct.byref(_cl(C=0))) == 0
 
 
 def _sel(**kw):

@@ -207,6 +207,17 @@ def test_cluster_reads_pinned_host_keys_and_refuses_pageable(L, C, dtype, metric
     assert st == ck.CKV_OK
     for a, b in zip(outs, ref):
         assert torch.equal(a, b)
+    # host keys need the workspace's copy region; device keys do without it
+    need_dev = ck.ckv_cluster_workspace_device(desc)
+    assert 0 < need_dev < ws.numel()
+    st = lib.ckv_cluster(ct.byref(desc), p(Kh), *(p(x) for x in outs), p(ws), need_dev, stream)
+    assert st == ck.CKV_ERR_WORKSPACE
+    outs2 = [torch.empty_like(x) for x in ref]
+    st = lib.ckv_cluster(ct.byref(desc), p(Kd), *(p(x) for x in outs2), p(ws), need_dev, stream)
+    torch.cuda.synchronize()
+    assert st == ck.CKV_OK
+    for a, b in zip(outs2, ref):
+        assert torch.equal(a, b)
     Kp = Kd.cpu()
     assert not Kp.is_pinned()
     st = lib.ckv_cluster(ct.byref(desc), p(Kp), *(p(x) for x in outs), p(ws), ws.numel(), stream)

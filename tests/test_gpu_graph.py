@@ -103,7 +103,7 @@ def test_cluster_graph_replay_matches_eager(H, L, C):
     desc = ck.ClusterDesc(H=H, d=128, L=L, k_head_stride=Kd.stride(0), token_base=0, n_sink=16,
                           C=C, iters=10, dtype=ck.CKV_BF16, c_base=0, c_cap=C, t_base=0,
                           t_cap=L - 16, metric=ck.CKV_COSINE)
-    ws = torch.empty(ck.ckv_cluster_workspace(desc), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(ck.ckv_cluster_workspace_device(desc), dtype=torch.uint8, device=DEV)
 
     def call():
         ck.ckv_cluster(Kd, 16, C, 10, centroids=out[0], assign=out[1], csr_offsets=out[2],
