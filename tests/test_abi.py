@@ -7,6 +7,8 @@
   status code before anything is enqueued.
 """
 import ctypes as ct
+
+import numpy as np
 import os
 import re
 import subprocess
@@ -124,6 +126,27 @@ def test_cluster_workspace_and_pointer_checks():
     assert _call_cluster(d, ws_bytes=need_dev - 1) == ck.CKV_ERR_WORKSPACE
     assert _call_cluster(d, nullK=True) == ck.CKV_ERR_INVALID_ARG
     assert lib.ckv_cluster_workspace_device(ct.byref(_cl(C=0))) == 0
+
+
+def test_cluster_workspace_device_is_a_prefix():
+    """Seeded descriptors of both dtypes and all three distances: the device-key
+    workspace is the host-key one less the key copy (the last region,
+    H * L' * d elements rounded up to 256 bytes)."""
+    rng = np.random.default_rng(11)
+    lib = ck.load()
+    for _ in range(64):
+        H = int(rng.integers(1, 65))
+        n_sink = int(rng.integers(0, 33))
+        L = n_sink + int(rng.integers(1, 200000))
+        C = int(rng.integers(1, min(2048, L - n_sink) + 1))
+        dtype = [ck.CKV_BF16, ck.CKV_F32][int(rng.integers(0, 2))]
+        d = _cl(H=H, L=L, n_sink=n_sink, C=C, c_cap=C, t_cap=L - n_sink, dtype=dtype,
+                metric=int(rng.integers(0, 3)), k_head_stride=L * 128)
+        need = lib.ckv_cluster_workspace(ct.byref(d))
+        need_dev = lib.ckv_cluster_workspace_device(ct.byref(d))
+        es = 2 if dtype == ck.CKV_BF16 else 4
+        copy = (H * (L - n_sink) * 128 * es + 255) // 256 * 256
+        assert need_dev > 0 and need - need_dev == copy, (H, L, n_sink, C, dtype)
 
 
 def _sel(**kw):
