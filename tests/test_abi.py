@@ -7,12 +7,11 @@
   status code before anything is enqueued.
 """
 import ctypes as ct
-
-import numpy as np
 import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 import torch
 
