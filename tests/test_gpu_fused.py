@@ -182,8 +182,10 @@ def test_cluster_reads_pinned_host_keys_and_refuses_pageable(L, C, dtype, metric
     """ckv_cluster over pinned host keys (copied once to the workspace, the
     assignment and the update then reading that copy) equals the clustering
     of the same keys in device memory, on the general and the small-window
-    path, for every distance and a nonzero token base; a pageable host
-    pointer is refused by the C entry point before anything is launched."""
+    path, for every distance and a nonzero token base; neither call writes
+    past the workspace size it declares (the device-key size for device
+    keys); a pageable host pointer is refused by the C entry point before
+    anything is launched."""
     say(f"ckv_cluster over pinned host keys: L={L} C={C} {dtype} {metric} base={token_base}")
     wl = synth.workload(1 if dtype == "bf16" else 0)
     K, _, _ = synth.make_kv(wl, L=L, heads=range(2)) if dtype == "bf16" else synth.make_kv(wl, L=L)
@@ -199,25 +201,32 @@ def test_cluster_reads_pinned_host_keys_and_refuses_pageable(L, C, dtype, metric
                           dtype=ck.CKV_BF16 if dtype == "bf16" else ck.CKV_F32, c_base=0, c_cap=C,
                           t_base=0, t_cap=Kd.shape[1] - 16, metric=m)
     lib = ck.load()
-    ws = torch.empty(max(ck.ckv_cluster_workspace(desc), 1), dtype=torch.uint8, device=DEV)
+    need = ck.ckv_cluster_workspace(desc)
+    guard = 4096                                  # bytes past the declared size, never written
+    ws = torch.empty(need + guard, dtype=torch.uint8, device=DEV)
+    ws[need:] = 0xA5
     p = lambda t: ct.c_void_p(t.data_ptr())
     stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
-    st = lib.ckv_cluster(ct.byref(desc), p(Kh), *(p(x) for x in outs), p(ws), ws.numel(), stream)
+    st = lib.ckv_cluster(ct.byref(desc), p(Kh), *(p(x) for x in outs), p(ws), need, stream)
     torch.cuda.synchronize()
     assert st == ck.CKV_OK
     for a, b in zip(outs, ref):
         assert torch.equal(a, b)
+    assert bool((ws[need:] == 0xA5).all())
     # host keys need the workspace's copy region; device keys do without it
+    # and write nothing past the smaller size
     need_dev = ck.ckv_cluster_workspace_device(desc)
-    assert 0 < need_dev < ws.numel()
+    assert 0 < need_dev < need
     st = lib.ckv_cluster(ct.byref(desc), p(Kh), *(p(x) for x in outs), p(ws), need_dev, stream)
     assert st == ck.CKV_ERR_WORKSPACE
+    ws[need_dev:] = 0x5A
     outs2 = [torch.empty_like(x) for x in ref]
     st = lib.ckv_cluster(ct.byref(desc), p(Kd), *(p(x) for x in outs2), p(ws), need_dev, stream)
     torch.cuda.synchronize()
     assert st == ck.CKV_OK
     for a, b in zip(outs2, ref):
         assert torch.equal(a, b)
+    assert bool((ws[need_dev:] == 0x5A).all())
     Kp = Kd.cpu()
     assert not Kp.is_pinned()
     st = lib.ckv_cluster(ct.byref(desc), p(Kp), *(p(x) for x in outs), p(ws), ws.numel(), stream)
