@@ -1,0 +1,129 @@
+"""Every entry point writes only inside the buffers it is given (GPU).
+
+Each output is a view into a larger buffer whose bytes before and after the
+view hold a pattern, and each workspace is followed by guard bytes past the
+size the call declares (the binding hands the library the declared size, not
+the tensor's): after the call every pattern byte must still be there. The
+shapes are ragged on purpose: token counts that are not a multiple of any
+tile, a budget B that is not a multiple of the 64-row attention split, and
+decode rows from pending tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_decode_attention_ckv_amd as ck
+import synth
+from tests.gpu_helpers import DEV, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+PAD = 4096                      # pattern bytes on each side (a 16-byte multiple)
+PATTERN = 0xA5
+
+
+class Guarded:
+    """A tensor of `shape` with PAD pattern bytes on both sides."""
+
+    def __init__(self, shape, dtype):
+        self.n = int(np.prod(shape))
+        self.es = torch.empty(0, dtype=dtype).element_size()
+        self.pre = PAD // self.es
+        self.buf = torch.empty(self.pre + self.n + PAD // self.es, dtype=dtype, device=DEV)
+        self.buf.view(torch.uint8).fill_(PATTERN)
+        self.t = self.buf[self.pre:self.pre + self.n].view(shape)
+
+    def intact(self) -> bool:
+        b = self.buf.view(torch.uint8)
+        lo, hi = self.pre * self.es, (self.pre + self.n) * self.es
+        return bool((b[:lo] == PATTERN).all()) and bool((b[hi:] == PATTERN).all())
+
+
+def _guarded_ws(nbytes):
+    ws = torch.empty(nbytes + PAD, dtype=torch.uint8, device=DEV)
+    ws.fill_(PATTERN)
+    return ws
+
+
+def _ws_intact(ws, nbytes) -> bool:
+    return bool((ws[nbytes:] == PATTERN).all())
+
+
+@pytest.mark.parametrize("H,L,C,dtype", [(2, 4121, 51, "bf16"), (3, 333, 4, "bf16"),
+                                          (1, 2087, 26, "fp32")])
+def test_cluster_writes_stay_inside(H, L, C, dtype):
+    say(f"bounds: ckv_cluster H={H} L={L} C={C} {dtype}")
+    wl = synth.workload(1 if dtype == "bf16" else 0)
+    K, _, _ = (synth.make_kv(wl, L=L, heads=range(H)) if dtype == "bf16"
+               else synth.make_kv(wl, L=L))
+    Kd = to_dev(K, dtype)
+    n_sink, Lp = 16, L - 16
+    cent = Guarded((H, C, 128), torch.float32)
+    asg = Guarded((H, L), torch.int32)
+    off = Guarded((H, C + 1), torch.int32)
+    tok = Guarded((H, Lp), torch.int32)
+    desc = ck.ClusterDesc(H=H, d=128, L=L, k_head_stride=Kd.stride(0), token_base=0,
+                          n_sink=n_sink, C=C, iters=4,
+                          dtype=ck.CKV_BF16 if dtype == "bf16" else ck.CKV_F32, c_base=0,
+                          c_cap=C, t_base=0, t_cap=Lp, metric=ck.CKV_COSINE)
+    nb = ck.ckv_cluster_workspace_device(desc)
+    ws = _guarded_ws(nb)
+    ck.ckv_cluster(Kd, n_sink, C, 4, centroids=cent.t, assign=asg.t, csr_offsets=off.t,
+                   csr_tokens=tok.t, workspace=ws)
+    torch.cuda.synchronize()
+    for name, g in (("centroids", cent), ("assign", asg), ("offsets", off), ("tokens", tok)):
+        assert g.intact(), name
+    assert _ws_intact(ws, nb)
+    # and the results are the ones an unguarded call gives
+    ref = ck.ckv_cluster(Kd, n_sink, C, 4)
+    torch.cuda.synchronize()
+    for a, b in zip((cent.t, asg.t, off.t, tok.t), ref):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("G,B,n_pending", [(4, 200, 0), (2, 1000, 37), (1, 65, 3)])
+def test_decode_writes_stay_inside(G, B, n_pending):
+    say(f"bounds: selection and attention G={G} B={B} pending={n_pending}")
+    H, L, C, n_sink = 2, 4121, 51, 16
+    wl = synth.workload(1)
+    K, V, _ = synth.make_kv(wl, L=L, heads=range(H))
+    Kd, Vd = to_dev(K, "bf16"), to_dev(V, "bf16")
+    rows = L + n_pending
+    Kx = torch.zeros((H, rows, 128), dtype=torch.bfloat16, device=DEV)
+    Vx = torch.zeros_like(Kx)
+    Kx[:, :L], Vx[:, :L] = Kd, Vd
+    Kx[:, L:] = Kd[:, :n_pending]
+    Vx[:, L:] = Vd[:, :n_pending]
+    cent, _, off, tok = ck.ckv_cluster(Kd, n_sink, C, 3)
+    torch.manual_seed(5)
+    q = (torch.randn((H * G, 128), device=DEV) * 0.5).to(torch.bfloat16)
+    kw = dict(n_sink=n_sink, pending_begin=L, n_pending=n_pending)
+
+    idx = Guarded((H, B), torch.int32)
+    nsel = Guarded((H,), torch.int32)
+    ck.ckv_select(q, cent, off, tok, C, B, idx=idx.t, n_sel=nsel.t, **kw)
+    torch.cuda.synchronize()
+    assert idx.intact() and nsel.intact()
+
+    out = Guarded((H * G, 128), torch.float32)
+    ck.ckv_sparse_attn(q, Kx, Vx, idx.t, nsel.t, out=out.t)
+    torch.cuda.synchronize()
+    assert out.intact()
+
+    sd = ck.SelectDesc(H=H, G=G, d=128, C=C, c_cap=C, n_sink=n_sink, t_cap=tok.shape[1],
+                       pending_begin=L, n_pending=n_pending, B=B, dtype=ck.CKV_BF16)
+    ad = ck.AttnDesc(H=H, G=G, d=128, B=B, kv_head_stride=Kx.stride(0), kv_rows=rows, scale=0.0,
+                     dtype=ck.CKV_BF16)
+    nb = ck.ckv_select_attn_workspace(sd, ad)
+    ws = _guarded_ws(nb)
+    idx2 = Guarded((H, B), torch.int32)
+    nsel2 = Guarded((H,), torch.int32)
+    out2 = Guarded((H * G, 128), torch.float32)
+    ck.ckv_select_attn(q, cent, off, tok, C, B, Kx, Vx, idx=idx2.t, n_sel=nsel2.t, out=out2.t,
+                       workspace=ws, **kw)
+    torch.cuda.synchronize()
+    assert idx2.intact() and nsel2.intact() and out2.intact()
+    assert _ws_intact(ws, nb)
+    # the fused call is bitwise the separate ones
+    assert torch.equal(idx2.t, idx.t) and torch.equal(nsel2.t, nsel.t)
+    assert torch.equal(out2.t, out.t)
