@@ -6,7 +6,8 @@ size the call declares (the binding hands the library the declared size, not
 the tensor's): after the call every pattern byte must still be there. The
 shapes are ragged on purpose: token counts that are not a multiple of any
 tile, a budget B that is not a multiple of the 64-row attention split, and
-decode rows from pending tokens.
+decode rows from pending tokens. ckv_select_attn_noalloc is covered too (its
+outputs; its workspace is the library's own).
 """
 import numpy as np
 import pytest
@@ -127,3 +128,13 @@ def test_decode_writes_stay_inside(G, B, n_pending):
     # the fused call is bitwise the separate ones
     assert torch.equal(idx2.t, idx.t) and torch.equal(nsel2.t, nsel.t)
     assert torch.equal(out2.t, out.t)
+
+    # the entry point without allocation (its workspace is the library's own)
+    idx3 = Guarded((H, B), torch.int32)
+    nsel3 = Guarded((H,), torch.int32)
+    out3 = Guarded((H * G, 128), torch.float32)
+    ck.ckv_select_attn_noalloc(q, cent, off, tok, C, B, Kx, Vx, idx=idx3.t, n_sel=nsel3.t,
+                               out=out3.t, **kw)
+    torch.cuda.synchronize()
+    assert idx3.intact() and nsel3.intact() and out3.intact()
+    assert torch.equal(idx3.t, idx.t) and torch.equal(out3.t, out.t)
