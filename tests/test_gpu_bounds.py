@@ -7,7 +7,7 @@ the tensor's): after the call every pattern byte must still be there. The
 shapes are ragged on purpose: token counts that are not a multiple of any
 tile, a budget B that is not a multiple of the 64-row attention split, and
 decode rows from pending tokens. ckv_select_attn_noalloc is covered too (its
-outputs; its workspace is the library's own).
+outputs; its workspace is the library's own), and ckv_cache_step's state.
 """
 import numpy as np
 import pytest
@@ -138,3 +138,35 @@ def test_decode_writes_stay_inside(G, B, n_pending):
     torch.cuda.synchronize()
     assert idx3.intact() and nsel3.intact() and out3.intact()
     assert torch.equal(idx3.t, idx.t) and torch.equal(out3.t, out.t)
+
+
+def test_cache_step_writes_stay_inside():
+    """ckv_cache_step: the ring, both row buffers, slot tokens, idx_cache,
+    stats and the workspace (a view of exactly the declared size) are guarded
+    views; four steps, and the state matches an unguarded run's bitwise."""
+    say("bounds: ckv_cache_step, 4 steps")
+    H, L, C, n_sink, B, R, G = 2, 4121, 51, 16, 200, 2, 4
+    wl = synth.workload(1)
+    K, V, _ = synth.make_kv(wl, L=L, heads=range(H))
+    Kd, Vd = to_dev(K, "bf16"), to_dev(V, "bf16")
+    cent, asg, off, tok = ck.ckv_cluster(Kd, n_sink, C, 3)
+    desc = ck.cache_desc(Kd, asg, off, tok, C, B, R, n_sink=n_sink)
+    ref = ck.cache_state(desc, DEV)
+    guards, st = {}, {"rows": ref["rows"]}
+    for k, v in ref.items():
+        if isinstance(v, torch.Tensor):
+            g = Guarded(tuple(v.shape), v.dtype)
+            if k != "workspace":
+                g.t.copy_(v)
+            guards[k], st[k] = g, g.t
+    torch.manual_seed(9)
+    for t in range(4):
+        q = (torch.randn((H * G, 128), device=DEV) * 0.5).to(torch.bfloat16)
+        idx, ns = ck.ckv_select(q, cent, off, tok, C, B, n_sink=n_sink)
+        ck.ckv_cache_step(desc, t, idx, ns, asg, off, tok, Kd, Vd, st)
+        ck.ckv_cache_step(desc, t, idx, ns, asg, off, tok, Kd, Vd, ref)
+    torch.cuda.synchronize()
+    for k, g in guards.items():
+        assert g.intact(), k
+    for k in ("ring", "cache_K", "cache_V", "cache_tok", "idx_cache", "stats"):
+        assert torch.equal(st[k], ref[k]), k
