@@ -4,8 +4,9 @@ Each output is a view into a larger buffer whose bytes before and after the
 view hold a pattern, and each workspace is followed by guard bytes past the
 size the call declares (the binding hands the library the declared size, not
 the tensor's): after the call every pattern byte must still be there. The
-shapes are ragged on purpose: token counts that are not a multiple of any
-tile, a budget B that is not a multiple of the 64-row attention split, and
+shapes are ragged on purpose (and C = 700 takes the three-launch counting
+sort and two LDS rounds of centroids): token counts that are not a multiple of
+any tile, a budget B that is not a multiple of the 64-row attention split, and
 decode rows from pending tokens. ckv_select_attn_noalloc is covered too (its
 outputs; its workspace is the library's own), and ckv_cache_step's state.
 """
@@ -50,10 +51,12 @@ def _ws_intact(ws, nbytes) -> bool:
     return bool((ws[nbytes:] == PATTERN).all())
 
 
-@pytest.mark.parametrize("H,L,C,dtype", [(2, 4121, 51, "bf16"), (3, 333, 4, "bf16"),
-                                          (1, 2087, 26, "fp32")])
-def test_cluster_writes_stay_inside(H, L, C, dtype):
-    say(f"bounds: ckv_cluster H={H} L={L} C={C} {dtype}")
+@pytest.mark.parametrize("H,L,C,dtype,metric", [
+    (2, 4121, 51, "bf16", ck.CKV_COSINE), (3, 333, 4, "bf16", ck.CKV_COSINE),
+    (1, 2087, 26, "fp32", ck.CKV_COSINE), (2, 6163, 700, "bf16", ck.CKV_COSINE),
+    (2, 4121, 51, "bf16", ck.CKV_L2), (1, 2087, 26, "fp32", ck.CKV_INNER_PRODUCT)])
+def test_cluster_writes_stay_inside(H, L, C, dtype, metric):
+    say(f"bounds: ckv_cluster H={H} L={L} C={C} {dtype} metric={metric}")
     wl = synth.workload(1 if dtype == "bf16" else 0)
     K, _, _ = (synth.make_kv(wl, L=L, heads=range(H)) if dtype == "bf16"
                else synth.make_kv(wl, L=L))
@@ -66,17 +69,17 @@ def test_cluster_writes_stay_inside(H, L, C, dtype):
     desc = ck.ClusterDesc(H=H, d=128, L=L, k_head_stride=Kd.stride(0), token_base=0,
                           n_sink=n_sink, C=C, iters=4,
                           dtype=ck.CKV_BF16 if dtype == "bf16" else ck.CKV_F32, c_base=0,
-                          c_cap=C, t_base=0, t_cap=Lp, metric=ck.CKV_COSINE)
+                          c_cap=C, t_base=0, t_cap=Lp, metric=metric)
     nb = ck.ckv_cluster_workspace_device(desc)
     ws = _guarded_ws(nb)
     ck.ckv_cluster(Kd, n_sink, C, 4, centroids=cent.t, assign=asg.t, csr_offsets=off.t,
-                   csr_tokens=tok.t, workspace=ws)
+                   csr_tokens=tok.t, workspace=ws, metric=metric)
     torch.cuda.synchronize()
     for name, g in (("centroids", cent), ("assign", asg), ("offsets", off), ("tokens", tok)):
         assert g.intact(), name
     assert _ws_intact(ws, nb)
     # and the results are the ones an unguarded call gives
-    ref = ck.ckv_cluster(Kd, n_sink, C, 4)
+    ref = ck.ckv_cluster(Kd, n_sink, C, 4, metric=metric)
     torch.cuda.synchronize()
     for a, b in zip((cent.t, asg.t, off.t, tok.t), ref):
         assert torch.equal(a, b)
