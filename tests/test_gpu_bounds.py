@@ -173,3 +173,35 @@ def test_cache_step_writes_stay_inside():
         assert g.intact(), k
     for k in ("ring", "cache_K", "cache_V", "cache_tok", "idx_cache", "stats"):
         assert torch.equal(st[k], ref[k]), k
+
+
+@pytest.mark.parametrize("Lw,C", [(320, 4), (1500, 40)])
+def test_append_writes_only_its_window(Lw, C):
+    """A decode-time increment (c_base, t_base > 0) on the small-window and the
+    general path writes centroid rows c_base .. c_base + C - 1, offsets
+    c_base .. c_base + C and token slots t_base .. t_base + Lw - 1 of the
+    shared buffers, and nothing else of them."""
+    say(f"bounds: append window Lw={Lw} C={C}")
+    H, L0, c_base, t_base = 2, 2000, 7, 100
+    c_cap, t_cap = c_base + C + 5, t_base + Lw + 50
+    wl = synth.workload(1)
+    K, _, _ = synth.make_kv(wl, L=L0 + Lw, heads=range(H))
+    Kd = to_dev(K, "bf16")
+    cent = Guarded((H, c_cap, 128), torch.float32)
+    off = Guarded((H, c_cap + 1), torch.int32)
+    tok = Guarded((H, t_cap), torch.int32)
+    asg = Guarded((H, Lw), torch.int32)
+    ck.ckv_cluster(Kd[:, L0:], 0, C, 3, token_base=L0, centroids=cent.t, assign=asg.t,
+                   csr_offsets=off.t, csr_tokens=tok.t, c_base=c_base, t_base=t_base)
+    torch.cuda.synchronize()
+    for g in (cent, off, tok, asg):
+        assert g.intact()
+    pat = lambda x: bool((x.contiguous().view(torch.uint8) == PATTERN).all())
+    assert pat(cent.t[:, :c_base]) and pat(cent.t[:, c_base + C:])
+    assert pat(off.t[:, :c_base]) and pat(off.t[:, c_base + C + 1:])
+    assert pat(tok.t[:, :t_base]) and pat(tok.t[:, t_base + Lw:])
+    # the window itself: offsets from t_base to t_base + Lw, every token once
+    o = off.t[:, c_base:c_base + C + 1].cpu().numpy()
+    assert (o[:, 0] == t_base).all() and (o[:, -1] == t_base + Lw).all()
+    w = np.sort(tok.t[:, t_base:t_base + Lw].cpu().numpy(), axis=1)
+    assert (w == np.arange(L0, L0 + Lw)[None, :]).all()
