@@ -4,7 +4,8 @@
 One step is one pass of the whole hot path over one batch of synthetic input
 (the Llama-3.1-8B-shaped 32k layer by default): ckv_cluster over the prompt
 (cosine K-means, 10 iterations) followed by the workload's decode steps,
-each a ckv_select + ckv_sparse_attn with a fresh query. Inputs are resident
+each one ckv_select_attn call with a fresh query (--separate: ckv_select then
+ckv_sparse_attn, bitwise the same). Inputs are resident
 in HBM before timing starts. The clustering call and the decode loop are
 each captured once as a HIP graph and replayed; every replay's results are
 checked bitwise against an eager run before timing.
